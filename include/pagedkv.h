@@ -1,0 +1,214 @@
+/*
+ * pagedkv.h — C ABI of a paged KV-cache attention library for AMD MI355X (gfx950).
+ *
+ * The KV cache of every sequence lives in fixed-size physical blocks taken
+ * from one shared pool; a per-sequence block table maps logical block j to a
+ * physical block ("Why PagedAttention multiplies LLM serving throughput",
+ * section "Block Table: the GPU page table"; "vLLM PagedAttention explained",
+ * sections 3.1-3.4). This library provides the device operations on that
+ * pool — writing new tokens' K/V into their slots, block copies for
+ * copy-on-write, decode attention and chunked-prefill attention read through
+ * the block tables — and a host block allocator that produces the tables.
+ *
+ * Conventions shared by every device entry point
+ *  - Memory: every device pointer is caller-owned device memory; the library
+ *    never allocates or frees device memory. Host pointers are marked "host".
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = null stream).
+ *    Device calls are asynchronous on that stream; they return after the
+ *    launch is queued.
+ *  - Layout: all arrays are dense, row-major, without padding.
+ *      k_pool, v_pool : [num_blocks][num_kv_heads][block_size][head_dim]
+ *    i.e. head-major inside a block, so one (block, head) tile is contiguous.
+ *    Token t of a sequence with table `bt` is at physical block bt[t / B],
+ *    offset t % B. A slot is the flat index block * B + offset
+ *    ("LLM inference engine internals", section 2.3, append_slot).
+ *  - Grouped heads: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *  - Errors: entry points return a pa_status and never abort. Every argument
+ *    that can be checked on the host is checked before any launch; on error no
+ *    work is queued. Contents of device arrays (block ids, slots, lengths) are
+ *    preconditions: they must index inside the pool and the tables.
+ *    pa_last_error() gives a message for the most recent failure on the calling
+ *    thread.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,      /* bad argument (null pointer, size, shape mismatch)      */
+  PA_ERR_UNSUPPORTED = -2,  /* valid but not built (dtype, head_dim, group size, ...) */
+  PA_ERR_OOM = -3,          /* allocator: not enough free blocks; state unchanged     */
+  PA_ERR_STATE = -4,        /* allocator: unknown / duplicate sequence id             */
+  PA_ERR_WORKSPACE = -5,    /* decode: workspace smaller than required                */
+  PA_ERR_HIP = -6           /* a HIP runtime call or kernel launch failed             */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,   /* IEEE float32                         */
+  PA_BF16 = 1   /* bfloat16 (upper 16 bits of float32)  */
+} pa_dtype;
+
+/* One layer's KV pool: two device arrays of identical shape and dtype. */
+typedef struct pa_pool {
+  void* k_pool;            /* device, [num_blocks][num_kv_heads][block_size][head_dim] */
+  void* v_pool;            /* device, same shape                                       */
+  int32_t num_blocks;      /* > 0                                                      */
+  int32_t num_kv_heads;    /* > 0                                                      */
+  int32_t block_size;      /* B: power of two, 1..256                                  */
+  int32_t head_dim;        /* D: 64 or 128                                             */
+  int32_t dtype;           /* pa_dtype                                                 */
+} pa_pool;
+
+const char* pa_status_string(pa_status s);
+/* Message for the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t pa_version(void);
+
+/* ---------------------------------------------------------------- device --- */
+
+/*
+ * pa_cache_write — store the K/V of new tokens into their slots.
+ * ("vLLM PagedAttention explained", section 3.3: the KV of the prompt and of
+ * each generated token is written into the physical blocks the block table
+ * maps; slot rule of "LLM inference engine internals", section 2.3.)
+ *   k_new, v_new : device, [num_tokens][num_kv_heads][head_dim], pool dtype
+ *   slot_mapping : device, int64 [num_tokens]; token i goes to block
+ *                  slot / B, offset slot % B, for every KV head. A negative
+ *                  slot means "skip this token" (padding).
+ * The result is a byte copy: bit-exact. Slots must be distinct and
+ * < num_blocks * B; nothing else in the pool is touched. num_tokens == 0 is a
+ * no-op.
+ */
+pa_status pa_cache_write(const pa_pool* pool, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/*
+ * pa_copy_blocks — copy whole physical blocks (all KV heads, K and V):
+ * pool[dst] = pool[src] for each pair, the device side of copy-on-write
+ * ("vLLM PagedAttention explained", section 4.1; the scheduler's
+ * blocks_to_copy output, "LLM inference engine internals", section 3.1).
+ *   src_dst : device, int32 [num_pairs][2] = {src, dst}. No block may appear
+ *             both as a source and as a destination in one call.
+ * Bit-exact. num_pairs == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(const pa_pool* pool, const int32_t* src_dst, int32_t num_pairs,
+                         void* stream);
+
+/*
+ * Workspace needed by pa_decode, in bytes, for the given sizes and partition
+ * length (0 = the library's default). 0 means no workspace is needed.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t partition_tokens);
+
+/*
+ * pa_decode — decode-step attention through the block tables.
+ * For every sequence s and query head h: out[s][h] = softmax(scale * K_s q) V_s
+ * over the seq_lens[s] cached tokens of s, the newest token included
+ * ("vLLM PagedAttention explained", section 3.3 step 2; kernel outline of
+ * "LLM inference engine internals", section 2.4, whose softmax and V step are
+ * completed here). Sequences are split into partitions of `partition_tokens`
+ * tokens that are combined exactly by a log-sum-exp reduction.
+ *   out          : device, [num_seqs][num_q_heads][head_dim], dtype of the pool
+ *   q            : device, [num_seqs][num_q_heads][head_dim], dtype of the pool
+ *   block_tables : device, int32 [num_seqs][max_blocks_per_seq]; only the first
+ *                  ceil(seq_lens[s] / B) entries of a row are read
+ *   seq_lens     : device, int32 [num_seqs], each in [0, max_blocks_per_seq * B];
+ *                  a sequence of length 0 gets an all-zero output
+ *   num_q_heads  : multiple of pool->num_kv_heads; group size <= 8 or a multiple of 8
+ *   scale        : softmax scale (typically 1/sqrt(head_dim))
+ *   partition_tokens : 0 = default, else a multiple of 16 and of B
+ *   workspace    : device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
+ *                  aligned (may be NULL when that is 0); contents are scratch
+ * Accumulation is fp32 for both dtypes; bf16 output is rounded to nearest even.
+ */
+pa_status pa_decode(void* out, const void* q, const pa_pool* pool,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                    float scale, int32_t partition_tokens,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_chunk — causal attention of a chunk of prompt rows per sequence
+ * over that sequence's paged K/V ("vLLM PagedAttention explained", section
+ * 7.2: a long prompt is processed in chunks that join the block table).
+ * The chunk's own K/V must already be in the pool (pa_cache_write).
+ *   out, q       : device, bf16 [total_rows][num_q_heads][head_dim];
+ *                  rows q_start_loc[s] .. q_start_loc[s+1]-1 belong to sequence s
+ *   q_start_loc  : device, int32 [num_seqs + 1], non-decreasing, q_start_loc[0] = 0
+ *   seq_lens     : device, int32 [num_seqs]: tokens in the pool for s, chunk
+ *                  included; chunk row i sits at absolute position
+ *                  seq_lens[s] - q_len_s + i and sees keys 0 .. that position
+ *   max_q_len    : host, >= every q_len_s (sizes the launch)
+ * bf16 only (PA_ERR_UNSUPPORTED otherwise); fp32 accumulation.
+ */
+pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,
+                           const int32_t* seq_lens, const pa_pool* pool,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t max_q_len,
+                           float scale, void* stream);
+
+/* ------------------------------------------------------------------ host --- */
+
+/*
+ * Host block allocator ("LLM inference engine internals", section 2.3; "vLLM
+ * PagedAttention explained", sections 4.1, 4.2, 7.1; "Why PagedAttention
+ * multiplies LLM serving throughput", section "Automatic prefix caching").
+ * FIFO free list, per-block reference counts, fork with copy-on-write of a
+ * shared partial last block, and hash-based sharing of full prompt blocks.
+ * It touches no device memory; it produces block tables, slots and the list
+ * of block copies for pa_copy_blocks. Not thread-safe: one owner at a time.
+ * Every call that fails leaves the allocator state unchanged.
+ */
+typedef struct pa_alloc pa_alloc;
+
+/* free_order: host, int32 [num_blocks] permutation giving the initial free-list
+ * order, or NULL for 0, 1, 2, ... */
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                          pa_alloc** out);
+void pa_alloc_destroy(pa_alloc* a);
+
+/* New sequence with an n-token prompt (host tokens[n]). Leading full blocks
+ * found in the prefix cache are shared; *cached_out (nullable) receives the
+ * number of leading tokens whose K/V is already in the pool. slots_out
+ * (host, nullable, int64 [n]) receives the slot of every position. */
+pa_status pa_alloc_allocate(pa_alloc* a, int64_t seq_id, const int32_t* tokens, int32_t n,
+                            int32_t* cached_out, int64_t* slots_out);
+/* Append one token; *slot_out receives its slot. May queue one block copy. */
+pa_status pa_alloc_append_slot(pa_alloc* a, int64_t seq_id, int32_t token, int64_t* slot_out);
+/* Append an n-token chunk (all or nothing); slots_out host int64 [n] (nullable). */
+pa_status pa_alloc_extend(pa_alloc* a, int64_t seq_id, const int32_t* tokens, int32_t n,
+                          int64_t* slots_out);
+/* child shares all of parent's blocks (reference counts + 1). */
+pa_status pa_alloc_fork(pa_alloc* a, int64_t parent, int64_t child);
+/* Release a sequence's blocks in table order; count 0 returns a block to the free list. */
+pa_status pa_alloc_free(pa_alloc* a, int64_t seq_id);
+/* Move the queued (src, dst) copies into host src_dst[cap][2], oldest first.
+ * *n_out = number queued; if cap < that, PA_ERR_INVALID and nothing is moved. */
+pa_status pa_alloc_take_copies(pa_alloc* a, int32_t* src_dst, int32_t cap, int32_t* n_out);
+/* Copy a sequence's block table into host out[cap]; *n_out = its length. */
+pa_status pa_alloc_block_table(const pa_alloc* a, int64_t seq_id, int32_t* out, int32_t cap,
+                               int32_t* n_out);
+pa_status pa_alloc_seq_len(const pa_alloc* a, int64_t seq_id, int32_t* len_out);
+/* Build a padded batch: host tables[n][max_blocks] (unused entries 0) and
+ * host seq_lens[n] for seq_ids[n]. PA_ERR_INVALID if a table is longer than max_blocks. */
+pa_status pa_alloc_batch_tables(const pa_alloc* a, const int64_t* seq_ids, int32_t n,
+                                int32_t* tables, int32_t max_blocks, int32_t* seq_lens);
+int32_t pa_alloc_num_free(const pa_alloc* a);
+/* Reference count of a physical block (0 = free). */
+pa_status pa_alloc_ref_count(const pa_alloc* a, int32_t block, int32_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,17 @@
+"""Paged KV-cache attention for AMD MI355X (gfx950).
+
+The KV cache lives in fixed-size physical blocks of one shared pool, reached
+through per-sequence block tables. The device work runs in the hand-written
+HIP kernels of ``libpagedkv.so`` behind the C ABI of ``include/pagedkv.h``;
+this package only marshals torch tensors (device memory, current stream) into
+those calls, and wraps the C++ host block allocator.
+"""
+
+from ._lib import (AllocatorStateError, OutOfBlocks, PagedKVError, LIB_PATH, SIGNATURES, lib)
+from .allocator import BlockAllocator
+from .ops import (DecodePlan, KVPool, cache_write, copy_blocks, decode, decode_workspace_bytes,
+                  prefill_chunk)
+
+__all__ = ["AllocatorStateError", "OutOfBlocks", "PagedKVError", "LIB_PATH", "SIGNATURES", "lib",
+           "BlockAllocator", "DecodePlan", "KVPool", "cache_write", "copy_blocks", "decode",
+           "decode_workspace_bytes", "prefill_chunk"]

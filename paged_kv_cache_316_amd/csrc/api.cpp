@@ -1,0 +1,248 @@
+// C ABI entry points: host-side argument checks, workspace sizing, dispatch
+// to the HIP launchers, and status / error-message plumbing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "device.h"
+#include "pagedkv.h"
+#include "status.h"
+
+namespace pa {
+
+namespace {
+thread_local char g_msg[512] = "";
+
+constexpr int32_t kDefaultPartitionTokens = 512;
+
+bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int32_t elt_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+pa_status check_pool(const pa_pool* p, const char* who) {
+  if (!p) return fail(PA_ERR_INVALID, "%s: pool is NULL", who);
+  if (!p->k_pool || !p->v_pool) return fail(PA_ERR_INVALID, "%s: k_pool/v_pool is NULL", who);
+  if (p->num_blocks <= 0 || p->num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID, "%s: num_blocks=%d num_kv_heads=%d must be > 0", who,
+                p->num_blocks, p->num_kv_heads);
+  if (!pow2(p->block_size) || p->block_size > 256)
+    return fail(PA_ERR_INVALID, "%s: block_size=%d must be a power of two in 1..256", who,
+                p->block_size);
+  if (p->dtype != PA_F32 && p->dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim=%d not supported (64, 128)", who, p->head_dim);
+  return PA_OK;
+}
+
+pa_status hip_status(hipError_t e, const char* who) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
+}
+
+int32_t effective_partition(int32_t requested, int32_t block_size) {
+  int32_t p = requested > 0 ? requested : kDefaultPartitionTokens;
+  const int32_t unit = block_size > 16 ? block_size : 16;
+  return ((p + unit - 1) / unit) * unit;
+}
+
+}  // namespace
+
+pa_status fail(pa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_error() { g_msg[0] = '\0'; }
+
+}  // namespace pa
+
+using pa::fail;
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_OOM: return "out of free blocks";
+    case PA_ERR_STATE: return "invalid allocator state (unknown or duplicate sequence)";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pa_last_error(void) { return pa::g_msg; }
+
+int32_t pa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+pa_status pa_cache_write(const pa_pool* pool, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
+  pa::clear_error();
+  if (pa_status s = pa::check_pool(pool, "pa_cache_write")) return s;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "pa_cache_write: num_tokens=%d < 0", num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_INVALID, "pa_cache_write: k_new/v_new/slot_mapping is NULL");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+       reinterpret_cast<uintptr_t>(pool->k_pool) | reinterpret_cast<uintptr_t>(pool->v_pool)) & 15)
+    return fail(PA_ERR_INVALID, "pa_cache_write: K/V arrays must be 16-byte aligned");
+  return pa::hip_status(pa::launch_cache_write(*pool, k_new, v_new, slot_mapping, num_tokens,
+                                               static_cast<hipStream_t>(stream)),
+                        "pa_cache_write");
+}
+
+pa_status pa_copy_blocks(const pa_pool* pool, const int32_t* src_dst, int32_t num_pairs,
+                         void* stream) {
+  pa::clear_error();
+  if (pa_status s = pa::check_pool(pool, "pa_copy_blocks")) return s;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID, "pa_copy_blocks: num_pairs=%d < 0", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!src_dst) return fail(PA_ERR_INVALID, "pa_copy_blocks: src_dst is NULL");
+  if ((reinterpret_cast<uintptr_t>(pool->k_pool) | reinterpret_cast<uintptr_t>(pool->v_pool)) & 15)
+    return fail(PA_ERR_INVALID, "pa_copy_blocks: pools must be 16-byte aligned");
+  const int32_t kMaxPairsPerLaunch = 65535;
+  for (int32_t off = 0; off < num_pairs; off += kMaxPairsPerLaunch) {
+    const int32_t n = num_pairs - off < kMaxPairsPerLaunch ? num_pairs - off : kMaxPairsPerLaunch;
+    hipError_t e = pa::launch_copy_blocks(*pool, src_dst + 2 * int64_t(off), n,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return pa::hip_status(e, "pa_copy_blocks");
+  }
+  return PA_OK;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t block_size,
+                                 int32_t partition_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0)
+    return 0;
+  const int32_t P = pa::effective_partition(partition_tokens, block_size);
+  const int64_t max_len = int64_t(max_blocks_per_seq) * block_size;
+  const int64_t max_parts = (max_len + P - 1) / P;
+  if (max_parts <= 1) return 0;
+  const int64_t rows = int64_t(num_seqs) * num_q_heads * max_parts;
+  return size_t(rows) * (size_t(head_dim) * 4 + 8);
+}
+
+pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t num_q_heads, float scale, int32_t partition_tokens, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  if (pa_status s = pa::check_pool(pool, "pa_decode")) return s;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0)
+    return fail(PA_ERR_INVALID, "pa_decode: num_seqs=%d max_blocks_per_seq=%d num_q_heads=%d",
+                num_seqs, max_blocks_per_seq, num_q_heads);
+  if (num_seqs == 0) return PA_OK;
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "pa_decode: num_seqs=%d > 65535", num_seqs);
+  if (!out || !q || !block_tables || !seq_lens)
+    return fail(PA_ERR_INVALID, "pa_decode: out/q/block_tables/seq_lens is NULL");
+  if (num_q_heads % pool->num_kv_heads)
+    return fail(PA_ERR_INVALID, "pa_decode: num_q_heads=%d not a multiple of num_kv_heads=%d",
+                num_q_heads, pool->num_kv_heads);
+  if (!(scale == scale)) return fail(PA_ERR_INVALID, "pa_decode: scale is NaN");
+  if (partition_tokens < 0 || (partition_tokens > 0 && (partition_tokens % 16 ||
+                                                        partition_tokens % pool->block_size)))
+    return fail(PA_ERR_INVALID, "pa_decode: partition_tokens=%d must be 0 or a multiple of 16 and of B=%d",
+                partition_tokens, pool->block_size);
+  if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
+       reinterpret_cast<uintptr_t>(pool->k_pool) | reinterpret_cast<uintptr_t>(pool->v_pool)) & 15)
+    return fail(PA_ERR_INVALID, "pa_decode: out/q/pools must be 16-byte aligned");
+  const int32_t G = num_q_heads / pool->num_kv_heads;
+  if (!pa::decode_supported(pool->dtype, pool->head_dim, G))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: dtype=%d head_dim=%d group=%d not built",
+                pool->dtype, pool->head_dim, G);
+  const int32_t P = pa::effective_partition(partition_tokens, pool->block_size);
+  if (P / pool->block_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: partition of %d tokens spans > 1024 blocks", P);
+  const int64_t max_len = int64_t(max_blocks_per_seq) * pool->block_size;
+  const int64_t max_parts = (max_len + P - 1) / P;
+  if (max_parts > 2147483647LL)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: too many partitions");
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim,
+                                                max_blocks_per_seq, pool->block_size,
+                                                partition_tokens);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes, %zu needed",
+                  workspace ? workspace_bytes : size_t(0), need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 15)
+      return fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
+  }
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  const int64_t rows = int64_t(num_seqs) * num_q_heads * max_parts;
+  a.ws_acc = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = need ? reinterpret_cast<float2*>(static_cast<char*>(workspace) +
+                                             size_t(rows) * pool->head_dim * 4)
+                 : nullptr;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.block_size = pool->block_size;
+  a.dtype = pool->dtype;
+  a.partition_tokens = P;
+  a.max_parts = int32_t(max_parts);
+  a.scale = scale;
+  return pa::hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)), "pa_decode");
+}
+
+pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,
+                           const int32_t* seq_lens, const pa_pool* pool,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t max_q_len, float scale,
+                           void* stream) {
+  pa::clear_error();
+  if (pa_status s = pa::check_pool(pool, "pa_prefill_chunk")) return s;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || max_q_len < 0)
+    return fail(PA_ERR_INVALID, "pa_prefill_chunk: bad sizes");
+  if (num_seqs == 0 || max_q_len == 0) return PA_OK;
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: num_seqs > 65535");
+  if (!out || !q || !q_start_loc || !seq_lens || !block_tables)
+    return fail(PA_ERR_INVALID, "pa_prefill_chunk: NULL pointer argument");
+  if (num_q_heads % pool->num_kv_heads)
+    return fail(PA_ERR_INVALID, "pa_prefill_chunk: num_q_heads not a multiple of num_kv_heads");
+  if (!(scale == scale)) return fail(PA_ERR_INVALID, "pa_prefill_chunk: scale is NaN");
+  if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
+       reinterpret_cast<uintptr_t>(pool->k_pool) | reinterpret_cast<uintptr_t>(pool->v_pool)) & 15)
+    return fail(PA_ERR_INVALID, "pa_prefill_chunk: out/q/pools must be 16-byte aligned");
+  const int32_t G = num_q_heads / pool->num_kv_heads;
+  if (!pa::prefill_supported(pool->dtype, pool->head_dim, pool->block_size, G))
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: dtype=%d head_dim=%d block_size=%d not built",
+                pool->dtype, pool->head_dim, pool->block_size);
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.q_start_loc = q_start_loc;
+  a.seq_lens = seq_lens;
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.block_size = pool->block_size;
+  a.max_q_len = max_q_len;
+  a.scale = scale;
+  return pa::hip_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream)),
+                        "pa_prefill_chunk");
+}
+
+}  // extern "C"

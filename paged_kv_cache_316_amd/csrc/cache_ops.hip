@@ -1,0 +1,80 @@
+// Cache write (slot scatter) and whole-block copy. Both are byte copies in
+// 16-byte units, so they are bit-exact for every dtype.
+//
+// Slot rule ("LLM inference engine internals", section 2.3): slot =
+// block * B + offset. Pool layout [num_blocks][Hkv][B][D]: the row of token
+// (block b, offset o) for head h starts at element ((b * Hkv + h) * B + o) * D.
+#include "device.h"
+
+namespace pa {
+namespace {
+
+// One thread per 16-byte chunk of one (token, head) row; K and V together.
+__global__ __launch_bounds__(256) void cache_write_kernel(
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+    const int64_t* __restrict__ slots, uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+    int64_t total_chunks, int32_t chunks_per_token, int32_t chunks_per_row, int32_t heads,
+    int32_t block_size) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total_chunks; i += stride) {
+    const int64_t t = i / chunks_per_token;
+    const int32_t rem = int32_t(i - t * chunks_per_token);
+    const int32_t h = rem / chunks_per_row;
+    const int32_t c = rem - h * chunks_per_row;
+    const int64_t slot = slots[t];
+    if (slot < 0) continue;  // padding token
+    const int64_t b = slot / block_size;
+    const int64_t o = slot - b * block_size;
+    const int64_t dst = ((b * heads + h) * block_size + o) * chunks_per_row + c;
+    k_pool[dst] = k_new[i];
+    v_pool[dst] = v_new[i];
+  }
+}
+
+// grid.y = pair index; each thread copies 16-byte chunks of one block, K and V.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    const int32_t* __restrict__ src_dst, uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+    int64_t chunks_per_block) {
+  const int64_t src = src_dst[2 * blockIdx.y];
+  const int64_t dst = src_dst[2 * blockIdx.y + 1];
+  const uint4* ks = k_pool + src * chunks_per_block;
+  const uint4* vs = v_pool + src * chunks_per_block;
+  uint4* kd = k_pool + dst * chunks_per_block;
+  uint4* vd = v_pool + dst * chunks_per_block;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < chunks_per_block;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+int elt_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+}  // namespace
+
+hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void* v_new,
+                              const int64_t* slots, int32_t T, hipStream_t stream) {
+  const int32_t cpr = pool.head_dim * elt_bytes(pool.dtype) / 16;
+  const int32_t cpt = cpr * pool.num_kv_heads;
+  const int64_t total = int64_t(T) * cpt;
+  const int64_t want = (total + 255) / 256;
+  const int grid = int(want < 8192 ? want : 8192);
+  cache_write_kernel<<<grid, 256, 0, stream>>>(
+      static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), slots,
+      static_cast<uint4*>(pool.k_pool), static_cast<uint4*>(pool.v_pool), total, cpt, cpr,
+      pool.num_kv_heads, pool.block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const pa_pool& pool, const int32_t* src_dst, int32_t n,
+                              hipStream_t stream) {
+  const int64_t cpb = int64_t(pool.num_kv_heads) * pool.block_size * pool.head_dim *
+                      elt_bytes(pool.dtype) / 16;
+  const int64_t want = (cpb + 255) / 256;
+  const int gx = int(want < 64 ? want : 64);
+  copy_blocks_kernel<<<dim3(gx, n), 256, 0, stream>>>(
+      src_dst, static_cast<uint4*>(pool.k_pool), static_cast<uint4*>(pool.v_pool), cpb);
+  return hipGetLastError();
+}
+
+}  // namespace pa

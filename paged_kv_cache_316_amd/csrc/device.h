@@ -1,0 +1,110 @@
+// Device helpers for gfx950 (CDNA4, wave64): element traits, bf16 packing,
+// cross-lane reductions on DPP, and the launch interface of the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+
+namespace pa {
+
+constexpr int kWave = 64;
+
+// Storage traits. One lane moves 16 bytes per load: VEC elements.
+template <int DTYPE> struct Elt;
+template <> struct Elt<PA_F32> { static constexpr int bytes = 4; };
+template <> struct Elt<PA_BF16> { static constexpr int bytes = 2; };
+
+template <int DTYPE, int D>
+struct RowShape {
+  static constexpr int VEC = 16 / Elt<DTYPE>::bytes;  // elements per 16-byte load
+  static constexpr int LPR = D / VEC;                 // lanes covering one token row
+  static constexpr int NR = kWave / LPR;              // token rows per wave-wide load
+  static_assert(LPR >= 1 && LPR <= kWave && kWave % LPR == 0, "unsupported head_dim");
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load: K/V rows are read once per step, so they are marked
+// non-temporal to keep them from displacing reused data in the caches.
+__device__ __forceinline__ uint4 load_stream16(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + (((u >> 16) & 1u) + 0x7fffu)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// DPP move inside rows of 16 lanes (all rows and banks enabled).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+constexpr int kQuadSwap1 = 0xb1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4e;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i inside each half row
+constexpr int kRowMirror = 0x140;     // lane i <-> 15-i inside each row
+
+// Sum over aligned groups of N consecutive lanes; every lane gets its group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<kQuadSwap1>(x);
+  if constexpr (N >= 4) x += dpp<kQuadSwap2>(x);
+  if constexpr (N >= 8) x += dpp<kRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kRowMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// ---------------------------------------------------------------- launches --
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* ws_acc;   // [S][Hq][max_parts][D] unnormalised partial sums
+  float2* ws_ml;   // [S][Hq][max_parts] (running max in log2 units, denominator)
+  int32_t max_blocks_per_seq;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
+  int32_t partition_tokens, max_parts;
+  float scale;
+};
+
+hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void* v_new,
+                              const int64_t* slots, int32_t T, hipStream_t stream);
+hipError_t launch_copy_blocks(const pa_pool& pool, const int32_t* src_dst, int32_t n,
+                              hipStream_t stream);
+// Returns hipErrorInvalidValue for shapes without a compiled kernel.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+bool decode_supported(int dtype, int head_dim, int group);
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const int32_t* q_start_loc;
+  const int32_t* seq_lens;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_q_len;
+  float scale;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+bool prefill_supported(int dtype, int head_dim, int block_size, int group);
+
+}  // namespace pa

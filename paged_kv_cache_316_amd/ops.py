@@ -1,0 +1,159 @@
+"""Device entry points: argument marshalling from torch tensors to the C ABI.
+
+torch supplies device memory and the current stream; every step of the
+attention path runs in the library's HIP kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import PA_BF16, PA_F32, PaPool, PagedKVError, check, lib
+
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=True) -> None:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+class KVPool:
+    """One layer's K and V pools: [num_blocks, num_kv_heads, block_size, head_dim]."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor):
+        if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
+            raise ValueError("k and v pools must be 4-D with equal shape and dtype")
+        if k.dtype not in _DTYPES:
+            raise ValueError(f"pool dtype {k.dtype} not supported")
+        _need(k, "k_pool")
+        _need(v, "v_pool")
+        self.k, self.v = k, v
+        nb, h, b, d = k.shape
+        self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim = nb, h, b, d
+        self.dtype = k.dtype
+        self.c = PaPool(k.data_ptr(), v.data_ptr(), nb, h, b, d, _DTYPES[k.dtype])
+
+    @classmethod
+    def empty(cls, num_blocks, num_kv_heads, block_size, head_dim, dtype, device="cuda"):
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        return cls(torch.empty(shape, dtype=dtype, device=device),
+                   torch.empty(shape, dtype=dtype, device=device))
+
+    @property
+    def kv_bytes_per_token(self) -> int:
+        return 2 * self.num_kv_heads * self.head_dim * self.k.element_size()
+
+
+def cache_write(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
+                slot_mapping: torch.Tensor) -> None:
+    """Store k_new/v_new [T, Hkv, D] at slots (int64 [T]; negative = skip)."""
+    T = slot_mapping.numel()
+    _need(slot_mapping, "slot_mapping", torch.int64)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, pool.dtype)
+        if tuple(t.shape) != (T, pool.num_kv_heads, pool.head_dim):
+            raise ValueError(f"{n} must be [{T}, {pool.num_kv_heads}, {pool.head_dim}]")
+    check(lib().pa_cache_write(ctypes.byref(pool.c), k_new.data_ptr(), v_new.data_ptr(),
+                               slot_mapping.data_ptr(), T, _stream()))
+
+
+def copy_blocks(pool: KVPool, src_dst: torch.Tensor) -> None:
+    """pool[dst] = pool[src] for each row of int32 [n, 2] (device)."""
+    _need(src_dst, "src_dst", torch.int32)
+    n = src_dst.shape[0] if src_dst.numel() else 0
+    if src_dst.numel() and tuple(src_dst.shape) != (n, 2):
+        raise ValueError("src_dst must be [n, 2]")
+    check(lib().pa_copy_blocks(ctypes.byref(pool.c), _ptr(src_dst), n, _stream()))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                           max_blocks_per_seq: int, block_size: int,
+                           partition_tokens: int = 0) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                               max_blocks_per_seq, block_size, partition_tokens))
+
+
+class DecodePlan:
+    """Output and workspace buffers for repeated decode calls of one shape."""
+
+    def __init__(self, pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks_per_seq: int,
+                 partition_tokens: int = 0):
+        self.pool = pool
+        self.num_seqs, self.num_q_heads = num_seqs, num_q_heads
+        self.max_blocks_per_seq = max_blocks_per_seq
+        self.partition_tokens = partition_tokens
+        self.out = torch.empty((num_seqs, num_q_heads, pool.head_dim), dtype=pool.dtype,
+                               device=pool.k.device)
+        nbytes = decode_workspace_bytes(num_seqs, num_q_heads, pool.head_dim, max_blocks_per_seq,
+                                        pool.block_size, partition_tokens)
+        self.workspace = (torch.empty(nbytes, dtype=torch.uint8, device=pool.k.device)
+                          if nbytes else None)
+
+
+def decode(q: torch.Tensor, pool: KVPool, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+           scale: float, partition_tokens: int = 0, plan: Optional[DecodePlan] = None,
+           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged decode attention. q [S, Hq, D]; block_tables int32 [S, maxB]; seq_lens int32 [S]."""
+    _need(q, "q", pool.dtype)
+    _need(block_tables, "block_tables", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    S, Hq, D = q.shape
+    if D != pool.head_dim or block_tables.dim() != 2 or block_tables.shape[0] != S \
+            or seq_lens.shape != (S,):
+        raise ValueError("shape mismatch between q, block_tables and seq_lens")
+    maxb = block_tables.shape[1]
+    if plan is None:
+        plan = DecodePlan(pool, S, Hq, maxb, partition_tokens)
+    elif (plan.num_seqs, plan.num_q_heads, plan.max_blocks_per_seq, plan.partition_tokens) != \
+            (S, Hq, maxb, partition_tokens):
+        raise ValueError("plan does not match this call")
+    if out is None:
+        out = plan.out
+    _need(out, "out", pool.dtype)
+    ws = plan.workspace
+    check(lib().pa_decode(out.data_ptr(), q.data_ptr(), ctypes.byref(pool.c),
+                          block_tables.data_ptr(), maxb, seq_lens.data_ptr(), S, Hq,
+                          float(scale), int(partition_tokens), _ptr(ws),
+                          0 if ws is None else ws.numel(), _stream()))
+    return out
+
+
+def prefill_chunk(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.Tensor,
+                  pool: KVPool, block_tables: torch.Tensor, max_q_len: int, scale: float,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal chunked-prefill attention. q [rows, Hq, D] bf16; q_start_loc int32 [S+1]."""
+    _need(q, "q", pool.dtype)
+    _need(q_start_loc, "q_start_loc", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(block_tables, "block_tables", torch.int32)
+    S = seq_lens.shape[0]
+    if q_start_loc.shape != (S + 1,) or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch between q_start_loc, seq_lens and block_tables")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", pool.dtype)
+    check(lib().pa_prefill_chunk(out.data_ptr(), q.data_ptr(), q_start_loc.data_ptr(),
+                                 seq_lens.data_ptr(), ctypes.byref(pool.c),
+                                 block_tables.data_ptr(), block_tables.shape[1], S, q.shape[1],
+                                 int(max_q_len), float(scale), _stream()))
+    return out
+
+
+__all__ = ["KVPool", "DecodePlan", "cache_write", "copy_blocks", "decode",
+           "decode_workspace_bytes", "prefill_chunk", "PagedKVError"]

@@ -1,0 +1,109 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any launch (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_316_amd as pkv
+from paged_kv_cache_316_amd._lib import PaPool, lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pagedkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("pa_cache_write", "pa_decode", "pa_prefill_chunk", "pa_copy_blocks",
+                 "pa_alloc_create", "pa_alloc_append_slot", "pa_alloc_fork"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    # and the ctypes signatures cover all of them
+    assert set(declared_functions()) <= set(pkv.SIGNATURES)
+
+
+def test_status_strings_and_version():
+    L = lib()
+    assert L.pa_status_string(0) == b"ok"
+    for s in range(-6, 0):
+        assert L.pa_status_string(s) not in (b"", b"unknown status")
+    assert L.pa_version() >= 10000
+
+
+def _pool(**kw):
+    base = dict(k_pool=16, v_pool=32, num_blocks=4, num_kv_heads=2, block_size=16, head_dim=128,
+                dtype=1)
+    base.update(kw)
+    return PaPool(base["k_pool"], base["v_pool"], base["num_blocks"], base["num_kv_heads"],
+                  base["block_size"], base["head_dim"], base["dtype"])
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(block_size=12), -1), (dict(block_size=512), -1), (dict(head_dim=96), -2),
+    (dict(dtype=7), -2), (dict(num_blocks=0), -1), (dict(k_pool=0), -1)])
+def test_pool_validation_rejects_before_launch(bad, status):
+    L = lib()
+    p = _pool(**bad)
+    assert L.pa_cache_write(ctypes.byref(p), 16, 16, 16, 1, None) == status
+    assert L.pa_last_error()
+    assert L.pa_copy_blocks(ctypes.byref(p), 16, 1, None) == status
+
+
+def test_decode_argument_checks():
+    L = lib()
+    p = _pool(num_kv_heads=8)
+    # q heads not a multiple of KV heads
+    st = L.pa_decode(16, 16, ctypes.byref(p), 16, 4, 16, 2, 12, 0.1, 0, None, 0, None)
+    assert st == -1 and b"multiple" in L.pa_last_error()
+    # partition not a multiple of 16
+    st = L.pa_decode(16, 16, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, 24, None, 0, None)
+    assert st == -1
+    # workspace required but missing: 4 blocks * 16 > default partition? use many blocks
+    need = L.pa_decode_workspace_bytes(2, 8, 128, 4096, 16, 0)
+    assert need > 0
+    st = L.pa_decode(16, 16, ctypes.byref(p), 16, 4096, 16, 2, 8, 0.1, 0, None, 0, None)
+    assert st == -5
+    # NULL output
+    st = L.pa_decode(None, 16, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, 0, None, 0, None)
+    assert st == -1
+    # misaligned q
+    st = L.pa_decode(16, 18, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, 0, None, 0, None)
+    assert st == -1
+    # zero sequences is a no-op
+    assert L.pa_decode(None, None, ctypes.byref(p), None, 4, None, 0, 8, 0.1, 0, None, 0, None) == 0
+
+
+def test_workspace_formula():
+    L = lib()
+    # one partition per sequence: no workspace
+    assert L.pa_decode_workspace_bytes(64, 40, 128, 32, 16, 512) == 0
+    # 2048 tokens / 512 = 4 partitions: S*Hq*4*(D*4+8)
+    assert L.pa_decode_workspace_bytes(64, 40, 128, 128, 16, 512) == 64 * 40 * 4 * (128 * 4 + 8)
+
+
+def test_prefill_argument_checks():
+    L = lib()
+    p = _pool(dtype=0)
+    st = L.pa_prefill_chunk(16, 16, 16, 16, ctypes.byref(p), 16, 4, 2, 2, 64, 0.1, None)
+    assert st in (-2, -1)
+    assert L.pa_prefill_chunk(16, 16, 16, 16, ctypes.byref(_pool()), 16, 4, 0, 2, 64, 0.1, None) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    from paged_kv_cache_316_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="no CPU or Python fallback"):
+        _lib.lib()

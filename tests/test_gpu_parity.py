@@ -1,0 +1,228 @@
+"""GPU parity: the library's HIP path against the fp64 oracle.
+
+Runs on an MI355X only (marker ``gpu``). Every call goes through the C ABI.
+Bars: cache writes and block copies bit-exact over the whole pool; decode
+output within 1e-5 max-abs (fp32) or rtol 2e-2 / atol 5e-3 per element
+(bf16 inputs, fp32 accumulation).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle.expected import decode_out, pool_after
+
+from gpu_util import Loaded, assert_close, out_f64, pool_bits, to_device
+
+pytestmark = pytest.mark.gpu
+
+NAMES = workloads.config_names()
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    torch.cuda.init()
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_cache_write_and_copies_bit_exact(name):
+    """After the whole op script, every byte of both pools equals the oracle's
+    mirror (written by the slot rule, copied block-wise): written slots are
+    right and nothing else changed (untouched slots keep their NaN fill)."""
+    wl = workloads.make(name, "small")
+    _note(f"cache_write/copy parity: {name} small")
+    g = Loaded(wl)
+    mirror, _, _ = pool_after(wl)
+    assert np.array_equal(pool_bits(g.pool.k), mirror.k.view(pool_bits(g.pool.k).dtype))
+    assert np.array_equal(pool_bits(g.pool.v), mirror.v.view(pool_bits(g.pool.v).dtype))
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_decode_matches_oracle_small(name):
+    wl = workloads.make(name, "small")
+    _note(f"decode parity: {name} small, S={len(wl.decode_seqs)}")
+    g = Loaded(wl)
+    got = out_f64(g.decode())
+    want = decode_out(wl)
+    stats = assert_close(wl, got, want, name)
+    _note(f"  {stats}")
+
+
+@pytest.mark.parametrize("partition", [16, 32, 64, 256, 512, 4096])
+@pytest.mark.parametrize("name", ["llama13b", "llama70b", "tiny"])
+def test_split_sizes_agree(name, partition):
+    """Different partition lengths (a 16-token partition up to one partition per
+    sequence) all meet the oracle bar."""
+    wl = workloads.make(name, "small")
+    B = wl.block_size
+    if partition % B:
+        pytest.skip("partition must be a multiple of the block size")
+    g = Loaded(wl)
+    got = out_f64(g.decode(partition_tokens=partition))
+    assert_close(wl, got, decode_out(wl), f"{name} P={partition}")
+
+
+def test_placement_invariance_bitwise():
+    """Permuting physical block ids (pool'[pi(b)] = pool[b], table' = pi(table))
+    gives a bitwise-identical output."""
+    wl = workloads.make("llama13b", "small")
+    g = Loaded(wl)
+    base = g.decode()
+    rng = np.random.default_rng(5)
+    for _ in range(3):
+        perm = torch.from_numpy(rng.permutation(wl.num_blocks)).cuda()
+        k2 = torch.empty_like(g.pool.k); v2 = torch.empty_like(g.pool.v)
+        k2[perm] = g.pool.k; v2[perm] = g.pool.v
+        import paged_kv_cache_316_amd as pkv
+        pool2 = pkv.KVPool(k2, v2)
+        tables2 = perm.to(torch.int32)[g.tables.long()].contiguous()
+        out2 = g.decode(tables=tables2, pool=pool2)
+        assert torch.equal(out2.view(torch.int16), base.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["cow", "cow504", "beam", "prefix"])
+def test_shared_blocks_equal_copied_blocks_bitwise(name):
+    """Sequences reading shared blocks (ref count > 1) give the same bits as when
+    each sequence reads its own physical copy of every block."""
+    import paged_kv_cache_316_amd as pkv
+    wl = workloads.make(name, "small")
+    g = Loaded(wl)
+    base = g.decode()
+    tables = g.tables.cpu().numpy()
+    lens = g.lens.cpu().numpy()
+    nb_needed = [-(-int(L) // wl.block_size) for L in lens]
+    total = int(sum(nb_needed))
+    k2 = torch.empty((total,) + tuple(g.pool.k.shape[1:]), dtype=g.pool.k.dtype, device="cuda")
+    v2 = torch.empty_like(k2)
+    new_tables = np.zeros_like(tables)
+    src, nxt = [], 0
+    for i, n in enumerate(nb_needed):
+        for j in range(n):
+            src.append(int(tables[i, j])); new_tables[i, j] = nxt; nxt += 1
+    src_t = torch.tensor(src, dtype=torch.long, device="cuda")
+    k2.copy_(g.pool.k[src_t]); v2.copy_(g.pool.v[src_t])
+    out2 = g.decode(tables=torch.from_numpy(new_tables).cuda(), pool=pkv.KVPool(k2, v2))
+    shared = sum(nb_needed) - len(set(src))
+    assert shared > 0, "workload should share blocks"
+    assert torch.equal(out2.view(torch.int16), base.view(torch.int16))
+
+
+def _single_seq(L, Hq, Hkv, D, B, dtype, seed, zero_keys=False):
+    """One sequence laid out in reverse block order, through the C ABI."""
+    import paged_kv_cache_316_amd as pkv
+    rng = np.random.default_rng(seed)
+    nb = -(-L // B)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    k = torch.from_numpy(rng.standard_normal((L, Hkv, D)).astype(np.float32)).to(tdt)
+    v = torch.from_numpy(rng.standard_normal((L, Hkv, D)).astype(np.float32)).to(tdt)
+    if zero_keys:
+        k.zero_()
+    q = torch.from_numpy(rng.standard_normal((1, Hq, D)).astype(np.float32)).to(tdt)
+    pool = pkv.KVPool.empty(nb + 3, Hkv, B, D, tdt)
+    pool.k.fill_(float("nan")); pool.v.fill_(float("nan"))
+    table = np.arange(nb + 2, 2, -1)[:nb].astype(np.int32)  # reversed, offset placement
+    slots = torch.from_numpy((table[np.arange(L) // B].astype(np.int64) * B + np.arange(L) % B)).cuda()
+    pkv.cache_write(pool, k.cuda().contiguous(), v.cuda().contiguous(), slots)
+    out = pkv.decode(q.cuda(), pool, torch.from_numpy(table[None]).cuda(),
+                     torch.tensor([L], dtype=torch.int32, device="cuda"), 1 / np.sqrt(D))
+    torch.cuda.synchronize()
+    return q.double().numpy(), k.double().numpy(), v.double().numpy(), out_f64(out)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("L", [1, 2, 15, 16, 17, 511, 512, 513, 1000, 4097])
+@pytest.mark.parametrize("D,B,Hq,Hkv", [(128, 16, 8, 1), (64, 4, 4, 4), (128, 32, 6, 2), (64, 8, 8, 8)])
+def test_edge_lengths(dtype, L, D, B, Hq, Hkv):
+    from oracle.attention import decode_attention
+    q, k, v, got = _single_seq(L, Hq, Hkv, D, B, dtype, seed=L * 7 + D)
+    want = decode_attention(q, [k], [v], 1 / np.sqrt(D))
+
+    class W:  # tolerance selector
+        pass
+    W.dtype = dtype
+    assert_close(W, got, want, f"L={L} D={D} B={B} G={Hq // Hkv} {dtype}")
+    if L == 1:  # one token: output is V[0]; exact in fp32
+        expect = np.repeat(v[0], Hq // Hkv, axis=0)[None]
+        if dtype == "f32":
+            assert np.array_equal(got, expect)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_keys_give_mean_of_values(dtype):
+    q, k, v, got = _single_seq(300, 4, 2, 128, 16, dtype, seed=3, zero_keys=True)
+    want = np.repeat(v.mean(axis=0), 2, axis=0)[None]
+
+    class W:
+        pass
+    W.dtype = dtype
+    assert_close(W, got, want, "zero keys")
+
+
+def test_empty_sequence_gives_zeros():
+    import paged_kv_cache_316_amd as pkv
+    pool = pkv.KVPool.empty(4, 2, 16, 128, torch.bfloat16)
+    pool.k.fill_(float("nan")); pool.v.fill_(float("nan"))
+    q = torch.randn(3, 4, 128, device="cuda").to(torch.bfloat16)
+    tables = torch.tensor([[0, 1], [2, 3], [1, 0]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([0, 0, 0], dtype=torch.int32, device="cuda")
+    out = pkv.decode(q, pool, tables, lens, 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(out.float(), torch.zeros_like(out.float()))
+
+
+def test_cache_write_skips_negative_slots():
+    import paged_kv_cache_316_amd as pkv
+    pool = pkv.KVPool.empty(4, 2, 16, 128, torch.bfloat16)
+    pool.k.zero_(); pool.v.zero_()
+    k = torch.randn(5, 2, 128, device="cuda").to(torch.bfloat16)
+    v = torch.randn(5, 2, 128, device="cuda").to(torch.bfloat16)
+    slots = torch.tensor([3, -1, 17, -5, 63], dtype=torch.int64, device="cuda")
+    pkv.cache_write(pool, k, v, slots)
+    torch.cuda.synchronize()
+    ref_k = torch.zeros_like(pool.k)
+    for i, s in enumerate([3, -1, 17, -5, 63]):
+        if s >= 0:
+            ref_k[s // 16, :, s % 16, :] = k[i]
+    assert torch.equal(pool.k.view(torch.int16), ref_k.view(torch.int16))
+
+
+FULL = ["tiny", "llama13b", "cow", "cow504", "beam", "prefix", "llama70b"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    """Full-size workloads in the default launch configuration: the pool bits
+    are checked on sampled blocks, and the decode output on sampled sequences
+    (shortest, longest and seeded picks) against the oracle."""
+    wl = workloads.make(name, "full")
+    _note(f"full-size parity: {name}, S={len(wl.decode_seqs)}")
+    g = Loaded(wl)
+    out = g.decode()
+    lens = wl.seq_lens
+    rng = np.random.default_rng(77)
+    idx = sorted(set([int(np.argmin(lens)), int(np.argmax(lens))] +
+                     [int(x) for x in rng.choice(len(lens), size=min(6, len(lens)), replace=False)]))
+    got = out_f64(out[torch.tensor(idx, device="cuda")])
+    want = decode_out(wl, idx)
+    stats = assert_close(wl, got, want, name)
+    _note(f"  sampled {idx}: {stats}")
+    # every sequence's table reads back its logical K rows (sampled blocks, bitwise)
+    tables = g.tables.cpu().numpy()
+    kb = pool_bits(g.pool.k)
+    for i in idx:
+        seq = wl.decode_seqs[i]
+        L = int(lens[i])
+        t = np.arange(L)
+        rows = kb[tables[i, t // wl.block_size], :, t % wl.block_size, :]
+        assert np.array_equal(rows, wl.rows_k[wl.hist[seq]].view(rows.dtype))

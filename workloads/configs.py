@@ -68,7 +68,15 @@ def _draw_values(rng: np.random.Generator, shape, dtype: str, data_scale: float 
     return out.reshape(shape)
 
 
+_STRUCTURE_ONLY = [False]
+
+
 def _finish(rng, wl_kwargs, n_rows, n_q, n_prefill_q, dtype, Hkv, Hq, D, data_scale=1.0):
+    if _STRUCTURE_ONLY[0]:  # values are drawn last, so skipping them changes nothing else
+        z = np.zeros((0, Hkv, D), dtype=np.float32 if dtype == "f32" else np.uint16)
+        return Workload(rows_k=z, rows_v=z, q=z, prefill_q=None, dtype=dtype,
+                        num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D,
+                        scale=1.0 / math.sqrt(D), **wl_kwargs)
     rows_k = _draw_values(rng, (n_rows, Hkv, D), dtype, data_scale)
     rows_v = _draw_values(rng, (n_rows, Hkv, D), dtype, data_scale)
     q = _draw_values(rng, (n_q, Hq, D), dtype)
@@ -311,16 +319,22 @@ def config_names() -> List[str]:
     return list(CONFIGS)
 
 
-def make(name: str, size: str = "full", seed: int | None = None) -> Workload:
+def make(name: str, size: str = "full", seed: int | None = None,
+         values: bool = True) -> Workload:
     """Draw workload ``name`` ("full" or "small"); the seed defaults to the
-    workload's own and is offset for the small size so the two differ."""
+    workload's own and is offset for the small size so the two differ.
+    ``values=False`` skips the K/V/q draws (empty arrays): structure only."""
     if size not in ("full", "small"):
         raise ValueError(f"size must be 'full' or 'small', not {size!r}")
     base, fn = CONFIGS[name]
     if seed is None:
         seed = base if size == "full" else 1000 + base
     rng = np.random.default_rng(seed)
-    wl = fn(rng, size)
+    _STRUCTURE_ONLY[0] = not values
+    try:
+        wl = fn(rng, size)
+    finally:
+        _STRUCTURE_ONLY[0] = False
     wl.meta["seed"] = seed
     wl.meta["size"] = size
     return wl
