@@ -108,7 +108,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama13b", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--partition", type=int, default=0, help="decode partition tokens (0 = default)")
+    ap.add_argument("--workers", type=int, default=0, help="decode wavefronts (0 = default)")
     ap.add_argument("--replicas", type=int, default=2, help="pool replicas rotated between steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -162,7 +162,7 @@ def main():
     lens_d = torch.from_numpy(lens).cuda()
     q = dev(wl.q)
     S, Hq = len(wl.decode_seqs), wl.num_q_heads
-    plans = [pkv.DecodePlan(p, S, Hq, tables.shape[1], args.partition) for p in pools]
+    plans = [pkv.DecodePlan(p, S, Hq, args.workers) for p in pools]
     torch.cuda.synchronize()
     log(f"set-up done in {time.time() - t0:.1f} s")
 
@@ -185,7 +185,7 @@ def main():
         step_write.run(p)
         if ev is not None:
             ev[1].record(stream)
-        pkv.decode(q, p, tables_d, lens_d, wl.scale, args.partition, plan=plans[i % len(pools)])
+        pkv.decode(q, p, tables_d, lens_d, wl.scale, args.workers, plan=plans[i % len(pools)])
         if ev is not None:
             ev[2].record(stream)
 
@@ -225,7 +225,7 @@ def main():
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "block_size": wl.block_size, "tokens": int(lens.sum()),
                    "kv_bytes_per_step": int(kv_bytes), "pool_replicas": len(pools),
-                   "accumulation": "fp32", "partition_tokens": args.partition or "default"},
+                   "accumulation": "fp32", "decode_workers": args.workers or "default (8 per CU)"},
         "pct_hbm_peak": round(100 * kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "decode_kv_gbps": round(achieved, 2),
@@ -236,7 +236,7 @@ def main():
         "cache_write_us": round(float(write_ms.mean()) * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "pa_decode (partition + LSE reduce)"},
+                     "traffic": traffic, "kernel": "pa_decode (balanced split kernel + LSE combine kernel)"},
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -103,12 +103,12 @@ pa_status pa_copy_blocks(const pa_pool* pool, const int32_t* src_dst, int32_t nu
                          void* stream);
 
 /*
- * Workspace needed by pa_decode, in bytes, for the given sizes and partition
- * length (0 = the library's default). 0 means no workspace is needed.
+ * Workspace needed by pa_decode, in bytes, for these sizes and worker count
+ * (0 = the library's default: 8 wavefronts per compute unit of the current
+ * device). Returns 0 for invalid sizes.
  */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_blocks_per_seq, int32_t block_size,
-                                 int32_t partition_tokens);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t num_workers);
 
 /*
  * pa_decode — decode-step attention through the block tables.
@@ -116,25 +116,30 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * over the seq_lens[s] cached tokens of s, the newest token included
  * ("vLLM PagedAttention explained", section 3.3 step 2; kernel outline of
  * "LLM inference engine internals", section 2.4, whose softmax and V step are
- * completed here). Sequences are split into partitions of `partition_tokens`
- * tokens that are combined exactly by a log-sum-exp reduction.
+ * completed here). The work — every (sequence, KV head) cut into 16-token
+ * tiles — is split evenly over `num_workers` wavefronts; a sequence split
+ * between wavefronts is recombined exactly with the log-sum-exp rule.
  *   out          : device, [num_seqs][num_q_heads][head_dim], dtype of the pool
  *   q            : device, [num_seqs][num_q_heads][head_dim], dtype of the pool
  *   block_tables : device, int32 [num_seqs][max_blocks_per_seq]; only the first
  *                  ceil(seq_lens[s] / B) entries of a row are read
  *   seq_lens     : device, int32 [num_seqs], each in [0, max_blocks_per_seq * B];
  *                  a sequence of length 0 gets an all-zero output
- *   num_q_heads  : multiple of pool->num_kv_heads; group size <= 8 or a multiple of 8
+ *   num_q_heads  : multiple of pool->num_kv_heads
  *   scale        : softmax scale (typically 1/sqrt(head_dim))
- *   partition_tokens : 0 = default, else a multiple of 16 and of B
+ *   num_workers  : 0 = default; any positive count gives the same result up to
+ *                  fp32 rounding order
  *   workspace    : device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
- *                  aligned (may be NULL when that is 0); contents are scratch
+ *                  aligned; scratch (no contents are needed before or kept
+ *                  after a call). Calls that share a workspace must not overlap.
+ * Two kernels run on the stream: the split decode, then the combine of the
+ * partials of sequences that were split between wavefronts.
  * Accumulation is fp32 for both dtypes; bf16 output is rounded to nearest even.
  */
 pa_status pa_decode(void* out, const void* q, const pa_pool* pool,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                    float scale, int32_t partition_tokens,
+                    float scale, int32_t num_workers,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*

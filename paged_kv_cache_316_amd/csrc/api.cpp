@@ -15,7 +15,44 @@ namespace pa {
 namespace {
 thread_local char g_msg[512] = "";
 
-constexpr int32_t kDefaultPartitionTokens = 512;
+constexpr int32_t kWavesPerCU = 8;  // default decode workers per compute unit
+
+int32_t device_cus() {
+  static int32_t cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+      (void)hipGetLastError();
+      cus = 256;  // MI355X
+    }
+    cached = cus;
+  }
+  return cached;
+}
+
+int32_t default_workers() { return device_cus() * kWavesPerCU; }
+
+struct DecodeLayout {
+  int32_t workers, heads_per_unit, units;
+  size_t acc_bytes, ml_bytes, seg_bytes;
+  size_t total() const { return acc_bytes + ml_bytes + seg_bytes; }
+};
+
+DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t workers) {
+  DecodeLayout d{};
+  d.workers = workers > 0 ? workers : default_workers();
+  d.heads_per_unit = decode_heads_per_unit(num_q_heads / num_kv_heads);
+  d.units = num_q_heads / d.heads_per_unit;
+  const size_t slots = size_t(2) * d.workers * d.heads_per_unit;
+  d.acc_bytes = slots * head_dim * 4;
+  d.ml_bytes = slots * 8;
+  d.seg_bytes = size_t(d.workers) * 16;
+  (void)num_seqs;
+  return d;
+}
 
 bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -40,12 +77,6 @@ pa_status check_pool(const pa_pool* p, const char* who) {
 pa_status hip_status(hipError_t e, const char* who) {
   if (e == hipSuccess) return PA_OK;
   return fail(PA_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
-}
-
-int32_t effective_partition(int32_t requested, int32_t block_size) {
-  int32_t p = requested > 0 ? requested : kDefaultPartitionTokens;
-  const int32_t unit = block_size > 16 ? block_size : 16;
-  return ((p + unit - 1) / unit) * unit;
 }
 
 }  // namespace
@@ -118,23 +149,17 @@ pa_status pa_copy_blocks(const pa_pool* pool, const int32_t* src_dst, int32_t nu
   return PA_OK;
 }
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_blocks_per_seq, int32_t block_size,
-                                 int32_t partition_tokens) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
-      block_size <= 0)
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t num_workers) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_workers < 0 || num_q_heads % num_kv_heads)
     return 0;
-  const int32_t P = pa::effective_partition(partition_tokens, block_size);
-  const int64_t max_len = int64_t(max_blocks_per_seq) * block_size;
-  const int64_t max_parts = (max_len + P - 1) / P;
-  if (max_parts <= 1) return 0;
-  const int64_t rows = int64_t(num_seqs) * num_q_heads * max_parts;
-  return size_t(rows) * (size_t(head_dim) * 4 + 8);
+  return pa::decode_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers).total();
 }
 
 pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t* block_tables,
                     int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
-                    int32_t num_q_heads, float scale, int32_t partition_tokens, void* workspace,
+                    int32_t num_q_heads, float scale, int32_t num_workers, void* workspace,
                     size_t workspace_bytes, void* stream) {
   pa::clear_error();
   if (pa_status s = pa::check_pool(pool, "pa_decode")) return s;
@@ -142,17 +167,14 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t
     return fail(PA_ERR_INVALID, "pa_decode: num_seqs=%d max_blocks_per_seq=%d num_q_heads=%d",
                 num_seqs, max_blocks_per_seq, num_q_heads);
   if (num_seqs == 0) return PA_OK;
-  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "pa_decode: num_seqs=%d > 65535", num_seqs);
   if (!out || !q || !block_tables || !seq_lens)
     return fail(PA_ERR_INVALID, "pa_decode: out/q/block_tables/seq_lens is NULL");
   if (num_q_heads % pool->num_kv_heads)
     return fail(PA_ERR_INVALID, "pa_decode: num_q_heads=%d not a multiple of num_kv_heads=%d",
                 num_q_heads, pool->num_kv_heads);
   if (!(scale == scale)) return fail(PA_ERR_INVALID, "pa_decode: scale is NaN");
-  if (partition_tokens < 0 || (partition_tokens > 0 && (partition_tokens % 16 ||
-                                                        partition_tokens % pool->block_size)))
-    return fail(PA_ERR_INVALID, "pa_decode: partition_tokens=%d must be 0 or a multiple of 16 and of B=%d",
-                partition_tokens, pool->block_size);
+  if (num_workers < 0 || num_workers > (1 << 24))
+    return fail(PA_ERR_INVALID, "pa_decode: num_workers=%d out of range", num_workers);
   if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
        reinterpret_cast<uintptr_t>(pool->k_pool) | reinterpret_cast<uintptr_t>(pool->v_pool)) & 15)
     return fail(PA_ERR_INVALID, "pa_decode: out/q/pools must be 16-byte aligned");
@@ -160,23 +182,13 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t
   if (!pa::decode_supported(pool->dtype, pool->head_dim, G))
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: dtype=%d head_dim=%d group=%d not built",
                 pool->dtype, pool->head_dim, G);
-  const int32_t P = pa::effective_partition(partition_tokens, pool->block_size);
-  if (P / pool->block_size > 1024)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: partition of %d tokens spans > 1024 blocks", P);
-  const int64_t max_len = int64_t(max_blocks_per_seq) * pool->block_size;
-  const int64_t max_parts = (max_len + P - 1) / P;
-  if (max_parts > 2147483647LL)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: too many partitions");
-  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim,
-                                                max_blocks_per_seq, pool->block_size,
-                                                partition_tokens);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need)
-      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes, %zu needed",
-                  workspace ? workspace_bytes : size_t(0), need);
-    if (reinterpret_cast<uintptr_t>(workspace) & 15)
-      return fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
-  }
+  const pa::DecodeLayout lay =
+      pa::decode_layout(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim, num_workers);
+  if (!workspace || workspace_bytes < lay.total())
+    return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes, %zu needed",
+                workspace ? workspace_bytes : size_t(0), lay.total());
+  if (reinterpret_cast<uintptr_t>(workspace) & 15)
+    return fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
   pa::DecodeArgs a{};
   a.out = out;
   a.q = q;
@@ -184,11 +196,10 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t
   a.v_pool = pool->v_pool;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
-  const int64_t rows = int64_t(num_seqs) * num_q_heads * max_parts;
-  a.ws_acc = need ? static_cast<float*>(workspace) : nullptr;
-  a.ws_ml = need ? reinterpret_cast<float2*>(static_cast<char*>(workspace) +
-                                             size_t(rows) * pool->head_dim * 4)
-                 : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_acc = reinterpret_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float2*>(ws + lay.acc_bytes);
+  a.ws_seg = reinterpret_cast<int4*>(ws + lay.acc_bytes + lay.ml_bytes);
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -196,8 +207,8 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t
   a.head_dim = pool->head_dim;
   a.block_size = pool->block_size;
   a.dtype = pool->dtype;
-  a.partition_tokens = P;
-  a.max_parts = int32_t(max_parts);
+  a.workers = lay.workers;
+  a.num_cus = pa::device_cus();
   a.scale = scale;
   return pa::hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)), "pa_decode");
 }

@@ -10,27 +10,37 @@
 // (the request sees contiguous KV; the lookup translates addresses).
 //
 // How (MI355X design, not the outline's):
-//  * One wavefront owns (sequence, KV head, partition of P tokens) and all the
-//    query heads that share that KV head (grouped heads), so each K/V row is
-//    read from HBM once per step.
+//  * Work list. A segment is (sequence, head unit), where a head unit is a KV
+//    head together with up to 8 of the query heads that read it, so each K/V
+//    row is read from HBM once per step. Segment (s, u) is cut into 16-token
+//    tiles; all tiles of all segments form one list, ordered by sequence,
+//    then unit, then tile, and each of W wavefronts takes an equal contiguous
+//    slice of it. Ragged lengths therefore cost nothing in balance: every
+//    wave streams the same number of bytes, and no workgroup is launched
+//    empty. Each wave finds its slice from a prefix sum of the tile counts
+//    of all sequences, computed at its start.
 //  * Lane layout: a token row of D elements is LPR lanes x 16 bytes; a
 //    wave-wide 16-byte load covers NR = 64 / LPR token rows (bf16, D = 128:
-//    16 lanes per row, 4 rows per load, 4 loads per 16-token tile). Loads are
-//    fully coalesced 16-byte accesses.
+//    16 lanes per row, 4 rows per load, 4 loads per tile). All K/V loads are
+//    fully coalesced 16-byte accesses, marked non-temporal.
+//  * Block-table entries are fetched two tiles ahead of use and the K/V of
+//    the next tile are in flight while the current tile is computed, across
+//    segment boundaries.
 //  * q.k: per-lane partial dot over its 16 bytes (v_dot2 for bf16), then a
 //    sum over the LPR lanes of the row with DPP (quad_perm, row_half_mirror,
 //    row_mirror).
 //  * Online softmax in base 2, kept per row group (lanes with the same token
 //    row index), so the hot loop has no cross-row traffic; the NR row groups
-//    are merged once per partition.
-//  * The block-table slice of the partition is staged once per workgroup in
-//    LDS and shared by its four waves (four KV heads of one sequence).
-//  * Tiles are double-buffered: the K/V loads of tile i+1 are in flight while
-//    tile i is computed.
-//  * Sequences longer than P are split into partitions; each writes
-//    (max, denominator, unnormalised sum) and a second kernel combines them
-//    with the log-sum-exp rule. A sequence with one partition writes its
-//    output directly.
+//    are merged when a segment ends.
+//  * A segment that lies inside one wave's slice is finished by that wave.
+//    A segment split between waves leaves one partial (running max,
+//    denominator, unnormalised sum) per wave, and its first wave records
+//    where it is. A second, small kernel then combines each split segment's
+//    partials with the log-sum-exp rule M = max m_p,
+//    out = sum 2^(m_p-M) acc_p / sum 2^(m_p-M) l_p. Doing this after the
+//    kernel boundary needs no atomics or device-wide fences: on this chip a
+//    device-scope fence writes back and invalidates a whole L2, and issuing
+//    one per split segment cost more than a third of the bandwidth.
 #include <math.h>
 
 #include "device.h"
@@ -38,18 +48,9 @@
 namespace pa {
 namespace {
 
-constexpr int kWavesPerGroup = 4;
-constexpr int kTile = 16;             // tokens per wave iteration
-constexpr int kMaxPartBlocks = 1024;  // LDS table-slice capacity (P / B)
+constexpr int kMaxWavesPerGroup = 8;  // one workgroup per CU holds that CU's waves
+constexpr int kTile = 16;  // tokens per tile
 constexpr float kLog2e = 1.4426950408889634f;
-
-template <int DTYPE, int D, int HPW>
-struct Tile {
-  using RS = RowShape<DTYPE, D>;
-  static constexpr int VEC = RS::VEC, LPR = RS::LPR, NR = RS::NR;
-  static constexpr int U = kTile / NR;  // 16-byte loads per lane per tile, for K and for V
-  static_assert(kTile % NR == 0, "tile must cover whole load rows");
-};
 
 typedef short bf16x2_t __attribute__((__vector_size__(2 * sizeof(short))));
 
@@ -95,7 +96,7 @@ __device__ __forceinline__ void unpack16<PA_BF16>(const uint4& v, float* f) {
   f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
-// Store VEC fp32 values as one 16-byte chunk of the output dtype.
+// VEC fp32 values as one 16-byte chunk of the output dtype.
 template <int DTYPE>
 __device__ __forceinline__ uint4 pack16(const float* f);
 
@@ -111,50 +112,128 @@ __device__ __forceinline__ uint4 pack16<PA_BF16>(const float* f) {
                     pack_bf16(f[6], f[7]));
 }
 
-template <int DTYPE, int D, int HPW>
-__global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_partition_kernel(
-    DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
-  using TL = Tile<DTYPE, D, HPW>;
-  constexpr int VEC = TL::VEC, LPR = TL::LPR, NR = TL::NR, U = TL::U;
-  constexpr int ELT = Elt<DTYPE>::bytes;
-  __shared__ int32_t s_bt[kMaxPartBlocks];
+__device__ __forceinline__ int tiles_of(int L) { return L > 0 ? (L + kTile - 1) / kTile : 0; }
 
-  const int part = blockIdx.x;
-  const int seq = blockIdx.z;
-  const int L = a.seq_lens[seq];
-  const int P = a.partition_tokens;
-  const int start = part * P;
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+// Position of one tile in the work list: tile j of segment (sequence s, unit u);
+// unit u reads KV head kvh; the sequence has n tiles and L tokens; seg0 = list
+// index of the segment's tile 0. All fields are wave-uniform.
+struct Cursor {
+  int s, u, kvh, hc, j, n, L;
+  int64_t seg0;
+};
+
+template <int DTYPE, int D, int HPW, bool BIG_B>
+__global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_kernel(
+    DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
+  using RS = RowShape<DTYPE, D>;
+  constexpr int VEC = RS::VEC, LPR = RS::LPR, NR = RS::NR;
+  constexpr int U = kTile / NR;  // 16-byte loads per lane per tile, for K and for V
+  static_assert(kTile % NR == 0, "a tile must cover whole load rows");
+  constexpr int QF = VEC > 4 ? 4 : VEC;
+
+  const int lane = threadIdx.x % kWave;
+  const int w = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int S = a.num_seqs;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int unit = blockIdx.y * kWavesPerGroup + wave;
-  const int kvh = unit / n_hchunk;
-  const int head0 = kvh * G + (unit % n_hchunk) * HPW;
-  const bool active = kvh < Hkv;
+  const int units = Hkv * n_hchunk;
   const int r = lane / LPR, c = lane % LPR;
+  const int B = a.block_size, Bm1 = B - 1;
+  if (w >= a.workers) return;
 
-  if (L <= 0) {  // empty sequence: output zeros
-    if (part == 0 && active && r == 0) {
-      uint4* o = static_cast<uint4*>(a.out) + ((int64_t(seq) * Hq + head0) * D) / VEC + c;
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) o[hh * (D / VEC)] = make_uint4(0, 0, 0, 0);
-    }
+  // ---- the work list: total tiles, this wave's slice -----------------------
+  int64_t total = 0;
+  for (int base = 0; base < S; base += kWave) {
+    const int s = base + lane;
+    total += wave_sum_i32(s < S ? tiles_of(a.seq_lens[s]) : 0);
+  }
+  total = uniform64(total * units);
+  const int64_t W = total < a.workers ? total : a.workers;  // every active wave gets >= 1 tile
+
+  // empty sequences: zeros, written by wave (s mod Wz)
+  const int Wz = W > 0 ? int(W) : a.workers;
+  for (int s = w; s < S; s += Wz) {
+    if (a.seq_lens[s] > 0) continue;
+    uint4* o = static_cast<uint4*>(a.out) + (int64_t(s) * Hq * D) / VEC;
+    for (int i = lane; i < Hq * D / VEC; i += kWave) o[i] = make_uint4(0, 0, 0, 0);
+  }
+  if (w >= W) {
+    if (lane == 0) a.ws_seg[w] = make_int4(-1, 0, 0, 0);
     return;
   }
-  if (start >= L) return;  // uniform over the workgroup
-  const int end = min(L, start + P);
-  const int first_blk = start >> b_shift;
-  const int nblk = ((end - 1) >> b_shift) - first_blk + 1;
-  const int32_t* bt_row = a.block_tables + int64_t(seq) * a.max_blocks_per_seq + first_blk;
-  for (int i = threadIdx.x; i < nblk; i += blockDim.x) s_bt[i] = bt_row[i];
-  __syncthreads();
-  if (!active) return;
+  const int64_t g_begin = total * w / W, g_end = total * (w + 1) / W;
 
-  // This lane's slice of the HPW query heads.
-  float qf[HPW][VEC > 4 ? 4 : VEC];
-  uint4 qb[HPW];
+  // lengths of 64 consecutive sequences, one per lane, read with v_readlane so
+  // that moving to the next sequence issues no memory load in the common case
+  int lwin_base = S, lwin = 0;
+  auto seq_len = [&](int s) -> int {
+    if (s - lwin_base >= kWave || s < lwin_base) {
+      lwin_base = s;
+      lwin = s + lane < S ? a.seq_lens[s + lane] : 0;
+    }
+    return __builtin_amdgcn_readlane(lwin, s - lwin_base);
+  };
+
+  // locate g_begin: the sequence whose tiles (times units) contain it
+  Cursor cur{};
   {
-    const uint4* qp = static_cast<const uint4*>(a.q) + ((int64_t(seq) * Hq + head0) * D) / VEC + c;
+    int64_t before = 0;  // tiles x units before this chunk of sequences
+    for (int base = 0; base < S; base += kWave) {
+      const int s = base + lane;
+      const int t = s < S ? tiles_of(a.seq_lens[s]) : 0;
+      const int64_t incl = before + int64_t(wave_incl_scan_i32(t, lane)) * units;
+      const int64_t excl = incl - int64_t(t) * units;
+      const unsigned long long hit = __ballot(s < S && t > 0 && excl <= g_begin && g_begin < incl);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        const int64_t seq0 = uniform64(__shfl(excl, l));
+        cur.s = base + l;
+        cur.n = __builtin_amdgcn_readfirstlane(__shfl(t, l));
+        cur.L = seq_len(cur.s);
+        const int64_t off = g_begin - seq0;
+        cur.u = int(off / cur.n);
+        cur.j = int(off - int64_t(cur.u) * cur.n);
+        cur.kvh = cur.u / n_hchunk;
+        cur.hc = cur.u - cur.kvh * n_hchunk;
+        cur.seg0 = seq0 + int64_t(cur.u) * cur.n;
+        break;
+      }
+      before = uniform64(__shfl(incl, kWave - 1));
+    }
+  }
+
+  const uint4* kp = static_cast<const uint4*>(a.k_pool);
+  const uint4* vp = static_cast<const uint4*>(a.v_pool);
+  const int64_t block_chunks = int64_t(Hkv) * B * LPR;  // 16-byte chunks per physical block
+
+  // ---- per-segment state ------------------------------------------------------
+  float qf[HPW][QF];
+  uint4 qb[HPW];
+  float m[HPW], l[HPW], acc[HPW][VEC];
+  auto head_of = [&](const Cursor& x) { return x.kvh * G + x.hc * HPW; };
+  auto begin_segment = [&](const Cursor& x) {
+    const uint4* qp = static_cast<const uint4*>(a.q) + ((int64_t(x.s) * Hq + head_of(x)) * D) / VEC + c;
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       qb[hh] = qp[hh * (D / VEC)];
@@ -164,61 +243,23 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_partition_kerne
         qf[hh][2] = __uint_as_float(qb[hh].z) * scale_log2;
         qf[hh][3] = __uint_as_float(qb[hh].w) * scale_log2;
       }
+      m[hh] = -INFINITY;
+      l[hh] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[hh][e] = 0.f;
     }
-  }
+  };
   const float zmul = DTYPE == PA_F32 ? 1.f : scale_log2;
 
-  float m[HPW], l[HPW], acc[HPW][VEC];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[hh][e] = 0.f;
-  }
-
-  const uint4* kp = static_cast<const uint4*>(a.k_pool);
-  const uint4* vp = static_cast<const uint4*>(a.v_pool);
-  const int Bm1 = a.block_size - 1;
-  const int64_t head_rows = int64_t(Hkv) * a.block_size;
-
-  auto chunk_index = [&](int lt) -> int64_t {
-    const int64_t pb = s_bt[(lt >> b_shift) - first_blk];
-    return ((pb * Hkv + kvh) * a.block_size + (lt & Bm1)) * LPR + c;
-  };
-  (void)head_rows;
-
-  auto load_full = [&](int base, uint4* kr, uint4* vr) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t idx = chunk_index(base + u * NR + r);
-      kr[u] = load_stream16(kp + idx);
-      vr[u] = load_stream16(vp + idx);
-    }
-  };
-  auto load_tail = [&](int base, uint4* kr, uint4* vr) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int lt = base + u * NR + r;
-      if (lt < end) {
-        const int64_t idx = chunk_index(lt);
-        kr[u] = load_stream16(kp + idx);
-        vr[u] = load_stream16(vp + idx);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto compute = [&](int base, const uint4* kr, const uint4* vr, bool masked) {
+  auto compute = [&](int j, int L, const uint4* kr, const uint4* vr) {
     float z[HPW][U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool valid = !masked || (base + u * NR + r < end);
+    for (int uu = 0; uu < U; ++uu) {
+      const bool valid = j * kTile + uu * NR + r < L;
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        const float s = group_sum<LPR>(dot16<DTYPE>(kr[u], qf[hh], qb[hh])) * zmul;
-        z[hh][u] = valid ? s : -INFINITY;
+        const float sv = group_sum<LPR>(dot16<DTYPE>(kr[uu], qf[hh], qb[hh])) * zmul;
+        z[hh][uu] = valid ? sv : -INFINITY;
       }
     }
     float p[HPW][U];
@@ -226,131 +267,215 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void decode_partition_kerne
     for (int hh = 0; hh < HPW; ++hh) {
       float mx = z[hh][0];
 #pragma unroll
-      for (int u = 1; u < U; ++u) mx = fmaxf(mx, z[hh][u]);
+      for (int uu = 1; uu < U; ++uu) mx = fmaxf(mx, z[hh][uu]);
       const float mn = fmaxf(m[hh], mx);
       const float ms = mn == -INFINITY ? 0.f : mn;
       const float alpha = __builtin_amdgcn_exp2f(m[hh] - ms);
       m[hh] = mn;
       float lsum = l[hh] * alpha;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        p[hh][u] = __builtin_amdgcn_exp2f(z[hh][u] - ms);
-        lsum += p[hh][u];
+      for (int uu = 0; uu < U; ++uu) {
+        p[hh][uu] = __builtin_amdgcn_exp2f(z[hh][uu] - ms);
+        lsum += p[hh][uu];
       }
       l[hh] = lsum;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc[hh][e] *= alpha;
     }
+    // clamped rows hold a real token's V, finite, and their weight p is 0
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int uu = 0; uu < U; ++uu) {
       float vf[VEC];
-      unpack16<DTYPE>(vr[u], vf);
+      unpack16<DTYPE>(vr[uu], vf);
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[hh][e] = fmaf(p[hh][u], vf[e], acc[hh][e]);
+        for (int e = 0; e < VEC; ++e) acc[hh][e] = fmaf(p[hh][uu], vf[e], acc[hh][e]);
     }
   };
 
-  const int ntok = end - start;
-  const int nfull = ntok / kTile;
-  uint4 ka[U], va[U], kb[U], vb[U];
-  int it = 0;
-  if (nfull > 0) load_full(start, ka, va);
-  for (; it + 2 <= nfull; it += 2) {
-    load_full(start + (it + 1) * kTile, kb, vb);
-    compute(start + it * kTile, ka, va, false);
-    if (it + 2 < nfull) load_full(start + (it + 2) * kTile, ka, va);
-    compute(start + (it + 1) * kTile, kb, vb, false);
-  }
-  if (it < nfull) {  // one full tile left, already in ka/va
-    compute(start + it * kTile, ka, va, false);
-    ++it;
-  }
-  if (ntok % kTile) {
-    load_tail(start + it * kTile, kb, vb);
-    compute(start + it * kTile, kb, vb, true);
-  }
+  // merge the NR row groups, then write the output or this wave's partial
+  auto end_segment = [&](const Cursor& x, bool owns_start, bool owns_end) {
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const float mo = __shfl_xor(m[hh], off);
+        const float lo = __shfl_xor(l[hh], off);
+        const float mn = fmaxf(m[hh], mo);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        const float fa = __builtin_amdgcn_exp2f(m[hh] - ms);
+        const float fb = __builtin_amdgcn_exp2f(mo - ms);
+        l[hh] = l[hh] * fa + lo * fb;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          acc[hh][e] = acc[hh][e] * fa + __shfl_xor(acc[hh][e], off) * fb;
+        m[hh] = mn;
+      }
+    }
+    uint4* o = static_cast<uint4*>(a.out) + ((int64_t(x.s) * Hq + head_of(x)) * D) / VEC + c;
+    if (owns_start && owns_end) {  // whole segment in this wave
+      if (r == 0) {
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          const float inv = 1.f / l[hh];
+          float f[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) f[e] = acc[hh][e] * inv;
+          o[hh * (D / VEC)] = pack16<DTYPE>(f);
+        }
+      }
+      return;
+    }
+    // split segment: this wave's partial goes to slot 2w (segment began before
+    // the slice) or 2w+1 (segment continues after the slice)
+    const int slot = 2 * w + (owns_start ? 1 : 0);
+    if (r == 0) {
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        float4* dst = reinterpret_cast<float4*>(a.ws_acc + (int64_t(slot) * HPW + hh) * D + c * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4)
+          dst[e / 4] = make_float4(acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]);
+        if (c == 0) a.ws_ml[int64_t(slot) * HPW + hh] = make_float2(m[hh], l[hh]);
+      }
+    }
+  };
 
-  // Merge the NR row groups: each holds the softmax state of its own tokens.
+  // Tiles [j0, j1) of one segment, in chunks whose blocks fit a 64-entry window
+  // of the block table (one entry per lane, read back with v_readlane / a lane
+  // shuffle). Inside a chunk the loop is branch-free and double-buffered:
+  // tile j+1 is loading while tile j is computed. Rows past the end of the
+  // sequence are clamped to its last token (a valid, written slot) and masked
+  // out in compute, so no load sits under divergent control flow.
+  auto run_tiles = [&](const Cursor& x, int j0, int j1) {
+    const int32_t* row = a.block_tables + int64_t(x.s) * a.max_blocks_per_seq;
+    const int nblk = (x.L + Bm1) >> b_shift;
+    const int Lm1 = x.L - 1;
+    for (int jc = j0; jc < j1;) {
+      const int jb0 = (jc * kTile) >> b_shift;
+      const int win = jb0 + lane < nblk ? row[jb0 + lane] : 0;
+      const int jc_end = min(j1, ((jb0 + kWave) << b_shift) / kTile);
+      auto load_tile = [&](int j, uint4* kr, uint4* vr) {
+        if constexpr (BIG_B) {
+          const int pb = __builtin_amdgcn_readlane(win, ((j * kTile) >> b_shift) - jb0);
+          const int64_t blk = int64_t(pb) * block_chunks;
+          const uint4* kb = kp + blk;
+          const uint4* vb = vp + blk;
 #pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1) {
+          for (int uu = 0; uu < U; ++uu) {
+            const int t = min(j * kTile + uu * NR + r, Lm1);
+            const int off = (x.kvh * B + (t & Bm1)) * LPR + c;
+            kr[uu] = load_stream16(kb + off);
+            vr[uu] = load_stream16(vb + off);
+          }
+        } else {
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const float mo = __shfl_xor(m[hh], off);
-      const float lo = __shfl_xor(l[hh], off);
-      const float mn = fmaxf(m[hh], mo);
-      const float ms = mn == -INFINITY ? 0.f : mn;
-      const float fa = __builtin_amdgcn_exp2f(m[hh] - ms);
-      const float fb = __builtin_amdgcn_exp2f(mo - ms);
-      l[hh] = l[hh] * fa + lo * fb;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[hh][e] = acc[hh][e] * fa + __shfl_xor(acc[hh][e], off) * fb;
-      m[hh] = mn;
+          for (int uu = 0; uu < U; ++uu) {
+            const int t = min(j * kTile + uu * NR + r, Lm1);
+            const int pb = __shfl(win, (t >> b_shift) - jb0);
+            const int64_t idx = int64_t(pb) * block_chunks + (x.kvh * B + (t & Bm1)) * LPR + c;
+            kr[uu] = load_stream16(kp + idx);
+            vr[uu] = load_stream16(vp + idx);
+          }
+        }
+      };
+      uint4 kA[U], vA[U], kB[U], vB[U];
+      int j = jc;
+      load_tile(j, kA, vA);
+      for (; j + 2 <= jc_end; j += 2) {
+        load_tile(j + 1, kB, vB);
+        __builtin_amdgcn_sched_barrier(0);  // keep the next tile's loads ahead of this math
+        compute(j, x.L, kA, vA);
+        if (j + 2 < jc_end) load_tile(j + 2, kA, vA);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(j + 1, x.L, kB, vB);
+      }
+      if (j < jc_end) compute(j, x.L, kA, vA);  // odd count: last tile already in A
+      jc = jc_end;
     }
-  }
-  if (r != 0) return;
+  };
 
-  const int nparts = (L + P - 1) / P;
-  if (nparts == 1) {
-    uint4* o = static_cast<uint4*>(a.out) + ((int64_t(seq) * Hq + head0) * D) / VEC + c;
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const float inv = 1.f / l[hh];
-      float f[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) f[e] = acc[hh][e] * inv;
-      o[hh * (D / VEC)] = pack16<DTYPE>(f);
+  // ---- walk the segments of this slice ------------------------------------------
+  int64_t g = g_begin;
+  int4 split = make_int4(-1, 0, 0, 0);  // the segment this slice starts and leaves unfinished
+  while (true) {
+    const int j1 = int(min(int64_t(cur.n), int64_t(cur.j) + (g_end - g)));
+    const bool owns_start = cur.j == 0, owns_end = j1 == cur.n;
+    begin_segment(cur);
+    run_tiles(cur, cur.j, j1);
+    end_segment(cur, owns_start, owns_end);
+    if (owns_start && !owns_end) {  // only the last segment of a slice can be left open
+      const int64_t last = cur.seg0 + cur.n - 1;
+      split = make_int4(cur.s, cur.u, int(((last + 1) * W - 1) / total), head_of(cur));
     }
-  } else {
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const int64_t row = (int64_t(seq) * Hq + head0 + hh) * a.max_parts + part;
-      float4* w = reinterpret_cast<float4*>(a.ws_acc + row * D + c * VEC);
-#pragma unroll
-      for (int e = 0; e < VEC; e += 4)
-        w[e / 4] = make_float4(acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]);
-      if (c == 0) a.ws_ml[row] = make_float2(m[hh], l[hh]);
+    g += j1 - cur.j;
+    if (g >= g_end) break;
+    // next segment: next unit of this sequence, or the next non-empty sequence
+    cur.j = 0;
+    cur.seg0 += cur.n;
+    ++cur.u;
+    if (++cur.hc == n_hchunk) {
+      cur.hc = 0;
+      ++cur.kvh;
+    }
+    if (cur.u == units) {
+      cur.u = cur.kvh = cur.hc = 0;
+      do {
+        ++cur.s;
+        cur.L = seq_len(cur.s);
+        cur.n = tiles_of(cur.L);
+      } while (cur.n == 0);
     }
   }
-  (void)ELT;
+  if (lane == 0) a.ws_seg[w] = split;
 }
 
-// Log-sum-exp combination of the partitions of one (sequence, head):
-// M = max_p m_p; out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
-template <int DTYPE, int D>
-__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a) {
-  constexpr int PER = D / kWave;
-  const int h = blockIdx.x, seq = blockIdx.y;
-  const int L = a.seq_lens[seq];
-  const int P = a.partition_tokens;
-  const int np = (L + P - 1) / P;
-  if (np <= 1) return;
-  const int64_t row0 = (int64_t(seq) * a.num_q_heads + h) * a.max_parts;
-  const float2* ml = a.ws_ml + row0;
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[p].x);
-  float den = 0.f, num[PER];
+// Combine the partials of each split segment. Wave w looks at the segment
+// that wave w of the decode kernel started and left open (if any); its
+// partials are in slot 2w+1 (wave w) and slots 2v for the waves v in
+// (w, last] that continued it.
+template <int DTYPE, int D, int HPW>
+__global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kernel(DecodeArgs a) {
+  using RS = RowShape<DTYPE, D>;
+  constexpr int VEC = RS::VEC, LPR = RS::LPR;
+  const int lane = threadIdx.x % kWave;
+  const int w = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (w >= a.workers) return;
+  const int4 seg = a.ws_seg[w];
+  if (seg.x < 0) return;
+  const int wb = seg.z, head0 = seg.w;
+  // one lane group of LPR lanes per query head of the unit
+  for (int hh = lane / LPR; hh < HPW; hh += kWave / LPR) {
+    const int c = lane % LPR;
+    float M = -INFINITY;
+    for (int v = w; v <= wb; ++v) {
+      const int sl = v == w ? 2 * v + 1 : 2 * v;
+      M = fmaxf(M, a.ws_ml[int64_t(sl) * HPW + hh].x);
+    }
+    float den = 0.f, num[VEC];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) num[j] = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float2 v = ml[p];
-    const float w = __builtin_amdgcn_exp2f(v.x - M);
-    den = fmaf(v.y, w, den);
-    const float* src = a.ws_acc + (row0 + p) * D + threadIdx.x * PER;
+    for (int e = 0; e < VEC; ++e) num[e] = 0.f;
+    for (int v = w; v <= wb; ++v) {
+      const int sl = v == w ? 2 * v + 1 : 2 * v;
+      const float2 ml = a.ws_ml[int64_t(sl) * HPW + hh];
+      const float f = __builtin_amdgcn_exp2f(ml.x - M);
+      den = fmaf(ml.y, f, den);
+      const float4* src = reinterpret_cast<const float4*>(a.ws_acc + (int64_t(sl) * HPW + hh) * D + c * VEC);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) num[j] = fmaf(src[j], w, num[j]);
-  }
-  const float inv = 1.f / den;
-  const int64_t o = (int64_t(seq) * a.num_q_heads + h) * D + threadIdx.x * PER;
-  if constexpr (DTYPE == PA_F32) {
-    float* out = static_cast<float*>(a.out) + o;
+      for (int e = 0; e < VEC; e += 4) {
+        const float4 x = src[e / 4];
+        num[e] = fmaf(x.x, f, num[e]);
+        num[e + 1] = fmaf(x.y, f, num[e + 1]);
+        num[e + 2] = fmaf(x.z, f, num[e + 2]);
+        num[e + 3] = fmaf(x.w, f, num[e + 3]);
+      }
+    }
+    const float inv = 1.f / den;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) out[j] = num[j] * inv;
-  } else {
-    uint16_t* out = static_cast<uint16_t*>(a.out) + o;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) out[j] = uint16_t(f32_to_bf16(num[j] * inv));
+    for (int e = 0; e < VEC; ++e) num[e] *= inv;
+    uint4* o = static_cast<uint4*>(a.out) + ((int64_t(seg.x) * a.num_q_heads + head0 + hh) * D) / VEC + c;
+    *o = pack16<DTYPE>(num);
   }
 }
 
@@ -358,28 +483,29 @@ template <int DTYPE, int D, int HPW>
 hipError_t run(const DecodeArgs& a, hipStream_t st) {
   int b_shift = 0;
   while ((1 << b_shift) < a.block_size) ++b_shift;
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int n_hchunk = G / HPW;
-  const int units = a.num_kv_heads * n_hchunk;
-  dim3 grid(a.max_parts, (units + kWavesPerGroup - 1) / kWavesPerGroup, a.num_seqs);
+  const int n_hchunk = (a.num_q_heads / a.num_kv_heads) / HPW;
+  // Persistent waves: size workgroups so that there is about one per compute
+  // unit; the dispatcher then spreads the waves evenly over the chip.
+  const int cus = a.num_cus > 0 ? a.num_cus : 1;
+  int wpg = (a.workers + cus - 1) / cus;
+  wpg = wpg < 1 ? 1 : (wpg > kMaxWavesPerGroup ? kMaxWavesPerGroup : wpg);
+  const int groups = (a.workers + wpg - 1) / wpg;
   const float scale_log2 = a.scale * kLog2e;
-  decode_partition_kernel<DTYPE, D, HPW>
-      <<<grid, kWave * kWavesPerGroup, 0, st>>>(a, b_shift, n_hchunk, scale_log2);
+  if (a.block_size >= kTile)
+    decode_balanced_kernel<DTYPE, D, HPW, true>
+        <<<groups, kWave * wpg, 0, st>>>(a, b_shift, n_hchunk, scale_log2);
+  else
+    decode_balanced_kernel<DTYPE, D, HPW, false>
+        <<<groups, kWave * wpg, 0, st>>>(a, b_shift, n_hchunk, scale_log2);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_parts <= 1) return e;
-  decode_reduce_kernel<DTYPE, D><<<dim3(a.num_q_heads, a.num_seqs), kWave, 0, st>>>(a);
+  if (e != hipSuccess) return e;
+  decode_combine_kernel<DTYPE, D, HPW><<<groups, kWave * wpg, 0, st>>>(a);
   return hipGetLastError();
-}
-
-int heads_per_wave(int G) {
-  for (int h : {8, 4, 2, 1})
-    if (G % h == 0) return h;
-  return 1;
 }
 
 template <int DTYPE, int D>
 hipError_t run_d(const DecodeArgs& a, hipStream_t st) {
-  switch (heads_per_wave(a.num_q_heads / a.num_kv_heads)) {
+  switch (decode_heads_per_unit(a.num_q_heads / a.num_kv_heads)) {
     case 8: return run<DTYPE, D, 8>(a, st);
     case 4: return run<DTYPE, D, 4>(a, st);
     case 2: return run<DTYPE, D, 2>(a, st);
@@ -389,13 +515,18 @@ hipError_t run_d(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
+int decode_heads_per_unit(int group) {
+  for (int h : {8, 4, 2, 1})
+    if (group % h == 0) return h;
+  return 1;
+}
+
 bool decode_supported(int dtype, int head_dim, int group) {
   return (dtype == PA_F32 || dtype == PA_BF16) && (head_dim == 64 || head_dim == 128) &&
          group >= 1;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  if (a.partition_tokens / a.block_size > kMaxPartBlocks) return hipErrorInvalidValue;
   if (a.dtype == PA_BF16) {
     if (a.head_dim == 128) return run_d<PA_BF16, 128>(a, st);
     if (a.head_dim == 64) return run_d<PA_BF16, 64>(a, st);

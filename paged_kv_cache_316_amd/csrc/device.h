@@ -76,11 +76,13 @@ struct DecodeArgs {
   const void* v_pool;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* ws_acc;   // [S][Hq][max_parts][D] unnormalised partial sums
-  float2* ws_ml;   // [S][Hq][max_parts] (running max in log2 units, denominator)
+  float* ws_acc;   // [2 * workers][heads per unit][D] unnormalised partial sums
+  float2* ws_ml;   // [2 * workers][heads per unit] (running max in log2 units, denominator)
+  int4* ws_seg;    // [workers] split segment each wave started: (seq, unit, last wave, head)
   int32_t max_blocks_per_seq;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
-  int32_t partition_tokens, max_parts;
+  int32_t workers;
+  int32_t num_cus;  // compute units of the device (sizes the workgroups)
   float scale;
 };
 
@@ -91,6 +93,8 @@ hipError_t launch_copy_blocks(const pa_pool& pool, const int32_t* src_dst, int32
 // Returns hipErrorInvalidValue for shapes without a compiled kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 bool decode_supported(int dtype, int head_dim, int group);
+// Query heads handled together with their KV head by one wave (divides the group size).
+int decode_heads_per_unit(int group);
 
 struct PrefillArgs {
   void* out;

@@ -82,32 +82,27 @@ def copy_blocks(pool: KVPool, src_dst: torch.Tensor) -> None:
     check(lib().pa_copy_blocks(ctypes.byref(pool.c), _ptr(src_dst), n, _stream()))
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
-                           max_blocks_per_seq: int, block_size: int,
-                           partition_tokens: int = 0) -> int:
-    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                               max_blocks_per_seq, block_size, partition_tokens))
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           workers: int = 0) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                               workers))
 
 
 class DecodePlan:
-    """Output and workspace buffers for repeated decode calls of one shape."""
+    """Output and workspace for repeated decode calls of one shape."""
 
-    def __init__(self, pool: KVPool, num_seqs: int, num_q_heads: int, max_blocks_per_seq: int,
-                 partition_tokens: int = 0):
+    def __init__(self, pool: KVPool, num_seqs: int, num_q_heads: int, workers: int = 0):
         self.pool = pool
-        self.num_seqs, self.num_q_heads = num_seqs, num_q_heads
-        self.max_blocks_per_seq = max_blocks_per_seq
-        self.partition_tokens = partition_tokens
+        self.num_seqs, self.num_q_heads, self.workers = num_seqs, num_q_heads, workers
         self.out = torch.empty((num_seqs, num_q_heads, pool.head_dim), dtype=pool.dtype,
                                device=pool.k.device)
-        nbytes = decode_workspace_bytes(num_seqs, num_q_heads, pool.head_dim, max_blocks_per_seq,
-                                        pool.block_size, partition_tokens)
-        self.workspace = (torch.empty(nbytes, dtype=torch.uint8, device=pool.k.device)
-                          if nbytes else None)
+        nbytes = decode_workspace_bytes(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim,
+                                        workers)
+        self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=pool.k.device)
 
 
 def decode(q: torch.Tensor, pool: KVPool, block_tables: torch.Tensor, seq_lens: torch.Tensor,
-           scale: float, partition_tokens: int = 0, plan: Optional[DecodePlan] = None,
+           scale: float, workers: int = 0, plan: Optional[DecodePlan] = None,
            out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Paged decode attention. q [S, Hq, D]; block_tables int32 [S, maxB]; seq_lens int32 [S]."""
     _need(q, "q", pool.dtype)
@@ -117,20 +112,17 @@ def decode(q: torch.Tensor, pool: KVPool, block_tables: torch.Tensor, seq_lens: 
     if D != pool.head_dim or block_tables.dim() != 2 or block_tables.shape[0] != S \
             or seq_lens.shape != (S,):
         raise ValueError("shape mismatch between q, block_tables and seq_lens")
-    maxb = block_tables.shape[1]
     if plan is None:
-        plan = DecodePlan(pool, S, Hq, maxb, partition_tokens)
-    elif (plan.num_seqs, plan.num_q_heads, plan.max_blocks_per_seq, plan.partition_tokens) != \
-            (S, Hq, maxb, partition_tokens):
+        plan = DecodePlan(pool, S, Hq, workers)
+    elif (plan.num_seqs, plan.num_q_heads, plan.workers, plan.pool) != (S, Hq, workers, pool):
         raise ValueError("plan does not match this call")
     if out is None:
         out = plan.out
     _need(out, "out", pool.dtype)
     ws = plan.workspace
     check(lib().pa_decode(out.data_ptr(), q.data_ptr(), ctypes.byref(pool.c),
-                          block_tables.data_ptr(), maxb, seq_lens.data_ptr(), S, Hq,
-                          float(scale), int(partition_tokens), _ptr(ws),
-                          0 if ws is None else ws.numel(), _stream()))
+                          block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(), S,
+                          Hq, float(scale), int(workers), ws.data_ptr(), ws.numel(), _stream()))
     return out
 
 

@@ -63,11 +63,10 @@ class Loaded:
         self.lens = torch.from_numpy(lens).cuda()
         torch.cuda.synchronize()
 
-    def decode(self, partition_tokens: int = 0, q=None, tables=None, lens=None, pool=None):
+    def decode(self, workers: int = 0, q=None, tables=None, lens=None, pool=None):
         out = pkv.decode(self.q if q is None else q, self.pool if pool is None else pool,
                          self.tables if tables is None else tables,
-                         self.lens if lens is None else lens, self.wl.scale,
-                         partition_tokens=partition_tokens)
+                         self.lens if lens is None else lens, self.wl.scale, workers=workers)
         torch.cuda.synchronize()
         return out.clone()
 

@@ -65,32 +65,34 @@ def test_decode_argument_checks():
     L = lib()
     p = _pool(num_kv_heads=8)
     # q heads not a multiple of KV heads
-    st = L.pa_decode(16, 16, ctypes.byref(p), 16, 4, 16, 2, 12, 0.1, 0, None, 0, None)
+    st = L.pa_decode(16, 16, ctypes.byref(p), 16, 4, 16, 2, 12, 0.1, 0, 16, 1 << 20, None)
     assert st == -1 and b"multiple" in L.pa_last_error()
-    # partition not a multiple of 16
-    st = L.pa_decode(16, 16, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, 24, None, 0, None)
+    # negative worker count
+    st = L.pa_decode(16, 16, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, -3, 16, 1 << 20, None)
     assert st == -1
-    # workspace required but missing: 4 blocks * 16 > default partition? use many blocks
-    need = L.pa_decode_workspace_bytes(2, 8, 128, 4096, 16, 0)
+    # workspace missing or too small
+    need = L.pa_decode_workspace_bytes(2, 8, 8, 128, 0)
     assert need > 0
-    st = L.pa_decode(16, 16, ctypes.byref(p), 16, 4096, 16, 2, 8, 0.1, 0, None, 0, None)
-    assert st == -5
+    assert L.pa_decode(16, 16, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, 0, None, 0, None) == -5
+    assert L.pa_decode(16, 16, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, 0, 16, need - 1, None) == -5
     # NULL output
-    st = L.pa_decode(None, 16, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, 0, None, 0, None)
+    st = L.pa_decode(None, 16, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, 0, 16, need, None)
     assert st == -1
-    # misaligned q
-    st = L.pa_decode(16, 18, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, 0, None, 0, None)
-    assert st == -1
+    # misaligned q / workspace
+    assert L.pa_decode(16, 18, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, 0, 16, need, None) == -1
+    assert L.pa_decode(16, 16, ctypes.byref(p), 16, 4, 16, 2, 8, 0.1, 0, 24, need, None) == -1
     # zero sequences is a no-op
     assert L.pa_decode(None, None, ctypes.byref(p), None, 4, None, 0, 8, 0.1, 0, None, 0, None) == 0
 
 
 def test_workspace_formula():
     L = lib()
-    # one partition per sequence: no workspace
-    assert L.pa_decode_workspace_bytes(64, 40, 128, 32, 16, 512) == 0
-    # 2048 tokens / 512 = 4 partitions: S*Hq*4*(D*4+8)
-    assert L.pa_decode_workspace_bytes(64, 40, 128, 128, 16, 512) == 64 * 40 * 4 * (128 * 4 + 8)
+    # MHA, 100 workers: 2*100 slots x 1 head x (128 floats + (m, l)) + 100 split records
+    assert L.pa_decode_workspace_bytes(64, 40, 40, 128, 100) == 200 * 128 * 4 + 200 * 8 + 100 * 16
+    # GQA 64/8: 8 query heads per unit
+    n = L.pa_decode_workspace_bytes(256, 64, 8, 128, 10)
+    assert n == 20 * 8 * 128 * 4 + 20 * 8 * 8 + 10 * 16
+    assert L.pa_decode_workspace_bytes(4, 6, 4, 128, 10) == 0  # 6 not a multiple of 4
 
 
 def test_prefill_argument_checks():
