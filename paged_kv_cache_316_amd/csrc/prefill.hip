@@ -1,11 +1,287 @@
-// Chunked-prefill attention over paged K/V (bf16 MFMA). Placeholder until the
-// MFMA kernel lands: reports every configuration as not built.
+// Chunked-prefill attention over paged K/V with bf16 MFMA (gfx950).
+//
+// What it computes ("vLLM PagedAttention explained", section 7.2: a long
+// prompt is processed in chunks that join the sequence's block table): for
+// each sequence s with a chunk of C = q_len rows whose keys are already in the
+// pool, row i sits at absolute position a_i = seq_lens[s] - C + i and
+//   out[row i][h] = sum_{t <= a_i} softmax_t(scale * q_i.K_s[t]) V_s[t],
+// K_s/V_s read through the block table. Query head h reads KV head h / G.
+//
+// How. This is the one place where the work is a dense contraction (queries x
+// keys x head_dim), so it runs on the matrix cores:
+//  * v_mfma_f32_32x32x16_bf16 computes S^T = K Q^T (keys x rows) and then
+//    O^T = V^T P^T (head_dim x rows). In both accumulators a lane holds one
+//    query row (lane % 32), so the online softmax of a row lives in two lanes
+//    (lane and lane ^ 32), and P^T is fed to the second product straight from
+//    the first product's accumulators, converted to bf16, with no shuffles.
+//  * A workgroup is (sequence, KV head, 32-row tile, up to 4 query heads of
+//    the group): its four waves share every K/V tile. K/V tiles of 64 keys
+//    are gathered from the pool (block-table lookup per key) into LDS: K as
+//    stored, V transposed (so the contraction over keys reads 8 consecutive
+//    bytes per operand half); rows are padded against bank conflicts.
+//  * The global loads of the next K/V tile are in flight while the MFMAs of
+//    the current one run. Causal masking only costs compares: keys past a
+//    row's position get -inf. Tiles beyond a wave's last row are skipped.
+//  * Workgroups that read the same (sequence, KV head) stream are placed on
+//    the same XCD (workgroup i runs on XCD i mod 8), so its L2 serves the
+//    repeated K/V reads; the longest (last) row tiles are dispatched first.
+#include <math.h>
+
 #include "device.h"
 
 namespace pa {
+namespace {
 
-bool prefill_supported(int, int, int, int) { return false; }
+constexpr int kWaves = 4;
+constexpr int kRows = 32;     // query rows per wave (MFMA N)
+constexpr int kKeys = 64;     // keys per K/V tile
+constexpr int kXcds = 8;
+constexpr float kLog2e = 1.4426950408889634f;
 
-hipError_t launch_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+template <int D>
+struct PrefillShape {
+  static constexpr int KSTEPS = D / 16;          // MFMA k-steps over head_dim
+  static constexpr int DTILES = D / 32;          // 32-row tiles of head_dim in O^T
+  static constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
+  static constexpr int K_STRIDE = D * 2 + 16;    // bytes per K row in LDS (padded)
+  static constexpr int V_STRIDE = kKeys * 2 + 8; // bytes per V^T row in LDS (padded)
+  static constexpr int K_BYTES = kKeys * K_STRIDE;
+  static constexpr int V_BYTES = D * V_STRIDE;
+  static constexpr int CHUNKS = kKeys * CPR / (kWave * kWaves);  // per thread per tile
+  static_assert(kKeys * CPR % (kWave * kWaves) == 0, "tile must split evenly over threads");
+};
+
+template <int D>
+__global__ __launch_bounds__(kWave * kWaves) void prefill_kernel(
+    PrefillArgs a, int32_t b_shift, int32_t heads_per_group, int32_t n_hchunk, int32_t n_rtiles,
+    float scale_log2) {
+  using PS = PrefillShape<D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* k_lds = smem;
+  unsigned char* vt_lds = smem + PS::K_BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = lane / 32;  // which half of the wave
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int R = kWaves / heads_per_group;  // row tiles per workgroup
+
+  // workgroup -> (sequence, KV head, head chunk, row tile); workgroups of one
+  // (sequence, KV head) are contiguous after the XCD swizzle
+  const int nblk = gridDim.x;
+  int b = blockIdx.x;
+  if (nblk % kXcds == 0) b = (b % kXcds) * (nblk / kXcds) + b / kXcds;
+  const int rt_rev = b % n_rtiles;
+  int rest = b / n_rtiles;
+  const int hc = rest % n_hchunk;
+  rest /= n_hchunk;
+  const int kvh = rest % Hkv;
+  const int s = rest / Hkv;
+  const int rt = n_rtiles - 1 - rt_rev;  // longest rows first
+
+  const int q0 = a.q_start_loc[s];
+  const int q_len = a.q_start_loc[s + 1] - q0;
+  const int L = a.seq_lens[s];
+  const int wg_row0 = rt * R * kRows;
+  if (wg_row0 >= q_len || L <= 0) return;  // uniform over the workgroup
+  const int start = L - q_len;                 // absolute position of chunk row 0
+  const int wg_last_key = start + min(q_len, wg_row0 + R * kRows) - 1;
+  const int n_ktiles = wg_last_key / kKeys + 1;
+
+  const int row0 = wg_row0 + (wave / heads_per_group) * kRows;  // this wave's first row
+  const int head = kvh * G + hc * heads_per_group + wave % heads_per_group;
+  const bool wave_active = row0 < q_len;
+  const int wave_last_key = wave_active ? start + min(q_len, row0 + kRows) - 1 : -1;
+  const int my_row = row0 + lane % kRows;
+  const bool row_valid = my_row < q_len;
+  const int my_pos = row_valid ? start + my_row : -1;
+
+  // Q^T operands: row my_row, dims 16*ks + 8*g .. +7 (rows past the chunk read its last row)
+  uint4 qop[PS::KSTEPS];
+  {
+    const int qr = q0 + min(my_row, q_len - 1);
+    const uint4* qp = static_cast<const uint4*>(a.q) + (int64_t(qr) * Hq + head) * PS::CPR;
+#pragma unroll
+    for (int ks = 0; ks < PS::KSTEPS; ++ks) qop[ks] = qp[2 * ks + g];
+  }
+
+  const int32_t* bt = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
+  const uint4* kp = static_cast<const uint4*>(a.k_pool);
+  const uint4* vp = static_cast<const uint4*>(a.v_pool);
+  const int B = a.block_size, Bm1 = B - 1;
+  uint4 kst[PS::CHUNKS], vst[PS::CHUNKS];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < PS::CHUNKS; ++q) {
+      const int i = tid + q * kWave * kWaves;
+      const int key = i / PS::CPR, c = i % PS::CPR;
+      const int t = min(kt * kKeys + key, L - 1);  // past the end: a valid, masked key
+      const int64_t pb = bt[t >> b_shift];
+      const int64_t idx = ((pb * Hkv + kvh) * B + (t & Bm1)) * PS::CPR + c;
+      kst[q] = load_stream16(kp + idx);
+      vst[q] = load_stream16(vp + idx);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int q = 0; q < PS::CHUNKS; ++q) {
+      const int i = tid + q * kWave * kWaves;
+      const int key = i / PS::CPR, c = i % PS::CPR;
+      *reinterpret_cast<uint4*>(k_lds + key * PS::K_STRIDE + c * 16) = kst[q];
+      const uint32_t w[4] = {vst[q].x, vst[q].y, vst[q].z, vst[q].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint16_t h = uint16_t(w[j / 2] >> (16 * (j % 2)));
+        *reinterpret_cast<uint16_t*>(vt_lds + (8 * c + j) * PS::V_STRIDE + key * 2) = h;
+      }
+    }
+  };
+
+  f32x16_t o[PS::DTILES];
+#pragma unroll
+  for (int dt = 0; dt < PS::DTILES; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
+
+  load_tile(0);
+  for (int kt = 0; kt < n_ktiles; ++kt) {
+    __syncthreads();  // previous tile's LDS reads are done
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < n_ktiles) load_tile(kt + 1);  // in flight during this tile's math
+    const int t0 = kt * kKeys;
+    if (!wave_active || t0 > wave_last_key) continue;  // uniform per wave
+
+    // S^T = K Q^T for keys t0 .. t0+63 (two 32-key m-tiles)
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.f;
+      const unsigned char* krow = k_lds + (mt * 32 + lane % 32) * PS::K_STRIDE + g * 16;
+#pragma unroll
+      for (int ks = 0; ks < PS::KSTEPS; ++ks) {
+        const uint4 kop = *reinterpret_cast<const uint4*>(krow + ks * 32);
+        sacc[mt] = mfma32(kop, qop[ks], sacc[mt]);
+      }
+    }
+    // mask, scale, running max of this lane's row (shared with lane ^ 32)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = t0 + mt * 32 + 8 * (i / 4) + 4 * g + (i % 4);
+        const float z = key <= my_pos ? sacc[mt][i] * scale_log2 : -INFINITY;
+        sacc[mt][i] = z;
+        mx = fmaxf(mx, z);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - ms);
+    m = mn;
+    float ps = 0.f;
+    uint4 pop[4];  // P^T operands for the four 16-key k-steps
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(sacc[mt][8 * h + j] - ms);
+          ps += p[j];
+        }
+        pop[2 * mt + h] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
+                                     pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
+      }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int dt = 0; dt < PS::DTILES; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    // O^T += V^T P^T; operand j of half g in k-step (mt, h) is key
+    // 32 mt + 16 h + 8 (j / 4) + 4 g + j % 4, matching the S^T accumulator order
+#pragma unroll
+    for (int dt = 0; dt < PS::DTILES; ++dt) {
+      const unsigned char* vrow = vt_lds + (dt * 32 + lane % 32) * PS::V_STRIDE + g * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kk * 32);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kk * 32 + 16);
+        o[dt] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pop[kk], o[dt]);
+      }
+    }
+  }
+
+  if (!wave_active || !row_valid) return;
+  const float l_row = lsum + __shfl_xor(lsum, 32);
+  const float inv = 1.f / l_row;
+  uint2* orow = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) +
+                                         (int64_t(q0 + my_row) * Hq + head) * D);
+#pragma unroll
+  for (int dt = 0; dt < PS::DTILES; ++dt)
+#pragma unroll
+    for (int bq = 0; bq < 4; ++bq) {
+      const int d0 = dt * 32 + 8 * bq + 4 * g;
+      orow[d0 / 4] = make_uint2(pack_bf16(o[dt][4 * bq] * inv, o[dt][4 * bq + 1] * inv),
+                                pack_bf16(o[dt][4 * bq + 2] * inv, o[dt][4 * bq + 3] * inv));
+    }
+}
+
+int gcd_pos(int x, int y) {
+  while (y) {
+    const int t = x % y;
+    x = y;
+    y = t;
+  }
+  return x;
+}
+
+}  // namespace
+
+bool prefill_supported(int dtype, int head_dim, int block_size, int group) {
+  return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) && block_size >= 1 && group >= 1;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+  int b_shift = 0;
+  while ((1 << b_shift) < a.block_size) ++b_shift;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int hpg = gcd_pos(G, kWaves);       // query heads per workgroup
+  const int n_hchunk = G / hpg;
+  const int rows_per_wg = (kWaves / hpg) * kRows;
+  const int n_rtiles = (a.max_q_len + rows_per_wg - 1) / rows_per_wg;
+  const int64_t blocks = int64_t(a.num_seqs) * a.num_kv_heads * n_hchunk * n_rtiles;
+  if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const float scale_log2 = a.scale * kLog2e;
+  if (a.head_dim == 128) {
+    using PS = PrefillShape<128>;
+    prefill_kernel<128><<<int(blocks), kWave * kWaves, PS::K_BYTES + PS::V_BYTES, st>>>(
+        a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
+  } else if (a.head_dim == 64) {
+    using PS = PrefillShape<64>;
+    prefill_kernel<64><<<int(blocks), kWave * kWaves, PS::K_BYTES + PS::V_BYTES, st>>>(
+        a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 }  // namespace pa
