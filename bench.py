@@ -102,6 +102,177 @@ def cpu_baseline(wl, budget_s: float):
             "os_cpu_count": os.cpu_count()}
 
 
+class Loaded:
+    """A workload set up on the GPU through the library, ready for timed steps."""
+
+    def __init__(self, name, replicas):
+        import numpy as np
+        import torch
+
+        import paged_kv_cache_316_amd as pkv
+        import workloads
+        from paged_kv_cache_316_amd.runner import WriteBatch, apply_events, run_script, split_phases
+
+        t0 = time.time()
+        self.name = name
+        wl = self.wl = workloads.make(name, "full")
+        log(f"workload {name}: {len(wl.decode_seqs)} seqs, drawn in {time.time() - t0:.1f} s")
+        self.dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+        def dev(a):
+            if wl.dtype == "f32":
+                return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(self.dt)
+
+        # set-up through the library: allocator -> copies / cache writes (untimed)
+        alloc = pkv.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
+        phases = split_phases(run_script(alloc, wl.ops))
+        rows_k, rows_v = dev(wl.rows_k), dev(wl.rows_v)
+        pool0 = pkv.KVPool.empty(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, self.dt)
+        apply_events(pool0, phases.get("setup", []), rows_k, rows_v)
+
+        def batch(events):
+            w = [e for e in events if e[0] == "write"]
+            return WriteBatch(np.concatenate([e[1] for e in w]), np.concatenate([e[2] for e in w]),
+                              rows_k, rows_v)
+
+        # the prefill chunk writes (if any) are a timed step of their own
+        self.prefill_write = batch(phases["prefill"]) if phases.get("prefill") else None
+        if self.prefill_write is not None:
+            self.prefill_write.run(pool0)
+        dec_events = phases["decode"]
+        self.decode_write = batch(dec_events)
+        copies = [e for e in dec_events if e[0] == "copy"]
+        if copies:  # copy-on-write caused by the decode tokens happens before the timed steps
+            apply_events(pool0, copies, rows_k, rows_v)
+        self.decode_write.run(pool0)
+        del rows_k, rows_v
+        self.pools = [pool0] + [pkv.KVPool(pool0.k.clone(), pool0.v.clone())
+                                for _ in range(replicas - 1)]
+        tables, lens = alloc.batch_tables(wl.decode_seqs)
+        self.lens = lens
+        self.tables_d = torch.from_numpy(tables).cuda()
+        self.lens_d = torch.from_numpy(lens).cuda()
+        self.q = dev(wl.q)
+        if wl.prefill_seqs:
+            C = wl.prefill_len
+            idx = [wl.decode_seqs.index(x) for x in wl.prefill_seqs]
+            self.p_tables = self.tables_d[torch.tensor(idx, device="cuda")].contiguous()
+            p_lens = np.array([int(wl.prefill_start[j]) + C for j in range(len(idx))], np.int64)
+            self.p_lens_d = torch.from_numpy(p_lens.astype(np.int32)).cuda()
+            self.p_loc = torch.arange(0, (len(idx) + 1) * C, C, dtype=torch.int32, device="cuda")
+            self.p_q = dev(wl.prefill_q)
+            # visible keys summed over chunk rows: row i of a chunk ending at P sees P - C + i + 1
+            self.p_keys = int(sum(C * (P - C) + C * (C + 1) // 2 for P in p_lens))
+        torch.cuda.synchronize()
+        log(f"set-up done in {time.time() - t0:.1f} s")
+
+    @property
+    def kv_bytes(self):
+        wl = self.wl
+        return float(self.lens.astype("int64").sum()) * 2 * wl.num_kv_heads * wl.head_dim * wl.elt_bytes
+
+
+def _stats_us(ms):
+    import numpy as np
+    return {"mean": round(float(ms.mean()) * 1e3, 2),
+            "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+            "p50": round(float(np.percentile(ms, 50)) * 1e3, 2),
+            "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)}
+
+
+def time_steps(step, steps, warmup):
+    """Run warmup steps, then exactly `steps` timed steps bracketed by synchronisation.
+    Each step records 3 events (before, between its two calls, after) on the launch stream."""
+    import numpy as np
+    import torch
+    for i in range(warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t_start
+    first = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    second = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    return total * 1e3 / steps, first, second
+
+
+def decode_step_fn(ld, workers):
+    import torch
+    import paged_kv_cache_316_amd as pkv
+    S, Hq = len(ld.wl.decode_seqs), ld.wl.num_q_heads
+    plans = [pkv.DecodePlan(p, S, Hq, workers) for p in ld.pools]
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev):
+        p = ld.pools[i % len(ld.pools)]
+        if ev is not None:
+            ev[0].record(stream)
+        ld.decode_write.run(p)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.decode(ld.q, p, ld.tables_d, ld.lens_d, ld.wl.scale, workers, plan=plans[i % len(ld.pools)])
+        if ev is not None:
+            ev[2].record(stream)
+    return step
+
+
+def prefill_step_fn(ld):
+    import torch
+    import paged_kv_cache_316_amd as pkv
+    out = torch.empty_like(ld.p_q)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev):
+        p = ld.pools[i % len(ld.pools)]
+        if ev is not None:
+            ev[0].record(stream)
+        ld.prefill_write.run(p)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.prefill_chunk(ld.p_q, ld.p_loc, ld.p_lens_d, p, ld.p_tables, ld.wl.prefill_len,
+                          ld.wl.scale, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+    return step
+
+
+def decode_row(ld, steps, warmup, workers):
+    ms_step, w_ms, d_ms = time_steps(decode_step_fn(ld, workers), steps, warmup)
+    S = len(ld.wl.decode_seqs)
+    achieved = ld.kv_bytes / (float(d_ms.mean()) * 1e-3) / 1e9
+    return {"ms_per_step": round(ms_step, 5),
+            "kv_gbps_step": round(ld.kv_bytes / (ms_step * 1e-3) / 1e9, 2),
+            "tokens_per_s": round(S / (ms_step * 1e-3), 1),
+            "decode_kv_gbps": round(achieved, 2),
+            "decode_us": _stats_us(d_ms), "cache_write_us": round(float(w_ms.mean()) * 1e3, 2),
+            "kv_bytes_per_step": int(ld.kv_bytes), "tokens": int(ld.lens.sum()),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                         "traffic": load_traffic(ld.name),
+                         "kernel": "pa_decode (balanced split kernel + LSE combine kernel)"}}
+
+
+def prefill_row(ld, steps, warmup):
+    ms_step, w_ms, p_ms = time_steps(prefill_step_fn(ld), steps, warmup)
+    wl = ld.wl
+    flops = 4.0 * wl.head_dim * wl.num_q_heads * ld.p_keys
+    tflops = flops / (float(p_ms.mean()) * 1e-3) / 1e12
+    rows = len(wl.prefill_seqs) * wl.prefill_len
+    return {"chunks": len(wl.prefill_seqs), "rows_per_chunk": wl.prefill_len,
+            "ms_per_step": round(ms_step, 5), "prefill_us": _stats_us(p_ms),
+            "cache_write_us": round(float(w_ms.mean()) * 1e3, 2),
+            "flops_per_call": flops, "prefill_tokens_per_s": round(rows / (ms_step * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "pa_prefill_chunk (bf16 MFMA 32x32x16)"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +283,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=2, help="pool replicas rotated between steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-rows", action="store_true",
+                    help="skip the Llama-2-70B-shaped GQA decode and chunked-prefill rows")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -122,52 +295,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
+    import gc
+
     import torch
 
-    import paged_kv_cache_316_amd as pkv
-    import workloads
-    from paged_kv_cache_316_amd.runner import WriteBatch, apply_events, run_script, split_phases
-
     torch.cuda.set_device(0)
-    t0 = time.time()
-    wl = workloads.make(args.workload, "full")
-    log(f"workload {args.workload}: {len(wl.decode_seqs)} seqs, drawn in {time.time() - t0:.1f} s")
-    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
-
-    def dev(a):
-        if wl.dtype == "f32":
-            return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(dt)
-
-    # set-up through the library: allocator -> copies / cache writes (untimed)
-    alloc = pkv.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
-    phases = split_phases(run_script(alloc, wl.ops))
-    rows_k, rows_v = dev(wl.rows_k), dev(wl.rows_v)
-    pool0 = pkv.KVPool.empty(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, dt)
-    for name in ("setup", "prefill"):
-        apply_events(pool0, phases.get(name, []), rows_k, rows_v)
-    dec_events = phases["decode"]
-    copies = [e for e in dec_events if e[0] == "copy"]
-    writes = [e for e in dec_events if e[0] == "write"]
-    slots = np.concatenate([e[1] for e in writes])
-    rows = np.concatenate([e[2] for e in writes])
-    step_write = WriteBatch(slots, rows, rows_k, rows_v)
-    if copies:  # copy-on-write caused by the decode tokens happens before the timed steps
-        apply_events(pool0, copies, rows_k, rows_v)
-    del rows_k, rows_v
-    pools = [pool0] + [pkv.KVPool(pool0.k.clone(), pool0.v.clone()) for _ in range(args.replicas - 1)]
-    tables, lens = alloc.batch_tables(wl.decode_seqs)
-    tables_d = torch.from_numpy(tables).cuda()
-    lens_d = torch.from_numpy(lens).cuda()
-    q = dev(wl.q)
-    S, Hq = len(wl.decode_seqs), wl.num_q_heads
-    plans = [pkv.DecodePlan(p, S, Hq, args.workers) for p in pools]
-    torch.cuda.synchronize()
-    log(f"set-up done in {time.time() - t0:.1f} s")
-
-    kv_bytes = float(lens.astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim * wl.elt_bytes
-
+    ld = Loaded(args.workload, args.replicas)
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -176,67 +309,33 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        p = pools[i % len(pools)]
-        if ev is not None:
-            ev[0].record(stream)
-        step_write.run(p)
-        if ev is not None:
-            ev[1].record(stream)
-        pkv.decode(q, p, tables_d, lens_d, wl.scale, args.workers, plan=plans[i % len(pools)])
-        if ev is not None:
-            ev[2].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed region: exactly K steps, synchronised on both sides
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
-    ms_per_step = t_total * 1e3 / args.steps
-    write_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    decode_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    dec_avg_s = float(decode_ms.mean()) * 1e-3
-
-    achieved = kv_bytes / dec_avg_s / 1e9
-    traffic = load_traffic(args.workload)
+    row = decode_row(ld, args.steps, args.warmup, args.workers)
+    wl = ld.wl
+    S = len(wl.decode_seqs)
     result = {
         "metric": "paged decode attention: KV GB/s read (% of HBM peak) and decode tokens/s",
-        "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "value": row["kv_gbps_step"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": row["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "num_seqs": S, "num_q_heads": Hq,
-                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
-                   "block_size": wl.block_size, "tokens": int(lens.sum()),
-                   "kv_bytes_per_step": int(kv_bytes), "pool_replicas": len(pools),
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "num_seqs": S,
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "block_size": wl.block_size, "tokens": row["tokens"],
+                   "kv_bytes_per_step": row["kv_bytes_per_step"], "pool_replicas": args.replicas,
                    "accumulation": "fp32", "decode_workers": args.workers or "default (8 per CU)"},
-        "pct_hbm_peak": round(100 * kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
-        "tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
-        "decode_kv_gbps": round(achieved, 2),
-        "decode_us": {"mean": round(float(decode_ms.mean()) * 1e3, 2),
-                      "p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
-                      "p50": round(float(np.percentile(decode_ms, 50)) * 1e3, 2),
-                      "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 2)},
-        "cache_write_us": round(float(write_ms.mean()) * 1e3, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "pa_decode (balanced split kernel + LSE combine kernel)"},
+        "pct_hbm_peak": round(100 * row["kv_gbps_step"] / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": row["tokens_per_s"],
+        "decode_kv_gbps": row["decode_kv_gbps"],
+        "decode_us": row["decode_us"],
+        "cache_write_us": row["cache_write_us"],
+        "roofline": row["roofline"],
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
@@ -244,6 +343,18 @@ def main():
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     else:
         result["cpu_baseline"] = None
+    if not args.no_extra_rows:
+        rows = {}
+        if args.workload != "llama70b":
+            del ld
+            gc.collect()
+            torch.cuda.empty_cache()
+            ld = Loaded("llama70b", args.replicas)
+            rows["decode_llama70b_gqa"] = decode_row(ld, max(20, args.steps // 4), args.warmup,
+                                                    args.workers)
+        rows["prefill_llama70b"] = prefill_row(ld, max(10, args.steps // 10), min(args.warmup, 5))
+        rows["workload_llama70b"] = WORKLOAD_TEXT["llama70b"] + "; prefill: 8 x 512-row causal chunks"
+        result["rows"] = rows
     print(json.dumps(result), flush=True)
 
 

@@ -36,15 +36,14 @@ __device__ __forceinline__ uint4 load_stream16(const uint4* p) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  return (u + (((u >> 16) & 1u) + 0x7fffu)) >> 16;
-}
+// Two floats -> packed bfloat16 pair (low half = lo), round to nearest even,
+// NaN kept quiet: one v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2_native __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const bf16x2_native v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16(f, 0.f) & 0xffffu; }
 
 // DPP move inside rows of 16 lanes (all rows and banks enabled).
 template <int CTRL>

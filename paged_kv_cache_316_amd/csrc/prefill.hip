@@ -16,12 +16,17 @@
 //    the first product's accumulators, converted to bf16, with no shuffles.
 //  * A workgroup is (sequence, KV head, 32-row tile, up to 4 query heads of
 //    the group): its four waves share every K/V tile. K/V tiles of 64 keys
-//    are gathered from the pool (block-table lookup per key) into LDS: K as
-//    stored, V transposed (so the contraction over keys reads 8 consecutive
-//    bytes per operand half); rows are padded against bank conflicts.
-//  * The global loads of the next K/V tile are in flight while the MFMAs of
-//    the current one run. Causal masking only costs compares: keys past a
-//    row's position get -inf. Tiles beyond a wave's last row are skipped.
+//    are gathered from the pool into LDS, double-buffered (one barrier per
+//    tile): K as stored, V transposed so that the contraction over keys
+//    reads 8 consecutive bytes per operand half. Each thread loads the same
+//    16-byte dim chunk of 4 consecutive keys (one block-table lookup) and
+//    transposes them in registers into eight 8-byte LDS stores. Rows are
+//    padded against bank conflicts.
+//  * The global loads of tile t+2 are in flight while the MFMAs of tile t run.
+//    The softmax scale is folded into the exponent (one FMA per score);
+//    causal masking (keys past a row's position get -inf) is applied only on
+//    tiles that reach the diagonal; the output rescale is skipped when no
+//    row's running max moved. Tiles beyond a wave's last row are skipped.
 //  * Workgroups that read the same (sequence, KV head) stream are placed on
 //    the same XCD (workgroup i runs on XCD i mod 8), so its L2 serves the
 //    repeated K/V reads; the longest (last) row tiles are dispatched first.
@@ -63,13 +68,12 @@ struct PrefillShape {
 };
 
 template <int D>
-__global__ __launch_bounds__(kWave * kWaves) void prefill_kernel(
+__global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     PrefillArgs a, int32_t b_shift, int32_t heads_per_group, int32_t n_hchunk, int32_t n_rtiles,
     float scale_log2) {
   using PS = PrefillShape<D>;
+  constexpr int KPT = PS::CHUNKS;  // consecutive keys per thread per tile (same dim chunk)
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* k_lds = smem;
-  unsigned char* vt_lds = smem + PS::K_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -105,9 +109,9 @@ __global__ __launch_bounds__(kWave * kWaves) void prefill_kernel(
   const int head = kvh * G + hc * heads_per_group + wave % heads_per_group;
   const bool wave_active = row0 < q_len;
   const int wave_last_key = wave_active ? start + min(q_len, row0 + kRows) - 1 : -1;
+  const bool wave_ragged = row0 + kRows > q_len;  // has rows past the chunk: always mask
   const int my_row = row0 + lane % kRows;
-  const bool row_valid = my_row < q_len;
-  const int my_pos = row_valid ? start + my_row : -1;
+  const int my_pos = my_row < q_len ? start + my_row : -1;
 
   // Q^T operands: row my_row, dims 16*ks + 8*g .. +7 (rows past the chunk read its last row)
   uint4 qop[PS::KSTEPS];
@@ -122,31 +126,47 @@ __global__ __launch_bounds__(kWave * kWaves) void prefill_kernel(
   const uint4* kp = static_cast<const uint4*>(a.k_pool);
   const uint4* vp = static_cast<const uint4*>(a.v_pool);
   const int B = a.block_size, Bm1 = B - 1;
-  uint4 kst[PS::CHUNKS], vst[PS::CHUNKS];
+  const int lc = tid % PS::CPR;        // this thread's 16-byte dim chunk
+  const int lk = (tid / PS::CPR) * KPT;  // its first key in the tile
+  uint4 kst[KPT], vst[KPT];
   auto load_tile = [&](int kt) {
+    const int t_first = kt * kKeys + lk;
+    const int64_t pb_first = bt[min(t_first, L - 1) >> b_shift];
 #pragma unroll
-    for (int q = 0; q < PS::CHUNKS; ++q) {
-      const int i = tid + q * kWave * kWaves;
-      const int key = i / PS::CPR, c = i % PS::CPR;
-      const int t = min(kt * kKeys + key, L - 1);  // past the end: a valid, masked key
-      const int64_t pb = bt[t >> b_shift];
-      const int64_t idx = ((pb * Hkv + kvh) * B + (t & Bm1)) * PS::CPR + c;
+    for (int q = 0; q < KPT; ++q) {
+      const int t = min(t_first + q, L - 1);  // past the end: a valid, masked key
+      // the KPT keys share a block unless blocks are smaller than KPT
+      const int64_t pb = B >= KPT ? pb_first : int64_t(bt[t >> b_shift]);
+      const int64_t idx = ((pb * Hkv + kvh) * B + (t & Bm1)) * PS::CPR + lc;
       kst[q] = load_stream16(kp + idx);
       vst[q] = load_stream16(vp + idx);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
+    unsigned char* k_lds = smem + buf * (PS::K_BYTES + PS::V_BYTES);
+    unsigned char* vt_lds = k_lds + PS::K_BYTES;
 #pragma unroll
-    for (int q = 0; q < PS::CHUNKS; ++q) {
-      const int i = tid + q * kWave * kWaves;
-      const int key = i / PS::CPR, c = i % PS::CPR;
-      *reinterpret_cast<uint4*>(k_lds + key * PS::K_STRIDE + c * 16) = kst[q];
-      const uint32_t w[4] = {vst[q].x, vst[q].y, vst[q].z, vst[q].w};
+    for (int q = 0; q < KPT; ++q)
+      *reinterpret_cast<uint4*>(k_lds + (lk + q) * PS::K_STRIDE + lc * 16) = kst[q];
+    // transpose KPT keys x 8 dims: V^T row 8*lc + j gets keys lk .. lk+KPT-1
+    uint32_t w[KPT][4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint16_t h = uint16_t(w[j / 2] >> (16 * (j % 2)));
-        *reinterpret_cast<uint16_t*>(vt_lds + (8 * c + j) * PS::V_STRIDE + key * 2) = h;
-      }
+    for (int q = 0; q < KPT; ++q) {
+      w[q][0] = vst[q].x; w[q][1] = vst[q].y; w[q][2] = vst[q].z; w[q][3] = vst[q].w;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = j / 2;
+      uint32_t pr[KPT / 2];
+#pragma unroll
+      for (int q = 0; q < KPT; q += 2)
+        pr[q / 2] = (j % 2 == 0) ? ((w[q][k] & 0xffffu) | (w[q + 1][k] << 16))
+                                 : ((w[q][k] >> 16) | (w[q + 1][k] & 0xffff0000u));
+      unsigned char* dst = vt_lds + (8 * lc + j) * PS::V_STRIDE + lk * 2;
+      if constexpr (KPT == 4)
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pr[0], pr[1]);
+      else
+        *reinterpret_cast<uint32_t*>(dst) = pr[0];
     }
   };
 
@@ -155,16 +175,19 @@ __global__ __launch_bounds__(kWave * kWaves) void prefill_kernel(
   for (int dt = 0; dt < PS::DTILES; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  float m = -INFINITY, lsum = 0.f;
+  float m = -INFINITY, lsum = 0.f;  // running max in raw score units
 
   load_tile(0);
+  store_tile(0);
+  if (n_ktiles > 1) load_tile(1);
   for (int kt = 0; kt < n_ktiles; ++kt) {
-    __syncthreads();  // previous tile's LDS reads are done
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < n_ktiles) load_tile(kt + 1);  // in flight during this tile's math
+    __syncthreads();  // tile kt's LDS writes are visible; buffer (kt+1)%2 is free again
+    if (kt + 1 < n_ktiles) store_tile((kt + 1) % 2);
+    if (kt + 2 < n_ktiles) load_tile(kt + 2);  // in flight during the math of tile kt
     const int t0 = kt * kKeys;
     if (!wave_active || t0 > wave_last_key) continue;  // uniform per wave
+    const unsigned char* k_lds = smem + (kt % 2) * (PS::K_BYTES + PS::V_BYTES);
+    const unsigned char* vt_lds = k_lds + PS::K_BYTES;
 
     // S^T = K Q^T for keys t0 .. t0+63 (two 32-key m-tiles)
     f32x16_t sacc[2];
@@ -179,21 +202,27 @@ __global__ __launch_bounds__(kWave * kWaves) void prefill_kernel(
         sacc[mt] = mfma32(kop, qop[ks], sacc[mt]);
       }
     }
-    // mask, scale, running max of this lane's row (shared with lane ^ 32)
+    // causal mask only where the tile reaches the diagonal (or rows past the chunk)
+    if (wave_ragged || t0 + kKeys - 1 > start + row0) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = t0 + mt * 32 + 8 * (i / 4) + 4 * g + (i % 4);
+          if (key > my_pos) sacc[mt][i] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = t0 + mt * 32 + 8 * (i / 4) + 4 * g + (i % 4);
-        const float z = key <= my_pos ? sacc[mt][i] * scale_log2 : -INFINITY;
-        sacc[mt][i] = z;
-        mx = fmaxf(mx, z);
-      }
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mn = fmaxf(m, mx);
     const float ms = mn == -INFINITY ? 0.f : mn;
-    const float alpha = __builtin_amdgcn_exp2f(m - ms);
+    const float nms = -ms * scale_log2;
+    const float alpha = __builtin_amdgcn_exp2f(fmaf(m, scale_log2, nms));
+    const bool moved = mn != m;
     m = mn;
     float ps = 0.f;
     uint4 pop[4];  // P^T operands for the four 16-key k-steps
@@ -204,17 +233,19 @@ __global__ __launch_bounds__(kWave * kWaves) void prefill_kernel(
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(sacc[mt][8 * h + j] - ms);
+          p[j] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * h + j], scale_log2, nms));
           ps += p[j];
         }
         pop[2 * mt + h] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
                                      pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
       }
     lsum = lsum * alpha + ps;
+    if (__ballot(moved)) {  // exact: alpha == 1 where no row max moved
 #pragma unroll
-    for (int dt = 0; dt < PS::DTILES; ++dt)
+      for (int dt = 0; dt < PS::DTILES; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
     // O^T += V^T P^T; operand j of half g in k-step (mt, h) is key
     // 32 mt + 16 h + 8 (j / 4) + 4 g + j % 4, matching the S^T accumulator order
 #pragma unroll
@@ -229,7 +260,7 @@ __global__ __launch_bounds__(kWave * kWaves) void prefill_kernel(
     }
   }
 
-  if (!wave_active || !row_valid) return;
+  if (!wave_active || my_pos < 0) return;
   const float l_row = lsum + __shfl_xor(lsum, 32);
   const float inv = 1.f / l_row;
   uint2* orow = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) +
@@ -272,11 +303,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const float scale_log2 = a.scale * kLog2e;
   if (a.head_dim == 128) {
     using PS = PrefillShape<128>;
-    prefill_kernel<128><<<int(blocks), kWave * kWaves, PS::K_BYTES + PS::V_BYTES, st>>>(
+    prefill_kernel<128><<<int(blocks), kWave * kWaves, 2 * (PS::K_BYTES + PS::V_BYTES), st>>>(
         a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
   } else if (a.head_dim == 64) {
     using PS = PrefillShape<64>;
-    prefill_kernel<64><<<int(blocks), kWave * kWaves, PS::K_BYTES + PS::V_BYTES, st>>>(
+    prefill_kernel<64><<<int(blocks), kWave * kWaves, 2 * (PS::K_BYTES + PS::V_BYTES), st>>>(
         a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
   } else {
     return hipErrorInvalidValue;
