@@ -17,16 +17,19 @@
 //  * A workgroup is (sequence, KV head, 32-row tile, up to 4 query heads of
 //    the group): its four waves share every K/V tile. K/V tiles of 64 keys
 //    are gathered from the pool into LDS, double-buffered (one barrier per
-//    tile): K as stored, V transposed so that the contraction over keys
-//    reads 8 consecutive bytes per operand half. Each thread loads the same
-//    16-byte dim chunk of 4 consecutive keys (one block-table lookup) and
-//    transposes them in registers into eight 8-byte LDS stores. Rows are
-//    padded against bank conflicts.
+//    tile), both in their natural [key][dim] layout with 16-byte stores. The
+//    contraction over keys needs V as columns (4 consecutive keys of one dim
+//    per lane): ds_read_b64_tr_b16 reads them transposed. Within 16 lanes,
+//    lane 4k+q points at V[key0+k][dim0+4q] and lane i receives
+//    V[key0..key0+3][dim0+i]. Each thread loads the same 16-byte dim chunk of
+//    4 consecutive keys (one block-table lookup). Rows are padded against
+//    bank conflicts.
 //  * The global loads of tile t+2 are in flight while the MFMAs of tile t run.
 //    The softmax scale is folded into the exponent (one FMA per score);
 //    causal masking (keys past a row's position get -inf) is applied only on
-//    tiles that reach the diagonal; the output rescale is skipped when no
-//    row's running max moved. Tiles beyond a wave's last row are skipped.
+//    tiles that reach the diagonal; the exponent base of a row only moves when
+//    its max grows by more than 2^8, so the output rescale is rare. Tiles
+//    beyond a wave's last row are skipped.
 //  * Workgroups that read the same (sequence, KV head) stream are placed on
 //    the same XCD (workgroup i runs on XCD i mod 8), so its L2 serves the
 //    repeated K/V reads; the longest (last) row tiles are dispatched first.
@@ -45,6 +48,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8_t, v);
@@ -60,9 +64,9 @@ struct PrefillShape {
   static constexpr int DTILES = D / 32;          // 32-row tiles of head_dim in O^T
   static constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
   static constexpr int K_STRIDE = D * 2 + 16;    // bytes per K row in LDS (padded)
-  static constexpr int V_STRIDE = kKeys * 2 + 8; // bytes per V^T row in LDS (padded)
+  static constexpr int V_STRIDE = D * 2 + 64;    // bytes per V row in LDS (padded)
   static constexpr int K_BYTES = kKeys * K_STRIDE;
-  static constexpr int V_BYTES = D * V_STRIDE;
+  static constexpr int V_BYTES = kKeys * V_STRIDE;
   static constexpr int CHUNKS = kKeys * CPR / (kWave * kWaves);  // per thread per tile
   static_assert(kKeys * CPR % (kWave * kWaves) == 0, "tile must split evenly over threads");
 };
@@ -131,6 +135,18 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
   uint4 kst[KPT], vst[KPT];
   auto load_tile = [&](int kt) {
     const int t_first = kt * kKeys + lk;
+    if (kt * kKeys + kKeys <= L && B >= KPT) {
+      // whole tile inside the sequence: KPT consecutive keys of one block
+      const int64_t pb = bt[t_first >> b_shift];
+      const uint4* kb = kp + ((pb * Hkv + kvh) * B + (t_first & Bm1)) * PS::CPR + lc;
+      const uint4* vb = vp + (kb - kp);
+#pragma unroll
+      for (int q = 0; q < KPT; ++q) {
+        kst[q] = load_stream16(kb + q * PS::CPR);
+        vst[q] = load_stream16(vb + q * PS::CPR);
+      }
+      return;
+    }
     const int64_t pb_first = bt[min(t_first, L - 1) >> b_shift];
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
@@ -144,31 +160,16 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
   };
   auto store_tile = [&](int buf) {
     unsigned char* k_lds = smem + buf * (PS::K_BYTES + PS::V_BYTES);
-    unsigned char* vt_lds = k_lds + PS::K_BYTES;
-#pragma unroll
-    for (int q = 0; q < KPT; ++q)
-      *reinterpret_cast<uint4*>(k_lds + (lk + q) * PS::K_STRIDE + lc * 16) = kst[q];
-    // transpose KPT keys x 8 dims: V^T row 8*lc + j gets keys lk .. lk+KPT-1
-    uint32_t w[KPT][4];
+    unsigned char* v_lds = k_lds + PS::K_BYTES;
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
-      w[q][0] = vst[q].x; w[q][1] = vst[q].y; w[q][2] = vst[q].z; w[q][3] = vst[q].w;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = j / 2;
-      uint32_t pr[KPT / 2];
-#pragma unroll
-      for (int q = 0; q < KPT; q += 2)
-        pr[q / 2] = (j % 2 == 0) ? ((w[q][k] & 0xffffu) | (w[q + 1][k] << 16))
-                                 : ((w[q][k] >> 16) | (w[q + 1][k] & 0xffff0000u));
-      unsigned char* dst = vt_lds + (8 * lc + j) * PS::V_STRIDE + lk * 2;
-      if constexpr (KPT == 4)
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pr[0], pr[1]);
-      else
-        *reinterpret_cast<uint32_t*>(dst) = pr[0];
+      *reinterpret_cast<uint4*>(k_lds + (lk + q) * PS::K_STRIDE + lc * 16) = kst[q];
+      *reinterpret_cast<uint4*>(v_lds + (lk + q) * PS::V_STRIDE + lc * 16) = vst[q];
     }
   };
+  // transposed-read address of this lane inside a V tile: key offset and byte column
+  const int tr_key = 4 * g + (lane % 16) / 4;
+  const int tr_col = (((lane / 16) % 2) * 16 + 4 * (lane % 4)) * 2;
 
   f32x16_t o[PS::DTILES];
 #pragma unroll
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     const int t0 = kt * kKeys;
     if (!wave_active || t0 > wave_last_key) continue;  // uniform per wave
     const unsigned char* k_lds = smem + (kt % 2) * (PS::K_BYTES + PS::V_BYTES);
-    const unsigned char* vt_lds = k_lds + PS::K_BYTES;
+    const unsigned char* v_lds = k_lds + PS::K_BYTES;
 
     // S^T = K Q^T for keys t0 .. t0+63 (two 32-key m-tiles)
     f32x16_t sacc[2];
@@ -218,11 +219,15 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
+    // The exponent base m only moves when a row's max exceeds it by more than
+    // 2^8 (or on the first scores): until then weights up to 256 are taken
+    // as they are. Numerator and denominator share the base, so this is
+    // exact, and it spares the output rescale on almost every tile.
+    const bool moved = m == -INFINITY ? mx != -INFINITY : (mx - m) * scale_log2 > 8.f;
+    const float mn = moved ? mx : m;
     const float ms = mn == -INFINITY ? 0.f : mn;
     const float nms = -ms * scale_log2;
-    const float alpha = __builtin_amdgcn_exp2f(fmaf(m, scale_log2, nms));
-    const bool moved = mn != m;
+    const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m, scale_log2, nms)) : 1.f;
     m = mn;
     float ps = 0.f;
     uint4 pop[4];  // P^T operands for the four 16-key k-steps
@@ -246,16 +251,19 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
     }
-    // O^T += V^T P^T; operand j of half g in k-step (mt, h) is key
-    // 32 mt + 16 h + 8 (j / 4) + 4 g + j % 4, matching the S^T accumulator order
+    // O^T += V^T P^T; operand j of half g in k-step kk = (mt, h) is key
+    // 16 kk + 8 (j / 4) + 4 g + j % 4, matching the S^T accumulator order
 #pragma unroll
     for (int dt = 0; dt < PS::DTILES; ++dt) {
-      const unsigned char* vrow = vt_lds + (dt * 32 + lane % 32) * PS::V_STRIDE + g * 8;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kk * 32);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kk * 32 + 16);
-        o[dt] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pop[kk], o[dt]);
+        const unsigned char* va = v_lds + (16 * kk + tr_key) * PS::V_STRIDE + dt * 64 + tr_col;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(va));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(va + 8 * PS::V_STRIDE));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        o[dt] = mfma32(make_uint4(l2.x, l2.y, h2.x, h2.y), pop[kk], o[dt]);
       }
     }
   }
