@@ -15,17 +15,22 @@
 //    (lane and lane ^ 32), and P^T is fed to the second product straight from
 //    the first product's accumulators, converted to bf16, with no shuffles.
 //  * A workgroup is (sequence, KV head, 32-row tile, up to 4 query heads of
-//    the group): its four waves share every K/V tile. K/V tiles of 64 keys
-//    are gathered from the pool into LDS, double-buffered (one barrier per
-//    tile), both in their natural [key][dim] layout with 16-byte stores. The
-//    contraction over keys needs V as columns (4 consecutive keys of one dim
-//    per lane): ds_read_b64_tr_b16 reads them transposed. Within 16 lanes,
-//    lane 4k+q points at V[key0+k][dim0+4q] and lane i receives
-//    V[key0..key0+3][dim0+i]. Each thread loads the same 16-byte dim chunk of
-//    4 consecutive keys (one block-table lookup). Rows are padded against
-//    bank conflicts.
-//  * The global loads of tile t+2 are in flight while the MFMAs of tile t run.
-//    The softmax scale is folded into the exponent (one FMA per score);
+//    the group): its four waves share every K/V tile of 64 keys.
+//  * K/V tiles go from the pool straight into LDS (global_load_lds_dwordx4:
+//    a wave's 64 lanes fill 1 KB of LDS, lane l at byte 16 l), double
+//    buffered: the loads of tile t+1 and the block-table entries of tile t+2
+//    are in flight while tile t is computed; one barrier per tile. No
+//    registers stage the data and no LDS store instructions run.
+//  * LDS rows are unpadded, [key][head_dim]; the 16-byte chunk c of row r is
+//    kept at chunk c ^ swz(r). A lane picks the global chunk that lands in
+//    its LDS slot, so the swizzle costs nothing on the way in, and swz is
+//    chosen so that both operand reads below touch every LDS bank at most
+//    once per pass.
+//  * The K operand of S^T is a 16-byte read (one key, 8 dims). The V operand
+//    of O^T needs 4 consecutive keys of one dim per lane: ds_read_b64_tr_b16
+//    reads it transposed. Within 16 lanes, lane 4k+q points at
+//    V[key0+k][dim0+4q .. +3] and lane i receives V[key0..key0+3][dim0+i].
+//  * The softmax scale is folded into the exponent (one FMA per score);
 //    causal masking (keys past a row's position get -inf) is applied only on
 //    tiles that reach the diagonal; the exponent base of a row only moves when
 //    its max grows by more than 2^8, so the output rescale is rare. Tiles
@@ -49,6 +54,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8_t, v);
@@ -60,23 +66,57 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
 
 template <int D>
 struct PrefillShape {
-  static constexpr int KSTEPS = D / 16;          // MFMA k-steps over head_dim
-  static constexpr int DTILES = D / 32;          // 32-row tiles of head_dim in O^T
-  static constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
-  static constexpr int K_STRIDE = D * 2 + 16;    // bytes per K row in LDS (padded)
-  static constexpr int V_STRIDE = D * 2 + 64;    // bytes per V row in LDS (padded)
-  static constexpr int K_BYTES = kKeys * K_STRIDE;
-  static constexpr int V_BYTES = kKeys * V_STRIDE;
-  static constexpr int CHUNKS = kKeys * CPR / (kWave * kWaves);  // per thread per tile
-  static_assert(kKeys * CPR % (kWave * kWaves) == 0, "tile must split evenly over threads");
+  static constexpr int KSTEPS = D / 16;               // MFMA k-steps over head_dim
+  static constexpr int DTILES = D / 32;               // 32-row tiles of head_dim in O^T
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per K/V row
+  static constexpr int ROW = D * 2;                   // bytes per K/V row in LDS
+  static constexpr int RPI = 1024 / ROW;              // rows one wave-wide load fills
+  static constexpr int NI = kKeys / (RPI * kWaves);   // loads per wave per tensor per tile
+  static constexpr int TILE = kKeys * ROW;            // bytes of one K or V tile
+  static constexpr int STAGE = 2 * TILE;              // K tile then V tile
+  static constexpr int LDS = 2 * STAGE;               // two stages
+  static_assert(NI >= 1 && kKeys % (RPI * kWaves) == 0, "tile must split evenly over waves");
 };
+
+// Chunk swizzle. For 16 chunks per row: swz(r) = 4 (r % 4) + (r / 4) % 4, a
+// bijection on 16 consecutive rows (K reads: 16 rows, one chunk) whose upper
+// two bits differ over any 4 consecutive rows (V reads: 4 rows x 4 aligned
+// chunks). For 8 chunks per row (two rows per 256-byte bank line) the same
+// two properties hold per row parity.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 16) return 4 * (r % 4) + (r / 4) % 4;
+  else return 4 * ((r / 2) % 2) + (r / 4) % 4;
+}
+
+// 16 bytes per lane from global memory into LDS at lds_addr + 16 * lane.
+// Issued from inline assembly so that the compiler does not put a wait for
+// it in front of every later LDS read; completion is awaited explicitly
+// (vmcnt) before the barrier that publishes the tile.
+__device__ __forceinline__ void load_lds16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// Wait for every outstanding load of this wave (including the direct-to-LDS
+// ones) and every LDS access, then meet the other waves. The wait is the
+// compiler's own s_waitcnt, so its bookkeeping of outstanding loads restarts
+// from zero here and it adds no waits of its own for older loads later in the
+// loop; the empty asm keeps LDS reads from moving above the barrier.
+__device__ __forceinline__ void drain_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int D>
 __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     PrefillArgs a, int32_t b_shift, int32_t heads_per_group, int32_t n_hchunk, int32_t n_rtiles,
     float scale_log2) {
   using PS = PrefillShape<D>;
-  constexpr int KPT = PS::CHUNKS;  // consecutive keys per thread per tile (same dim chunk)
+  constexpr int NI = PS::NI;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -126,50 +166,50 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     for (int ks = 0; ks < PS::KSTEPS; ++ks) qop[ks] = qp[2 * ks + g];
   }
 
+  // Tile loads: load i of this wave fills LDS rows (wave*NI + i)*RPI + lane/CPR
+  // of the K and the V tile, lane l the chunk slot l % CPR.
   const int32_t* bt = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
-  const uint4* kp = static_cast<const uint4*>(a.k_pool);
-  const uint4* vp = static_cast<const uint4*>(a.v_pool);
+  const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool);
+  const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool);
   const int B = a.block_size, Bm1 = B - 1;
-  const int lc = tid % PS::CPR;        // this thread's 16-byte dim chunk
-  const int lk = (tid / PS::CPR) * KPT;  // its first key in the tile
-  uint4 kst[KPT], vst[KPT];
-  auto load_tile = [&](int kt) {
-    const int t_first = kt * kKeys + lk;
-    if (kt * kKeys + kKeys <= L && B >= KPT) {
-      // whole tile inside the sequence: KPT consecutive keys of one block
-      const int64_t pb = bt[t_first >> b_shift];
-      const uint4* kb = kp + ((pb * Hkv + kvh) * B + (t_first & Bm1)) * PS::CPR + lc;
-      const uint4* vb = vp + (kb - kp);
+  const uint32_t lds0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)smem));
+  int ld_row[NI], ld_chunk[NI];
 #pragma unroll
-      for (int q = 0; q < KPT; ++q) {
-        kst[q] = load_stream16(kb + q * PS::CPR);
-        vst[q] = load_stream16(vb + q * PS::CPR);
-      }
-      return;
-    }
-    const int64_t pb_first = bt[min(t_first, L - 1) >> b_shift];
+  for (int i = 0; i < NI; ++i) {
+    ld_row[i] = (wave * NI + i) * PS::RPI + lane / PS::CPR;
+    ld_chunk[i] = (lane % PS::CPR) ^ swz<PS::CPR>(ld_row[i]);
+  }
+  auto load_table = [&](int kt, int32_t (&tab)[NI]) {
 #pragma unroll
-    for (int q = 0; q < KPT; ++q) {
-      const int t = min(t_first + q, L - 1);  // past the end: a valid, masked key
-      // the KPT keys share a block unless blocks are smaller than KPT
-      const int64_t pb = B >= KPT ? pb_first : int64_t(bt[t >> b_shift]);
-      const int64_t idx = ((pb * Hkv + kvh) * B + (t & Bm1)) * PS::CPR + lc;
-      kst[q] = load_stream16(kp + idx);
-      vst[q] = load_stream16(vp + idx);
+    for (int i = 0; i < NI; ++i) tab[i] = bt[min(kt * kKeys + ld_row[i], L - 1) >> b_shift];
+  };
+  auto issue_tile = [&](int kt, const int32_t (&tab)[NI]) {
+    const uint32_t st = lds0 + uint32_t((kt % 2) * PS::STAGE);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int t = min(kt * kKeys + ld_row[i], L - 1);  // past the end: a valid, masked key
+      const int64_t off =
+          ((int64_t(tab[i]) * Hkv + kvh) * B + (t & Bm1)) * PS::ROW + ld_chunk[i] * 16;
+      const uint32_t dst = st + uint32_t((wave * NI + i) * 1024);
+      load_lds16(kpool + off, dst);
+      load_lds16(vpool + off, dst + PS::TILE);
     }
   };
-  auto store_tile = [&](int buf) {
-    unsigned char* k_lds = smem + buf * (PS::K_BYTES + PS::V_BYTES);
-    unsigned char* v_lds = k_lds + PS::K_BYTES;
-#pragma unroll
-    for (int q = 0; q < KPT; ++q) {
-      *reinterpret_cast<uint4*>(k_lds + (lk + q) * PS::K_STRIDE + lc * 16) = kst[q];
-      *reinterpret_cast<uint4*>(v_lds + (lk + q) * PS::V_STRIDE + lc * 16) = vst[q];
-    }
-  };
-  // transposed-read address of this lane inside a V tile: key offset and byte column
-  const int tr_key = 4 * g + (lane % 16) / 4;
-  const int tr_col = (((lane / 16) % 2) * 16 + 4 * (lane % 4)) * 2;
+
+  // Operand-read byte addresses inside a stage.
+  // K: row mt*32 + lane%32, chunk 2ks + g  ->  (k_addr ^ 32 ks) + mt * 32 rows.
+  const int kr = lane % 32;
+  const uint32_t k_addr = uint32_t(kr * PS::ROW + ((g ^ swz<PS::CPR>(kr)) * 16));
+  // V, read transposed: rows 16kk + 4g + (lane%16)/4 (+8 for the upper four
+  // keys), dims 32dt + 16((lane/16)%2) + 4(lane%4) .. +3, i.e. chunk 4dt + cl,
+  // half lane%2  ->  (v_lo ^ 64 dt) + 16 kk rows.
+  const int vr = 4 * g + (lane % 16) / 4;
+  const int cl = 2 * ((lane / 16) % 2) + (lane % 4) / 2;
+  const uint32_t v_lo =
+      uint32_t(PS::TILE + vr * PS::ROW + ((cl ^ swz<PS::CPR>(vr)) * 16) + 8 * (lane % 2));
+  const uint32_t v_hi =
+      uint32_t(PS::TILE + (vr + 8) * PS::ROW + ((cl ^ swz<PS::CPR>(vr + 8)) * 16) + 8 * (lane % 2));
 
   f32x16_t o[PS::DTILES];
 #pragma unroll
@@ -178,31 +218,38 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
   float m = -INFINITY, lsum = 0.f;  // running max in raw score units
 
-  load_tile(0);
-  store_tile(0);
-  if (n_ktiles > 1) load_tile(1);
+  int32_t tab[NI];
+  load_table(0, tab);
+  issue_tile(0, tab);
+  if (n_ktiles > 1) load_table(1, tab);
   for (int kt = 0; kt < n_ktiles; ++kt) {
-    __syncthreads();  // tile kt's LDS writes are visible; buffer (kt+1)%2 is free again
-    if (kt + 1 < n_ktiles) store_tile((kt + 1) % 2);
-    if (kt + 2 < n_ktiles) load_tile(kt + 2);  // in flight during the math of tile kt
+    // tile kt is in LDS for every wave, and every wave is done with tile
+    // kt-1, whose stage the loads of tile kt+1 now overwrite
+    drain_and_barrier();
+    if (kt + 1 < n_ktiles) issue_tile(kt + 1, tab);
+    if (kt + 2 < n_ktiles) load_table(kt + 2, tab);
     const int t0 = kt * kKeys;
     if (!wave_active || t0 > wave_last_key) continue;  // uniform per wave
-    const unsigned char* k_lds = smem + (kt % 2) * (PS::K_BYTES + PS::V_BYTES);
-    const unsigned char* v_lds = k_lds + PS::K_BYTES;
+    const unsigned char* stage = smem + (kt % 2) * PS::STAGE;
 
     // S^T = K Q^T for keys t0 .. t0+63 (two 32-key m-tiles)
+    uint4 kop[2][PS::KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < PS::KSTEPS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        kop[mt][ks] = *reinterpret_cast<const uint4*>(
+            stage + ((k_addr ^ (32u * ks)) + mt * 32 * PS::ROW));
     f32x16_t sacc[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.f;
-      const unsigned char* krow = k_lds + (mt * 32 + lane % 32) * PS::K_STRIDE + g * 16;
 #pragma unroll
-      for (int ks = 0; ks < PS::KSTEPS; ++ks) {
-        const uint4 kop = *reinterpret_cast<const uint4*>(krow + ks * 32);
-        sacc[mt] = mfma32(kop, qop[ks], sacc[mt]);
-      }
-    }
+    for (int ks = 0; ks < PS::KSTEPS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma32(kop[mt][ks], qop[ks], sacc[mt]);
+
     // causal mask only where the tile reaches the diagonal (or rows past the chunk)
     if (wave_ragged || t0 + kKeys - 1 > start + row0) {
 #pragma unroll
@@ -254,14 +301,14 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     // O^T += V^T P^T; operand j of half g in k-step kk = (mt, h) is key
     // 16 kk + 8 (j / 4) + 4 g + j % 4, matching the S^T accumulator order
 #pragma unroll
-    for (int dt = 0; dt < PS::DTILES; ++dt) {
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const unsigned char* va = v_lds + (16 * kk + tr_key) * PS::V_STRIDE + dt * 64 + tr_col;
+      for (int dt = 0; dt < PS::DTILES; ++dt) {
+        const uint32_t rows = uint32_t(kk * 16 * PS::ROW);
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16_t*)(va));
+            (lds_v4i16_t*)(stage + ((v_lo ^ (64u * dt)) + rows)));
         const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16_t*)(va + 8 * PS::V_STRIDE));
+            (lds_v4i16_t*)(stage + ((v_hi ^ (64u * dt)) + rows)));
         const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
         o[dt] = mfma32(make_uint4(l2.x, l2.y, h2.x, h2.y), pop[kk], o[dt]);
       }
@@ -310,12 +357,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
   const float scale_log2 = a.scale * kLog2e;
   if (a.head_dim == 128) {
-    using PS = PrefillShape<128>;
-    prefill_kernel<128><<<int(blocks), kWave * kWaves, 2 * (PS::K_BYTES + PS::V_BYTES), st>>>(
+    prefill_kernel<128><<<int(blocks), kWave * kWaves, PrefillShape<128>::LDS, st>>>(
         a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
   } else if (a.head_dim == 64) {
-    using PS = PrefillShape<64>;
-    prefill_kernel<64><<<int(blocks), kWave * kWaves, 2 * (PS::K_BYTES + PS::V_BYTES), st>>>(
+    prefill_kernel<64><<<int(blocks), kWave * kWaves, PrefillShape<64>::LDS, st>>>(
         a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
   } else {
     return hipErrorInvalidValue;
