@@ -55,6 +55,8 @@ typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef short bf16x2_t __attribute__((__vector_size__(2 * sizeof(short))));
+typedef __attribute__((address_space(4))) const int32_t const_i32;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8_t, v);
@@ -92,13 +94,24 @@ __device__ __forceinline__ int swz(int r) {
 // 16 bytes per lane from global memory into LDS at lds_addr + 16 * lane.
 // Issued from inline assembly so that the compiler does not put a wait for
 // it in front of every later LDS read; completion is awaited explicitly
-// (vmcnt) before the barrier that publishes the tile.
+// (vmcnt) before the barrier that publishes the tile. M0 holds the LDS
+// address; nothing else in this kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load_lds16(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gptr), "s"(lds_addr)
                : "memory", "m0");
 }
+// Same, from a wave-uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // Wait for every outstanding load of this wave (including the direct-to-LDS
 // ones) and every LDS access, then meet the other waves. The wait is the
@@ -111,7 +124,9 @@ __device__ __forceinline__ void drain_and_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D>
+// WAVE_BLOCK: blocks of at least 16 tokens, so that a wave's 16 keys of a
+// tile lie in one block.
+template <int D, bool WAVE_BLOCK>
 __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     PrefillArgs a, int32_t b_shift, int32_t heads_per_group, int32_t n_hchunk, int32_t n_rtiles,
     float scale_log2) {
@@ -167,7 +182,8 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
   }
 
   // Tile loads: load i of this wave fills LDS rows (wave*NI + i)*RPI + lane/CPR
-  // of the K and the V tile, lane l the chunk slot l % CPR.
+  // of the K and the V tile, lane l the chunk slot l % CPR. A wave's loads
+  // cover the 16 consecutive keys kt*64 + 16*wave .. +15.
   const int32_t* bt = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
   const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool);
   const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool);
@@ -175,25 +191,56 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
   const uint32_t lds0 = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)smem));
   int ld_row[NI], ld_chunk[NI];
+  uint32_t ld_off[NI];  // byte offset of this lane's chunk from the wave's first row
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     ld_row[i] = (wave * NI + i) * PS::RPI + lane / PS::CPR;
     ld_chunk[i] = (lane % PS::CPR) ^ swz<PS::CPR>(ld_row[i]);
+    ld_off[i] = uint32_t((i * PS::RPI + lane / PS::CPR) * PS::ROW + ld_chunk[i] * 16);
   }
-  auto load_table = [&](int kt, int32_t (&tab)[NI]) {
+  // WAVE_BLOCK: the wave's block is found with one scalar load; clamped keys
+  // (past the end) stay in it, since it is looked up for min(first key, L-1).
+  const_i32* btc = (const_i32*)bt;
+  const int64_t head_bytes = int64_t(kvh) * B * PS::ROW;
+  const int64_t block_bytes = int64_t(Hkv) * B * PS::ROW;
+  auto load_table = [&](int kt, int32_t (&tab)[NI], int32_t& sblk) {
+    if constexpr (WAVE_BLOCK) {
+      sblk = btc[min(kt * kKeys + 16 * wave, L - 1) >> b_shift];
+    } else {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) tab[i] = bt[min(kt * kKeys + ld_row[i], L - 1) >> b_shift];
+      for (int i = 0; i < NI; ++i) tab[i] = bt[min(kt * kKeys + ld_row[i], L - 1) >> b_shift];
+    }
   };
-  auto issue_tile = [&](int kt, const int32_t (&tab)[NI]) {
-    const uint32_t st = lds0 + uint32_t((kt % 2) * PS::STAGE);
+  auto issue_tile = [&](int kt, const int32_t (&tab)[NI], int32_t sblk) {
+    const uint32_t st = lds0 + uint32_t((kt % 2) * PS::STAGE) + uint32_t(wave * NI * 1024);
+    const int key0 = kt * kKeys + 16 * wave;
+    if constexpr (WAVE_BLOCK) {
+      const int64_t base = int64_t(sblk) * block_bytes + head_bytes;
+      if (key0 + 16 <= L) {  // no clamping: every offset is a per-lane constant
+        const int64_t wb = base + int64_t(key0 & Bm1) * PS::ROW;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          load_lds16(kpool + wb, ld_off[i], st + uint32_t(i * 1024));
+          load_lds16(vpool + wb, ld_off[i], st + uint32_t(i * 1024 + PS::TILE));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int t = min(kt * kKeys + ld_row[i], L - 1);  // past the end: a valid, masked key
+          const uint32_t off = uint32_t((t & Bm1) * PS::ROW + ld_chunk[i] * 16);
+          load_lds16(kpool + base, off, st + uint32_t(i * 1024));
+          load_lds16(vpool + base, off, st + uint32_t(i * 1024 + PS::TILE));
+        }
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t = min(kt * kKeys + ld_row[i], L - 1);  // past the end: a valid, masked key
-      const int64_t off =
-          ((int64_t(tab[i]) * Hkv + kvh) * B + (t & Bm1)) * PS::ROW + ld_chunk[i] * 16;
-      const uint32_t dst = st + uint32_t((wave * NI + i) * 1024);
-      load_lds16(kpool + off, dst);
-      load_lds16(vpool + off, dst + PS::TILE);
+      const int64_t off = int64_t(tab[i]) * block_bytes + head_bytes +
+                          int64_t((t & Bm1) * PS::ROW + ld_chunk[i] * 16);
+      load_lds16(kpool + off, st + uint32_t(i * 1024));
+      load_lds16(vpool + off, st + uint32_t(i * 1024 + PS::TILE));
+    }
     }
   };
 
@@ -218,16 +265,16 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
   float m = -INFINITY, lsum = 0.f;  // running max in raw score units
 
-  int32_t tab[NI];
-  load_table(0, tab);
-  issue_tile(0, tab);
-  if (n_ktiles > 1) load_table(1, tab);
+  int32_t tab[NI], sblk = 0;
+  load_table(0, tab, sblk);
+  issue_tile(0, tab, sblk);
+  if (n_ktiles > 1) load_table(1, tab, sblk);
   for (int kt = 0; kt < n_ktiles; ++kt) {
     // tile kt is in LDS for every wave, and every wave is done with tile
     // kt-1, whose stage the loads of tile kt+1 now overwrite
     drain_and_barrier();
-    if (kt + 1 < n_ktiles) issue_tile(kt + 1, tab);
-    if (kt + 2 < n_ktiles) load_table(kt + 2, tab);
+    if (kt + 1 < n_ktiles) issue_tile(kt + 1, tab, sblk);
+    if (kt + 2 < n_ktiles) load_table(kt + 2, tab, sblk);
     const int t0 = kt * kKeys;
     if (!wave_active || t0 > wave_last_key) continue;  // uniform per wave
     const unsigned char* stage = smem + (kt % 2) * PS::STAGE;
@@ -276,7 +323,6 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     const float nms = -ms * scale_log2;
     const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m, scale_log2, nms)) : 1.f;
     m = mn;
-    float ps = 0.f;
     uint4 pop[4];  // P^T operands for the four 16-key k-steps
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -284,14 +330,22 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
       for (int h = 0; h < 2; ++h) {
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 8; ++j)
           p[j] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * h + j], scale_log2, nms));
-          ps += p[j];
-        }
         pop[2 * mt + h] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
                                      pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
       }
-    lsum = lsum * alpha + ps;
+    // the row sum adds up the same bf16 weights that the PV product uses
+    const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].x), ones, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].y), ones, ps1, false);
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].z), ones, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].w), ones, ps1, false);
+    }
+    lsum = lsum * alpha + (ps0 + ps1);
     if (__ballot(moved)) {  // exact: alpha == 1 where no row max moved
 #pragma unroll
       for (int dt = 0; dt < PS::DTILES; ++dt)
@@ -356,12 +410,20 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const int64_t blocks = int64_t(a.num_seqs) * a.num_kv_heads * n_hchunk * n_rtiles;
   if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
   const float scale_log2 = a.scale * kLog2e;
+  const bool wave_block = b_shift >= 4;
+  const dim3 grid{unsigned(blocks)}, block{unsigned(kWave * kWaves)};
   if (a.head_dim == 128) {
-    prefill_kernel<128><<<int(blocks), kWave * kWaves, PrefillShape<128>::LDS, st>>>(
-        a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
+    constexpr int lds = PrefillShape<128>::LDS;
+    if (wave_block)
+      prefill_kernel<128, true><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
+    else
+      prefill_kernel<128, false><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
   } else if (a.head_dim == 64) {
-    prefill_kernel<64><<<int(blocks), kWave * kWaves, PrefillShape<64>::LDS, st>>>(
-        a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
+    constexpr int lds = PrefillShape<64>::LDS;
+    if (wave_block)
+      prefill_kernel<64, true><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
+    else
+      prefill_kernel<64, false><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
   } else {
     return hipErrorInvalidValue;
   }
