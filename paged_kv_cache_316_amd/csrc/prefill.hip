@@ -37,7 +37,9 @@
 //    beyond a wave's last row are skipped.
 //  * Workgroups that read the same (sequence, KV head) stream are placed on
 //    the same XCD (workgroup i runs on XCD i mod 8), so its L2 serves the
-//    repeated K/V reads; the longest (last) row tiles are dispatched first.
+//    repeated K/V reads, and these groups are dealt round-robin over the
+//    XCDs so that sequences of different lengths load them evenly; within a
+//    group the longest (last) row tiles are dispatched first.
 #include <math.h>
 
 #include "device.h"
@@ -129,7 +131,7 @@ __device__ __forceinline__ void drain_and_barrier() {
 template <int D, bool WAVE_BLOCK>
 __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     PrefillArgs a, int32_t b_shift, int32_t heads_per_group, int32_t n_hchunk, int32_t n_rtiles,
-    float scale_log2) {
+    int32_t chunk_wgs, int32_t chunks_per_group, float scale_log2) {
   using PS = PrefillShape<D>;
   constexpr int NI = PS::NI;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -142,17 +144,21 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
   const int G = Hq / Hkv;
   const int R = kWaves / heads_per_group;  // row tiles per workgroup
 
-  // workgroup -> (sequence, KV head, head chunk, row tile); workgroups of one
-  // (sequence, KV head) are contiguous after the XCD swizzle
-  const int nblk = gridDim.x;
-  int b = blockIdx.x;
-  if (nblk % kXcds == 0) b = (b % kXcds) * (nblk / kXcds) + b / kXcds;
-  const int rt_rev = b % n_rtiles;
-  int rest = b / n_rtiles;
-  const int hc = rest % n_hchunk;
-  rest /= n_hchunk;
-  const int kvh = rest % Hkv;
-  const int s = rest / Hkv;
+  // Workgroup -> (sequence, KV head, head chunk, row tile). The workgroups of
+  // one (sequence, KV head) group read the same K/V and are cut into chunks
+  // of chunk_wgs; hardware workgroup i runs on XCD i % 8, and XCD x takes
+  // chunks x, x+8, x+16, ... so that every chunk stays on one XCD (its L2
+  // serves the repeated K/V reads) and the groups are dealt out evenly.
+  const int gs = n_hchunk * n_rtiles;  // workgroups per group
+  const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int c = (j / chunk_wgs) * kXcds + x;
+  const int group = c / chunks_per_group;
+  const int member = (c % chunks_per_group) * chunk_wgs + j % chunk_wgs;
+  if (group >= a.num_seqs * a.num_kv_heads || member >= gs) return;  // grid padding
+  const int rt_rev = member % n_rtiles;
+  const int hc = member / n_rtiles;
+  const int kvh = group % a.num_kv_heads;
+  const int s = group / a.num_kv_heads;
   const int rt = n_rtiles - 1 - rt_rev;  // longest rows first
 
   const int q0 = a.q_start_loc[s];
@@ -407,23 +413,32 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const int n_hchunk = G / hpg;
   const int rows_per_wg = (kWaves / hpg) * kRows;
   const int n_rtiles = (a.max_q_len + rows_per_wg - 1) / rows_per_wg;
-  const int64_t blocks = int64_t(a.num_seqs) * a.num_kv_heads * n_hchunk * n_rtiles;
-  if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  // deal (sequence, KV head) groups to the XCDs; split groups when there are
+  // too few of them to give every XCD several chunks
+  const int64_t n_groups = int64_t(a.num_seqs) * a.num_kv_heads;
+  const int gs = n_hchunk * n_rtiles;
+  int split = 1;
+  while (n_groups * split < 4 * kXcds && split < gs) split *= 2;
+  const int chunk_wgs = (gs + split - 1) / split;
+  const int chunks_per_group = (gs + chunk_wgs - 1) / chunk_wgs;
+  const int64_t n_chunks = n_groups * chunks_per_group;
+  const int64_t blocks = (n_chunks + kXcds - 1) / kXcds * kXcds * chunk_wgs;
+  if (n_groups <= 0 || gs <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
   const float scale_log2 = a.scale * kLog2e;
   const bool wave_block = b_shift >= 4;
   const dim3 grid{unsigned(blocks)}, block{unsigned(kWave * kWaves)};
   if (a.head_dim == 128) {
     constexpr int lds = PrefillShape<128>::LDS;
     if (wave_block)
-      prefill_kernel<128, true><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
+      prefill_kernel<128, true><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, chunk_wgs, chunks_per_group, scale_log2);
     else
-      prefill_kernel<128, false><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
+      prefill_kernel<128, false><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, chunk_wgs, chunks_per_group, scale_log2);
   } else if (a.head_dim == 64) {
     constexpr int lds = PrefillShape<64>::LDS;
     if (wave_block)
-      prefill_kernel<64, true><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
+      prefill_kernel<64, true><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, chunk_wgs, chunks_per_group, scale_log2);
     else
-      prefill_kernel<64, false><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, scale_log2);
+      prefill_kernel<64, false><<<grid, block, lds, st>>>(a, b_shift, hpg, n_hchunk, n_rtiles, chunk_wgs, chunks_per_group, scale_log2);
   } else {
     return hipErrorInvalidValue;
   }
