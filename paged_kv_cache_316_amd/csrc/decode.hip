@@ -143,26 +143,20 @@ struct Cursor {
   int64_t seg0;
 };
 
-template <int DTYPE, int D, int HPW, bool BIG_B>
-__global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_kernel(
-    DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
-  using RS = RowShape<DTYPE, D>;
-  constexpr int VEC = RS::VEC, LPR = RS::LPR, NR = RS::NR;
-  constexpr int U = kTile / NR;  // 16-byte loads per lane per tile, for K and for V
-  static_assert(kTile % NR == 0, "a tile must cover whole load rows");
-  constexpr int QF = VEC > 4 ? 4 : VEC;
-
-  const int lane = threadIdx.x % kWave;
-  const int w = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+// This wave's slice of the work list, walked segment by segment: for each
+// segment (sequence, unit) it calls begin(cursor), run(cursor, j0, j1) for
+// the slice's tiles [j0, j1) of it, and end(cursor, owns_start, owns_end),
+// then records the segment the slice starts and leaves open (if any) for the
+// combine kernel. Also writes zeros for empty sequences. VEC: elements of the
+// output dtype per 16 bytes; hpw: query heads per unit.
+template <int D, int VEC, class Begin, class Run, class End>
+__device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane, int n_hchunk,
+                                           int hpw, Begin begin, Run run, End end) {
   const int S = a.num_seqs;
-  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-  const int G = Hq / Hkv;
-  const int units = Hkv * n_hchunk;
-  const int r = lane / LPR, c = lane % LPR;
-  const int B = a.block_size, Bm1 = B - 1;
-  if (w >= a.workers) return;
+  const int Hq = a.num_q_heads;
+  const int G = Hq / a.num_kv_heads;
+  const int units = a.num_kv_heads * n_hchunk;
 
-  // ---- the work list: total tiles, this wave's slice -----------------------
   int64_t total = 0;
   for (int base = 0; base < S; base += kWave) {
     const int s = base + lane;
@@ -222,6 +216,60 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
       before = uniform64(__shfl(incl, kWave - 1));
     }
   }
+
+
+  // walk the segments of this slice
+  int64_t g = g_begin;
+  int4 split = make_int4(-1, 0, 0, 0);  // the segment this slice starts and leaves unfinished
+  while (true) {
+    const int j1 = int(min(int64_t(cur.n), int64_t(cur.j) + (g_end - g)));
+    const bool owns_start = cur.j == 0, owns_end = j1 == cur.n;
+    begin(cur);
+    run(cur, cur.j, j1);
+    end(cur, owns_start, owns_end);
+    if (owns_start && !owns_end) {  // only the last segment of a slice can be left open
+      const int64_t last = cur.seg0 + cur.n - 1;
+      split = make_int4(cur.s, cur.u, int(((last + 1) * W - 1) / total),
+                        cur.kvh * G + cur.hc * hpw);
+    }
+    g += j1 - cur.j;
+    if (g >= g_end) break;
+    // next segment: next unit of this sequence, or the next non-empty sequence
+    cur.j = 0;
+    cur.seg0 += cur.n;
+    ++cur.u;
+    if (++cur.hc == n_hchunk) {
+      cur.hc = 0;
+      ++cur.kvh;
+    }
+    if (cur.u == units) {
+      cur.u = cur.kvh = cur.hc = 0;
+      do {
+        ++cur.s;
+        cur.L = seq_len(cur.s);
+        cur.n = tiles_of(cur.L);
+      } while (cur.n == 0);
+    }
+  }
+  if (lane == 0) a.ws_seg[w] = split;
+}
+
+template <int DTYPE, int D, int HPW, bool BIG_B>
+__global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_kernel(
+    DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
+  using RS = RowShape<DTYPE, D>;
+  constexpr int VEC = RS::VEC, LPR = RS::LPR, NR = RS::NR;
+  constexpr int U = kTile / NR;  // 16-byte loads per lane per tile, for K and for V
+  static_assert(kTile % NR == 0, "a tile must cover whole load rows");
+  constexpr int QF = VEC > 4 ? 4 : VEC;
+
+  const int lane = threadIdx.x % kWave;
+  const int w = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int r = lane / LPR, c = lane % LPR;
+  const int B = a.block_size, Bm1 = B - 1;
+  if (w >= a.workers) return;
 
   const uint4* kp = static_cast<const uint4*>(a.k_pool);
   const uint4* vp = static_cast<const uint4*>(a.v_pool);
@@ -396,39 +444,214 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
     }
   };
 
-  // ---- walk the segments of this slice ------------------------------------------
-  int64_t g = g_begin;
-  int4 split = make_int4(-1, 0, 0, 0);  // the segment this slice starts and leaves unfinished
-  while (true) {
-    const int j1 = int(min(int64_t(cur.n), int64_t(cur.j) + (g_end - g)));
-    const bool owns_start = cur.j == 0, owns_end = j1 == cur.n;
-    begin_segment(cur);
-    run_tiles(cur, cur.j, j1);
-    end_segment(cur, owns_start, owns_end);
-    if (owns_start && !owns_end) {  // only the last segment of a slice can be left open
-      const int64_t last = cur.seg0 + cur.n - 1;
-      split = make_int4(cur.s, cur.u, int(((last + 1) * W - 1) / total), head_of(cur));
-    }
-    g += j1 - cur.j;
-    if (g >= g_end) break;
-    // next segment: next unit of this sequence, or the next non-empty sequence
-    cur.j = 0;
-    cur.seg0 += cur.n;
-    ++cur.u;
-    if (++cur.hc == n_hchunk) {
-      cur.hc = 0;
-      ++cur.kvh;
-    }
-    if (cur.u == units) {
-      cur.u = cur.kvh = cur.hc = 0;
-      do {
-        ++cur.s;
-        cur.L = seq_len(cur.s);
-        cur.n = tiles_of(cur.L);
-      } while (cur.n == 0);
-    }
+  walk_slice<D, VEC>(a, w, lane, n_hchunk, HPW, begin_segment, run_tiles, end_segment);
+}
+
+// GQA decode on the matrix cores (bf16, HPW >= 4 query heads per KV head).
+// Same work list, partials and combine as decode_balanced_kernel; per 16-token
+// tile of a unit:
+//  * K and V tiles are loaded with whole rows per lane group (each 16-byte
+//    load instruction covers 1 KB of consecutive rows), which the memory
+//    system serves far better than operand-shaped loads that touch every
+//    cache line of the tile, and written to the wave's own 8 KB of LDS (16-byte
+//    chunk c of row r kept at c ^ f(r), f a bijection over the rows that
+//    share a bank line position, so that every read below is conflict-free).
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: M = the 16 keys, N = the
+//    unit's query heads (HPW of 16 columns used), K = head_dim in D/32 steps;
+//    lane l reads its A operand (key l%16, 8 dims) from LDS.
+//  * The accumulator gives lane l the scores of head l%16 for keys
+//    4(l/16) + i, which is exactly the B operand (P^T) of
+//    v_mfma_f32_16x16x16_bf16 for O^T = V^T P^T, so p needs no shuffle.
+//  * V^T, the A operand of that product, needs 4 consecutive keys of one dim
+//    per lane: ds_read_b64_tr_b16 reads it from the V tile transposed.
+//  * Online softmax per head with the exponent base moved only when a head's
+//    max grows by more than 2^8 (exact, as numerator and denominator share
+//    it); the row sum adds the bf16 weights the product uses.
+// The MFMA work is a small fraction of the time the tile's bytes take to
+// arrive, so the kernel streams K/V like the MHA kernel while the per-head
+// VALU work of that kernel (dot products, reductions) disappears.
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+template <int D, int HPW, bool BIG_B>
+__global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
+    DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
+  constexpr int ROW = 2 * D;        // bytes per K/V row
+  constexpr int KS = D / 32;        // 16x16x32 k-steps over head_dim
+  constexpr int DT = D / 16;        // 16-dim tiles of O^T
+  constexpr int CPR = ROW / 16;     // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROW;   // rows per wave-wide 16-byte load
+  constexpr int NI = kTile / RPI;   // loads per lane per tile, for K and for V
+  constexpr int RPL = 256 / ROW;    // rows per 256-byte LDS bank line
+  constexpr int TB = kTile * ROW;   // bytes of one K or V tile
+  static_assert(HPW <= 16, "one MFMA N tile holds the unit's heads");
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int lane = threadIdx.x % kWave;
+  const int wig = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int w = blockIdx.x * (blockDim.x / kWave) + wig;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int g = lane / 16, i16 = lane % 16;
+  const int B = a.block_size, Bm1 = B - 1;
+  if (w >= a.workers) return;
+
+  unsigned char* kt_lds = smem + wig * (2 * TB);  // this wave's K tile, then its V tile
+  unsigned char* vt = kt_lds + TB;
+  auto swz = [](int r) { return (r / RPL) % CPR; };
+  // load u of lane l: row u*RPI + l/CPR, chunk l%CPR (written to LDS the same way)
+  const int lrow = lane / CPR, lch = lane % CPR;
+  uint32_t wr[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int r = u * RPI + lrow;
+    wr[u] = uint32_t(r * ROW + ((lch ^ swz(r)) * 16));
   }
-  if (lane == 0) a.ws_seg[w] = split;
+  // K operand of k-step ks: row i16, chunk 4ks + g  ->  kr0 ^ (64 ks)
+  const uint32_t kr0 = uint32_t(i16 * ROW + ((g ^ swz(i16)) * 16));
+  // V, read transposed: lane (g, 4k+q) points at row 4g + k, dims 16 dt + 4q .. +3
+  const int rr = 4 * g + i16 / 4;
+  const uint32_t rd0 = uint32_t(rr * ROW + 8 * (i16 % 2) + (((i16 % 4) / 2) ^ swz(rr)) * 16);
+
+  const unsigned char* kp = static_cast<const unsigned char*>(a.k_pool);
+  const unsigned char* vp = static_cast<const unsigned char*>(a.v_pool);
+  const int64_t block_bytes = int64_t(Hkv) * B * ROW;
+
+  uint4 qop[KS];
+  f32x4_t o[DT];
+  float m, lpart;
+  const float c2 = scale_log2;
+  auto head_of = [&](const Cursor& x) { return x.kvh * G + x.hc * HPW; };
+  auto begin_segment = [&](const Cursor& x) {
+    // columns past the unit's heads multiply zeros (their load is clamped to a real head)
+    const unsigned char* qp = static_cast<const unsigned char*>(a.q) +
+                              (int64_t(x.s) * Hq + head_of(x) + min(i16, HPW - 1)) * ROW + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 qv = *reinterpret_cast<const uint4*>(qp + 64 * ks);
+      qop[ks] = i16 < HPW ? qv : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    lpart = 0.f;
+  };
+
+  auto compute = [&](int j, int L, const uint4* kr, const uint4* vr) {
+    // tiles -> LDS (the previous tile's reads were issued earlier by this
+    // wave, and LDS serves one wave's accesses in order)
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      *reinterpret_cast<uint4*>(kt_lds + wr[u]) = kr[u];
+      *reinterpret_cast<uint4*>(vt + wr[u]) = vr[u];
+    }
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 kop = *reinterpret_cast<const uint4*>(kt_lds + (kr0 ^ (64u * ks)));
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop),
+                                                  __builtin_bit_cast(bf16x8_t, qop[ks]), sc, 0, 0, 0);
+    }
+    const int key0 = j * kTile + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (key0 + i >= L) sc[i] = -INFINITY;
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool moved = m == -INFINITY ? mx != -INFINITY : (mx - m) * c2 > 8.f;
+    const float mn = moved ? mx : m;
+    const float nms = mn == -INFINITY ? 0.f : -mn * c2;
+    const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m, c2, nms)) : 1.f;
+    m = mn;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, nms));
+    const uint2 pb = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
+    const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+    float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb.x), ones, 0.f, false);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb.y), ones, ps, false);
+    lpart = lpart * alpha + ps;
+    if (__ballot(moved)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)(vt + (rd0 ^ (32u * dt))));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(bf16x4_t, pb),
+                                                      o[dt], 0, 0, 0);
+    }
+  };
+
+  auto end_segment = [&](const Cursor& x, bool owns_start, bool owns_end) {
+    float l = lpart + __shfl_xor(lpart, 16);
+    l += __shfl_xor(l, 32);
+    if (i16 >= HPW) return;
+    if (owns_start && owns_end) {
+      const float inv = 1.f / l;
+      uint2* orow = reinterpret_cast<uint2*>(static_cast<unsigned char*>(a.out) +
+                                             (int64_t(x.s) * Hq + head_of(x) + i16) * ROW);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        orow[(16 * dt + 4 * g) / 4] = make_uint2(pack_bf16(o[dt][0] * inv, o[dt][1] * inv),
+                                                 pack_bf16(o[dt][2] * inv, o[dt][3] * inv));
+      return;
+    }
+    const int slot = 2 * w + (owns_start ? 1 : 0);
+    float4* dst = reinterpret_cast<float4*>(a.ws_acc + (int64_t(slot) * HPW + i16) * D);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      dst[(16 * dt + 4 * g) / 4] = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (g == 0) a.ws_ml[int64_t(slot) * HPW + i16] = make_float2(m * c2, l);
+  };
+
+  // Tiles [j0, j1) of one segment, in chunks whose blocks fit a 64-entry
+  // window of the block table; branch-free and double-buffered as in the
+  // VALU kernel. Keys past the end are clamped to the last token (a valid,
+  // written slot) and masked out in compute.
+  auto run_tiles = [&](const Cursor& x, int j0, int j1) {
+    const int32_t* row = a.block_tables + int64_t(x.s) * a.max_blocks_per_seq;
+    const int nblk = (x.L + Bm1) >> b_shift;
+    const int Lm1 = x.L - 1;
+    const int64_t head_off = int64_t(x.kvh) * B * ROW + lch * 16;
+    for (int jc = j0; jc < j1;) {
+      const int jb0 = (jc * kTile) >> b_shift;
+      const int win = jb0 + lane < nblk ? row[jb0 + lane] : 0;
+      const int jc_end = min(j1, ((jb0 + kWave) << b_shift) / kTile);
+      auto load_tile = [&](int j, uint4* kr, uint4* vr) {
+        int pb = 0;
+        if constexpr (BIG_B) pb = __builtin_amdgcn_readlane(win, ((j * kTile) >> b_shift) - jb0);
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+          const int t = min(j * kTile + u * RPI + lrow, Lm1);
+          if constexpr (!BIG_B) pb = __shfl(win, (t >> b_shift) - jb0);
+          const int64_t off = int64_t(pb) * block_bytes + head_off + int64_t(t & Bm1) * ROW;
+          kr[u] = load_stream16(reinterpret_cast<const uint4*>(kp + off));
+          vr[u] = load_stream16(reinterpret_cast<const uint4*>(vp + off));
+        }
+      };
+      uint4 kA[NI], vA[NI], kB[NI], vB[NI];
+      int j = jc;
+      load_tile(j, kA, vA);
+      for (; j + 2 <= jc_end; j += 2) {
+        load_tile(j + 1, kB, vB);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(j, x.L, kA, vA);
+        if (j + 2 < jc_end) load_tile(j + 2, kA, vA);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(j + 1, x.L, kB, vB);
+      }
+      if (j < jc_end) compute(j, x.L, kA, vA);
+      jc = jc_end;
+    }
+  };
+
+  walk_slice<D, 8>(a, w, lane, n_hchunk, HPW, begin_segment, run_tiles, end_segment);
 }
 
 // Combine the partials of each split segment. Wave w looks at the segment
@@ -491,12 +714,22 @@ hipError_t run(const DecodeArgs& a, hipStream_t st) {
   wpg = wpg < 1 ? 1 : (wpg > kMaxWavesPerGroup ? kMaxWavesPerGroup : wpg);
   const int groups = (a.workers + wpg - 1) / wpg;
   const float scale_log2 = a.scale * kLog2e;
-  if (a.block_size >= kTile)
-    decode_balanced_kernel<DTYPE, D, HPW, true>
-        <<<groups, kWave * wpg, 0, st>>>(a, b_shift, n_hchunk, scale_log2);
-  else
-    decode_balanced_kernel<DTYPE, D, HPW, false>
-        <<<groups, kWave * wpg, 0, st>>>(a, b_shift, n_hchunk, scale_log2);
+  if constexpr (DTYPE == PA_BF16 && HPW >= 4) {
+    const size_t lds = size_t(wpg) * 2 * kTile * 2 * D;  // a K and a V tile per wave
+    if (a.block_size >= kTile)
+      decode_mfma_kernel<D, HPW, true>
+          <<<groups, kWave * wpg, lds, st>>>(a, b_shift, n_hchunk, scale_log2);
+    else
+      decode_mfma_kernel<D, HPW, false>
+          <<<groups, kWave * wpg, lds, st>>>(a, b_shift, n_hchunk, scale_log2);
+  } else {
+    if (a.block_size >= kTile)
+      decode_balanced_kernel<DTYPE, D, HPW, true>
+          <<<groups, kWave * wpg, 0, st>>>(a, b_shift, n_hchunk, scale_log2);
+    else
+      decode_balanced_kernel<DTYPE, D, HPW, false>
+          <<<groups, kWave * wpg, 0, st>>>(a, b_shift, n_hchunk, scale_log2);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_combine_kernel<DTYPE, D, HPW><<<groups, kWave * wpg, 0, st>>>(a);

@@ -163,7 +163,12 @@ def _single_seq(L, Hq, Hkv, D, B, dtype, seed, zero_keys=False):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("L", [1, 2, 15, 16, 17, 511, 512, 513, 1000, 4097])
-@pytest.mark.parametrize("D,B,Hq,Hkv", [(128, 16, 8, 1), (64, 4, 4, 4), (128, 32, 6, 2), (64, 8, 8, 8)])
+@pytest.mark.parametrize("D,B,Hq,Hkv", [
+    (128, 16, 8, 1), (64, 4, 4, 4), (128, 32, 6, 2), (64, 8, 8, 8),
+    # groups of >= 4 query heads per KV head (bf16 runs these on the matrix
+    # cores): head_dim 64, blocks smaller than a 16-token tile, two head
+    # chunks per KV head
+    (64, 8, 16, 4), (128, 4, 16, 2), (64, 16, 32, 2)])
 def test_edge_lengths(dtype, L, D, B, Hq, Hkv):
     from oracle.attention import decode_attention
     q, k, v, got = _single_seq(L, Hq, Hkv, D, B, dtype, seed=L * 7 + D)
