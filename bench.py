@@ -51,25 +51,32 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = {
+    "decode": ("decode.hip", "cache_ops.hip", "device.h"),
+    "prefill": ("prefill.hip", "device.h"),
+}
+
+
+def kernel_source_hash(kind: str = "decode") -> str:
     h = hashlib.sha256()
-    for f in ("decode.hip", "cache_ops.hip", "device.h"):
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "paged_kv_cache_316_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM traffic per decode call from committed rocprofv3 PMC runs, if they were
-    taken on the current kernel sources; else None."""
-    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+def load_traffic(workload: str, kind: str = "decode"):
+    """HBM bytes per call from committed rocprofv3 PMC runs, if they were taken on
+    the current kernel sources; else None."""
+    name = f"traffic_{workload}.json" if kind == "decode" else f"traffic_{kind}_{workload}.json"
+    path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
-    return t.get("bytes_per_decode_call")
+    return t.get("bytes_per_call", t.get("bytes_per_decode_call"))
 
 
 def cpu_baseline(wl, budget_s: float):
@@ -269,7 +276,8 @@ def prefill_row(ld, steps, warmup):
             "flops_per_call": flops, "prefill_tokens_per_s": round(rows / (ms_step * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": load_traffic(ld.name, "prefill"),
                          "kernel": "pa_prefill_chunk (bf16 MFMA 32x32x16)"}}
 
 
@@ -337,6 +345,7 @@ def main():
         "cache_write_us": row["cache_write_us"],
         "roofline": row["roofline"],
         "kernel_source_hash": kernel_source_hash(),
+        "prefill_source_hash": kernel_source_hash("prefill"),
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
