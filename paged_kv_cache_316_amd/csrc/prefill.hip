@@ -188,8 +188,8 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
   }
 
   // Tile loads: load i of this wave fills LDS rows (wave*NI + i)*RPI + lane/CPR
-  // of the K and the V tile, lane l the chunk slot l % CPR. A wave's loads
-  // cover the 16 consecutive keys kt*64 + 16*wave .. +15.
+  // of a K or V tile, lane l the chunk slot l % CPR. A wave's loads cover the
+  // 16 consecutive keys t*64 + 16*wave .. +15 of tile t.
   const int32_t* bt = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
   const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool);
   const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool);
@@ -206,51 +206,51 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
   }
   // WAVE_BLOCK: the wave's block is found with one scalar load; clamped keys
   // (past the end) stay in it, since it is looked up for min(first key, L-1).
+  // Otherwise each lane looks up the block of each of its keys.
   const_i32* btc = (const_i32*)bt;
   const int64_t head_bytes = int64_t(kvh) * B * PS::ROW;
   const int64_t block_bytes = int64_t(Hkv) * B * PS::ROW;
-  auto load_table = [&](int kt, int32_t (&tab)[NI], int32_t& sblk) {
+  auto load_table = [&](int t, int32_t (&tab)[NI]) {
     if constexpr (WAVE_BLOCK) {
-      sblk = btc[min(kt * kKeys + 16 * wave, L - 1) >> b_shift];
+      tab[0] = btc[min(t * kKeys + 16 * wave, L - 1) >> b_shift];
     } else {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) tab[i] = bt[min(kt * kKeys + ld_row[i], L - 1) >> b_shift];
+      for (int i = 0; i < NI; ++i) tab[i] = bt[min(t * kKeys + ld_row[i], L - 1) >> b_shift];
     }
   };
-  auto issue_tile = [&](int kt, const int32_t (&tab)[NI], int32_t sblk) {
-    const uint32_t st = lds0 + uint32_t((kt % 2) * PS::STAGE) + uint32_t(wave * NI * 1024);
-    const int key0 = kt * kKeys + 16 * wave;
+  // tile t of one tensor (pool) into the LDS tile at byte offset tile_off
+  auto issue_tile = [&](const unsigned char* pool, int t, const int32_t (&tab)[NI],
+                        uint32_t tile_off) {
+    const uint32_t st = lds0 + tile_off + uint32_t(wave * NI * 1024);
+    const int key0 = t * kKeys + 16 * wave;
     if constexpr (WAVE_BLOCK) {
-      const int64_t base = int64_t(sblk) * block_bytes + head_bytes;
+      const int64_t base = int64_t(tab[0]) * block_bytes + head_bytes;
       if (key0 + 16 <= L) {  // no clamping: every offset is a per-lane constant
         const int64_t wb = base + int64_t(key0 & Bm1) * PS::ROW;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          load_lds16(kpool + wb, ld_off[i], st + uint32_t(i * 1024));
-          load_lds16(vpool + wb, ld_off[i], st + uint32_t(i * 1024 + PS::TILE));
-        }
+        for (int i = 0; i < NI; ++i) load_lds16(pool + wb, ld_off[i], st + uint32_t(i * 1024));
       } else {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          const int t = min(kt * kKeys + ld_row[i], L - 1);  // past the end: a valid, masked key
-          const uint32_t off = uint32_t((t & Bm1) * PS::ROW + ld_chunk[i] * 16);
-          load_lds16(kpool + base, off, st + uint32_t(i * 1024));
-          load_lds16(vpool + base, off, st + uint32_t(i * 1024 + PS::TILE));
+          const int tk = min(t * kKeys + ld_row[i], L - 1);  // past the end: a valid, masked key
+          const uint32_t off = uint32_t((tk & Bm1) * PS::ROW + ld_chunk[i] * 16);
+          load_lds16(pool + base, off, st + uint32_t(i * 1024));
         }
       }
     } else {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int t = min(kt * kKeys + ld_row[i], L - 1);  // past the end: a valid, masked key
-      const int64_t off = int64_t(tab[i]) * block_bytes + head_bytes +
-                          int64_t((t & Bm1) * PS::ROW + ld_chunk[i] * 16);
-      load_lds16(kpool + off, st + uint32_t(i * 1024));
-      load_lds16(vpool + off, st + uint32_t(i * 1024 + PS::TILE));
-    }
+      for (int i = 0; i < NI; ++i) {
+        const int tk = min(t * kKeys + ld_row[i], L - 1);  // past the end: a valid, masked key
+        const int64_t off = int64_t(tab[i]) * block_bytes + head_bytes +
+                            int64_t((tk & Bm1) * PS::ROW + ld_chunk[i] * 16);
+        load_lds16(pool + off, st + uint32_t(i * 1024));
+      }
     }
   };
 
-  // Operand-read byte addresses inside a stage.
+  // LDS: K tiles in stages 0, 1 (bytes 0, TILE), V tiles in stages 0, 1 (bytes
+  // 2 TILE, 3 TILE); tile t of either tensor uses stage t % 2.
+  // Operand-read byte addresses inside a tile.
   // K: row mt*32 + lane%32, chunk 2ks + g  ->  (k_addr ^ 32 ks) + mt * 32 rows.
   const int kr = lane % 32;
   const uint32_t k_addr = uint32_t(kr * PS::ROW + ((g ^ swz<PS::CPR>(kr)) * 16));
@@ -259,10 +259,9 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
   // half lane%2  ->  (v_lo ^ 64 dt) + 16 kk rows.
   const int vr = 4 * g + (lane % 16) / 4;
   const int cl = 2 * ((lane / 16) % 2) + (lane % 4) / 2;
-  const uint32_t v_lo =
-      uint32_t(PS::TILE + vr * PS::ROW + ((cl ^ swz<PS::CPR>(vr)) * 16) + 8 * (lane % 2));
+  const uint32_t v_lo = uint32_t(vr * PS::ROW + ((cl ^ swz<PS::CPR>(vr)) * 16) + 8 * (lane % 2));
   const uint32_t v_hi =
-      uint32_t(PS::TILE + (vr + 8) * PS::ROW + ((cl ^ swz<PS::CPR>(vr + 8)) * 16) + 8 * (lane % 2));
+      uint32_t((vr + 8) * PS::ROW + ((cl ^ swz<PS::CPR>(vr + 8)) * 16) + 8 * (lane % 2));
 
   f32x16_t o[PS::DTILES];
 #pragma unroll
@@ -271,29 +270,9 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
   float m = -INFINITY, lsum = 0.f;  // running max in raw score units
 
-  int32_t tab[NI], sblk = 0;
-  load_table(0, tab, sblk);
-  issue_tile(0, tab, sblk);
-  if (n_ktiles > 1) load_table(1, tab, sblk);
-  for (int kt = 0; kt < n_ktiles; ++kt) {
-    // tile kt is in LDS for every wave, and every wave is done with tile
-    // kt-1, whose stage the loads of tile kt+1 now overwrite
-    drain_and_barrier();
-    if (kt + 1 < n_ktiles) issue_tile(kt + 1, tab, sblk);
-    if (kt + 2 < n_ktiles) load_table(kt + 2, tab, sblk);
-    const int t0 = kt * kKeys;
-    if (!wave_active || t0 > wave_last_key) continue;  // uniform per wave
-    const unsigned char* stage = smem + (kt % 2) * PS::STAGE;
-
-    // S^T = K Q^T for keys t0 .. t0+63 (two 32-key m-tiles)
-    uint4 kop[2][PS::KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < PS::KSTEPS; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        kop[mt][ks] = *reinterpret_cast<const uint4*>(
-            stage + ((k_addr ^ (32u * ks)) + mt * 32 * PS::ROW));
-    f32x16_t sacc[2];
+  // S^T = K Q^T for the 64 keys of the K tile at tile_off (two 32-key m-tiles)
+  auto qk = [&](uint32_t tile_off, f32x16_t (&sacc)[2]) {
+    const unsigned char* kt_lds = smem + tile_off;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -301,7 +280,35 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
 #pragma unroll
     for (int ks = 0; ks < PS::KSTEPS; ++ks)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma32(kop[mt][ks], qop[ks], sacc[mt]);
+      for (int mt = 0; mt < 2; ++mt) {
+        const uint4 kop = *reinterpret_cast<const uint4*>(
+            kt_lds + ((k_addr ^ (32u * ks)) + mt * 32 * PS::ROW));
+        sacc[mt] = mfma32(kop, qop[ks], sacc[mt]);
+      }
+  };
+
+  // One tile of the loop, software-pipelined: the scores of tile kt are in
+  // cur.s (computed one step earlier); this step computes the scores of tile
+  // kt+1 into nxt.s on the matrix cores while the VALU runs the softmax of
+  // tile kt, then multiplies tile kt's weights with its V tile. Loads run two
+  // tiles ahead for K and one for V; block-table entries one step before
+  // their loads. The state of consecutive steps alternates between two sets
+  // of registers (the loop is unrolled by two), so no value is copied.
+  struct Step {
+    f32x16_t s[2];    // scores of the tile this step works on
+    int32_t tk[NI];   // block-table entries for the K tile this step loads
+    int32_t tv[NI];   // ... and for the V tile
+  };
+  auto step = [&](int kt, int par, Step& cur, Step& nxt) {
+    // K(kt+1) and V(kt) are in LDS for every wave, and every wave is done
+    // with K(kt) and V(kt-1), whose stages the loads below overwrite
+    drain_and_barrier();
+    if (kt + 2 < n_ktiles) issue_tile(kpool, kt + 2, cur.tk, uint32_t(par * PS::TILE));
+    if (kt + 1 < n_ktiles) issue_tile(vpool, kt + 1, cur.tv, uint32_t((3 - par) * PS::TILE));
+    if (kt + 3 < n_ktiles) load_table(kt + 3, nxt.tk);
+    if (kt + 2 < n_ktiles) load_table(kt + 2, nxt.tv);
+    const int t0 = kt * kKeys;
+    if (!wave_active || t0 > wave_last_key) return;  // uniform per wave
 
     // causal mask only where the tile reaches the diagonal (or rows past the chunk)
     if (wave_ragged || t0 + kKeys - 1 > start + row0) {
@@ -310,73 +317,117 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = t0 + mt * 32 + 8 * (i / 4) + 4 * g + (i % 4);
-          if (key > my_pos) sacc[mt][i] = -INFINITY;
+          if (key > my_pos) cur.s[mt][i] = -INFINITY;
         }
     }
+    // scores of tile kt+1 (unused when this wave stops at kt; the K stage then
+    // holds an older tile, which is harmless)
+    qk(uint32_t((1 - par) * PS::TILE), nxt.s);
+
+    // Weights of tile kt against the current exponent base m, while those
+    // MFMAs run. The base only moves when a row's max exceeds it by more than
+    // 2^8 (or on a row's first scores): until then weights up to 256 are
+    // taken as they are. Numerator and denominator share the base, so this
+    // is exact, and the rare move redoes the weights below.
+    uint4 pop[4];  // P^T operands for the four 16-key k-steps
+    float ps;
+    auto weights = [&](float nms) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float p[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            p[j] = __builtin_amdgcn_exp2f(fmaf(cur.s[mt][8 * h + j], scale_log2, nms));
+          pop[2 * mt + h] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
+                                       pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
+        }
+      // the row sum adds up the same bf16 weights that the PV product uses
+      const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].x), ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].y), ones, ps1, false);
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].z), ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].w), ones, ps1, false);
+      }
+      ps = ps0 + ps1;
+    };
+    weights(m == -INFINITY ? 0.f : -m * scale_log2);
+    // keep this work before the branch below (next to the MFMAs above) rather
+    // than let it sink into the common path after it
+    asm volatile("" ::"v"(pop[0].x), "v"(pop[0].y), "v"(pop[0].z), "v"(pop[0].w),
+                 "v"(pop[1].x), "v"(pop[1].y), "v"(pop[1].z), "v"(pop[1].w),
+                 "v"(pop[2].x), "v"(pop[2].y), "v"(pop[2].z), "v"(pop[2].w),
+                 "v"(pop[3].x), "v"(pop[3].y), "v"(pop[3].z), "v"(pop[3].w), "v"(ps));
+
     float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // The exponent base m only moves when a row's max exceeds it by more than
-    // 2^8 (or on the first scores): until then weights up to 256 are taken
-    // as they are. Numerator and denominator share the base, so this is
-    // exact, and it spares the output rescale on almost every tile.
-    const bool moved = m == -INFINITY ? mx != -INFINITY : (mx - m) * scale_log2 > 8.f;
-    const float mn = moved ? mx : m;
-    const float ms = mn == -INFINITY ? 0.f : mn;
-    const float nms = -ms * scale_log2;
-    const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m, scale_log2, nms)) : 1.f;
-    m = mn;
-    uint4 pop[4];  // P^T operands for the four 16-key k-steps
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          p[j] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][8 * h + j], scale_log2, nms));
-        pop[2 * mt + h] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
-                                     pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
-      }
-    // the row sum adds up the same bf16 weights that the PV product uses
-    const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].x), ones, ps0, false);
-      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].y), ones, ps1, false);
-      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].z), ones, ps0, false);
-      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pop[k].w), ones, ps1, false);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, cur.s[mt][i]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max over lanes l, l^32
     }
-    lsum = lsum * alpha + (ps0 + ps1);
-    if (__ballot(moved)) {  // exact: alpha == 1 where no row max moved
+    const bool moved = m == -INFINITY ? mx != -INFINITY : (mx - m) * scale_log2 > 8.f;
+    if (__ballot(moved)) {  // rare: new base for the rows that moved, weights again
+      const float mn = moved ? mx : m;
+      const float nms = mn == -INFINITY ? 0.f : -mn * scale_log2;
+      const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m, scale_log2, nms)) : 1.f;
+      m = mn;
+      weights(nms);
+      lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < PS::DTILES; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
     }
+    lsum += ps;
     // O^T += V^T P^T; operand j of half g in k-step kk = (mt, h) is key
     // 16 kk + 8 (j / 4) + 4 g + j % 4, matching the S^T accumulator order
+    const unsigned char* vt_lds = smem + (2 + par) * PS::TILE;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int dt = 0; dt < PS::DTILES; ++dt) {
         const uint32_t rows = uint32_t(kk * 16 * PS::ROW);
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)(stage + ((v_lo ^ (64u * dt)) + rows)));
+            (lds_v4i16_t*)(vt_lds + ((v_lo ^ (64u * dt)) + rows)));
         const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)(stage + ((v_hi ^ (64u * dt)) + rows)));
+            (lds_v4i16_t*)(vt_lds + ((v_hi ^ (64u * dt)) + rows)));
         const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
         o[dt] = mfma32(make_uint4(l2.x, l2.y, h2.x, h2.y), pop[kk], o[dt]);
       }
     }
+  };
+
+  // prologue: K(0), V(0), K(1) in flight, then the scores of tile 0
+  Step st_a, st_b;
+  {
+    int32_t t0[NI], t1[NI];
+    load_table(0, t0);
+    if (n_ktiles > 1) load_table(1, t1);
+    issue_tile(kpool, 0, t0, 0u);
+    issue_tile(vpool, 0, t0, uint32_t(2 * PS::TILE));
+    if (n_ktiles > 1) issue_tile(kpool, 1, t1, uint32_t(PS::TILE));
+  }
+  if (n_ktiles > 2) load_table(2, st_a.tk);
+  if (n_ktiles > 1) load_table(1, st_a.tv);
+  drain_and_barrier();
+  if (wave_active) qk(0u, st_a.s);
+  for (int kt = 0; kt < n_ktiles; kt += 2) {
+    step(kt, 0, st_a, st_b);
+    if (kt + 1 < n_ktiles) step(kt + 1, 1, st_b, st_a);
   }
 
   if (!wave_active || my_pos < 0) return;
-  const float l_row = lsum + __shfl_xor(lsum, 32);
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
+                                                    false, false);
+  const float l_row = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);  // lanes l and l^32
   const float inv = 1.f / l_row;
   uint2* orow = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) +
                                          (int64_t(q0 + my_row) * Hq + head) * D);
