@@ -31,6 +31,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
+MODEL_LAYERS = {"llama13b": 40, "llama70b": 80, "prefix": 40, "cow": 40, "cow504": 40, "beam": 40,
+                "tiny": 1}
 
 WORKLOAD_TEXT = {
     "llama13b": "LLaMA-13B-shaped decode layer: 64 seqs, 40 MHA heads x 128, bf16 KV, "
@@ -248,6 +250,32 @@ def prefill_step_fn(ld):
     return step
 
 
+def stream_read_ceiling(gib: int = 4):
+    """Best streaming-read rate (GB/s) of pa_probe_stream_read over a few grid sizes."""
+    import torch
+    import paged_kv_cache_316_amd as pkv
+    buf = torch.ones(gib << 28, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    best, best_grid = 0.0, 0
+    stream = torch.cuda.current_stream()
+    for grid in (4 * cus, 8 * cus, 16 * cus, 32 * cus):
+        pkv.probe_stream_read(buf, sink, grid)
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pkv.probe_stream_read(buf, sink, grid)
+            e1.record(stream)
+            e1.synchronize()
+            gbps = buf.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if gbps > best:
+                best, best_grid = gbps, grid
+    del buf
+    torch.cuda.empty_cache()
+    return {"gbps": round(best, 1), "grid": best_grid, "bytes": gib << 30,
+            "kernel": "pa_probe_stream_read (16-byte non-temporal loads, 4 in flight per lane)"}
+
+
 def decode_row(ld, steps, warmup, workers):
     ms_step, w_ms, d_ms = time_steps(decode_step_fn(ld, workers), steps, warmup)
     S = len(ld.wl.decode_seqs)
@@ -318,6 +346,7 @@ def main():
         del a, b
 
     row = decode_row(ld, args.steps, args.warmup, args.workers)
+    ceiling = stream_read_ceiling()
     wl = ld.wl
     S = len(wl.decode_seqs)
     result = {
@@ -340,11 +369,16 @@ def main():
                    "accumulation": "fp32", "decode_workers": args.workers or "default (8 per CU)"},
         "pct_hbm_peak": round(100 * row["kv_gbps_step"] / HBM_PEAK_GBPS, 2),
         "tokens_per_s": row["tokens_per_s"],
+        "tokens_per_s_model_equiv": {"layers": MODEL_LAYERS[args.workload],
+                                     "value": round(row["tokens_per_s"] / MODEL_LAYERS[args.workload], 1),
+                                     "note": "attention-only: one layer's step time x layers"},
         "decode_kv_gbps": row["decode_kv_gbps"],
         "decode_us": row["decode_us"],
         "cache_write_us": row["cache_write_us"],
         "roofline": row["roofline"],
         "kernel_source_hash": kernel_source_hash(),
+        "stream_read_ceiling": ceiling,
+        "pct_of_stream_ceiling": round(100 * row["decode_kv_gbps"] / ceiling["gbps"], 2),
         "prefill_source_hash": kernel_source_hash("prefill"),
     }
     if not args.no_cpu_baseline:
@@ -361,6 +395,9 @@ def main():
             ld = Loaded("llama70b", args.replicas)
             rows["decode_llama70b_gqa"] = decode_row(ld, max(20, args.steps // 4), args.warmup,
                                                     args.workers)
+            g = rows["decode_llama70b_gqa"]
+            g["tokens_per_s_model_equiv"] = round(g["tokens_per_s"] / MODEL_LAYERS["llama70b"], 1)
+            g["pct_of_stream_ceiling"] = round(100 * g["decode_kv_gbps"] / ceiling["gbps"], 2)
         rows["prefill_llama70b"] = prefill_row(ld, max(10, args.steps // 10), min(args.warmup, 5))
         rows["workload_llama70b"] = WORKLOAD_TEXT["llama70b"] + "; prefill: 8 x 512-row causal chunks"
         result["rows"] = rows

@@ -103,6 +103,19 @@ pa_status pa_copy_blocks(const pa_pool* pool, const int32_t* src_dst, int32_t nu
                          void* stream);
 
 /*
+ * pa_probe_stream_read — measurement aid, not part of the attention path:
+ * reads `bytes` of device memory once, with 16-byte non-temporal loads from
+ * `grid` workgroups of 256 threads (grid <= 0: 16 per compute unit). Timing
+ * it gives this device's streaming-read rate, the ceiling that the decode
+ * kernels' HBM rate is compared against.
+ *   buf  : device, 16-byte aligned; bytes a multiple of 16 (0: no-op)
+ *   sink : device uint32; written only if the XOR of all loaded words equals
+ *          a fixed constant (it keeps the loads from being optimized away)
+ */
+pa_status pa_probe_stream_read(const void* buf, size_t bytes, int32_t grid, uint32_t* sink,
+                               void* stream);
+
+/*
  * Workspace needed by pa_decode, in bytes, for these sizes and worker count
  * (0 = the library's default: 8 wavefronts per compute unit of the current
  * device). Returns 0 for invalid sizes.

@@ -40,6 +40,7 @@ SIGNATURES = {
     "pa_version": (c_int32, []),
     "pa_cache_write": (c_int32, [_P(PaPool), c_void_p, c_void_p, c_void_p, c_int32, c_void_p]),
     "pa_copy_blocks": (c_int32, [_P(PaPool), c_void_p, c_int32, c_void_p]),
+    "pa_probe_stream_read": (c_int32, [c_void_p, c_size_t, c_int32, c_void_p, c_void_p]),
     "pa_decode_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode": (c_int32, [c_void_p, c_void_p, _P(PaPool), c_void_p, c_int32, c_void_p, c_int32,
                             c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p]),

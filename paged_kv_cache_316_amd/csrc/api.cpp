@@ -149,6 +149,18 @@ pa_status pa_copy_blocks(const pa_pool* pool, const int32_t* src_dst, int32_t nu
   return PA_OK;
 }
 
+pa_status pa_probe_stream_read(const void* buf, size_t bytes, int32_t grid, uint32_t* sink,
+                               void* stream) {
+  pa::clear_error();
+  if (bytes == 0) return PA_OK;
+  if (!buf || !sink) return fail(PA_ERR_INVALID, "pa_probe_stream_read: buf/sink is NULL");
+  if ((reinterpret_cast<uintptr_t>(buf) & 15) || (bytes & 15))
+    return fail(PA_ERR_INVALID, "pa_probe_stream_read: buf and bytes must be 16-byte aligned");
+  const int g = grid > 0 ? grid : pa::device_cus() * 16;
+  return pa::hip_status(pa::launch_stream_read(buf, bytes, g, sink, static_cast<hipStream_t>(stream)),
+                        "pa_probe_stream_read");
+}
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t num_workers) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||

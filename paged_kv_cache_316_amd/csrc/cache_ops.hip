@@ -66,6 +66,32 @@ hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void
   return hipGetLastError();
 }
 
+// Streaming read for measuring the device's read ceiling: grid-stride loop,
+// four independent 16-byte non-temporal loads in flight per thread.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* p, int64_t n, uint32_t* sink) {
+  uint32_t acc = 0;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const uint4 a = load_stream16(p + i), b = load_stream16(p + i + stride);
+    const uint4 c = load_stream16(p + i + 2 * stride), d = load_stream16(p + i + 3 * stride);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
+           d.z ^ d.w;
+  }
+  for (; i < n; i += stride) {
+    const uint4 a = load_stream16(p + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9e3779b9u) *sink = acc;
+}
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, int grid, uint32_t* sink,
+                              hipStream_t stream) {
+  stream_read_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint4*>(buf),
+                                               int64_t(bytes / 16), sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_blocks(const pa_pool& pool, const int32_t* src_dst, int32_t n,
                               hipStream_t stream) {
   const int64_t cpb = int64_t(pool.num_kv_heads) * pool.block_size * pool.head_dim *

@@ -87,6 +87,8 @@ struct DecodeArgs {
 
 hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void* v_new,
                               const int64_t* slots, int32_t T, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, size_t bytes, int grid, uint32_t* sink,
+                              hipStream_t stream);
 hipError_t launch_copy_blocks(const pa_pool& pool, const int32_t* src_dst, int32_t n,
                               hipStream_t stream);
 // Returns hipErrorInvalidValue for shapes without a compiled kernel.

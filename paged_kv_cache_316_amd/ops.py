@@ -82,6 +82,14 @@ def copy_blocks(pool: KVPool, src_dst: torch.Tensor) -> None:
     check(lib().pa_copy_blocks(ctypes.byref(pool.c), _ptr(src_dst), n, _stream()))
 
 
+def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, grid: int = 0) -> None:
+    """Read all of `buf` once (measurement aid: the device's streaming-read rate)."""
+    _need(buf, "buf")
+    _need(sink, "sink", torch.int32)
+    check(lib().pa_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), grid,
+                                     _ptr(sink), _stream()))
+
+
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                            workers: int = 0) -> int:
     return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,

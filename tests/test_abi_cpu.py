@@ -109,3 +109,12 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="no CPU or Python fallback"):
         _lib.lib()
+
+
+def test_stream_probe_rejects_bad_arguments():
+    L = lib()
+    assert L.pa_probe_stream_read(None, 0, 0, None, None) == 0  # no bytes: no-op
+    assert L.pa_probe_stream_read(None, 16, 0, 16, None) == -1  # NULL buffer
+    assert L.pa_probe_stream_read(16, 24, 0, 16, None) == -1  # bytes not a multiple of 16
+    assert L.pa_probe_stream_read(8, 16, 0, 16, None) == -1  # unaligned buffer
+    assert L.pa_last_error()
