@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 MODEL_LAYERS = {"llama13b": 40, "llama70b": 80, "prefix": 40, "cow": 40, "cow504": 40, "beam": 40,
-                "tiny": 1}
+                "tiny": 1, "llama13b_fp8": 40}
 
 WORKLOAD_TEXT = {
     "llama13b": "LLaMA-13B-shaped decode layer: 64 seqs, 40 MHA heads x 128, bf16 KV, "
@@ -46,6 +46,9 @@ WORKLOAD_TEXT = {
     "cow504": "parallel sampling, 504-token prompts (partial block copied on write)",
     "beam": "beam search width 4: 32 groups on 512-token prompts, U[1,256] steps",
     "tiny": "tiny fp32: 2 seqs (7, 11), 4 heads x 64, block 4",
+    "llama13b_fp8": "LLaMA-13B-shaped decode layer with an FP8 (OCP E4M3) KV cache: 64 seqs, "
+                    "40 MHA heads x 128, scale 2^-6 per pool, bf16 q/out, block 16, "
+                    "lengths U[1,2048], random placement",
 }
 
 
@@ -137,7 +140,10 @@ class Loaded:
         alloc = pkv.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
         phases = split_phases(run_script(alloc, wl.ops))
         rows_k, rows_v = dev(wl.rows_k), dev(wl.rows_v)
-        pool0 = pkv.KVPool.empty(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, self.dt)
+        pool_dt = {"f32": torch.float32, "bf16": torch.bfloat16,
+                   "fp8_e4m3": torch.float8_e4m3fn}[wl.pool_dtype]
+        pool0 = pkv.KVPool.empty(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, pool_dt,
+                                 k_scale=wl.k_scale, v_scale=wl.v_scale)
         apply_events(pool0, phases.get("setup", []), rows_k, rows_v)
 
         def batch(events):
@@ -156,7 +162,7 @@ class Loaded:
             apply_events(pool0, copies, rows_k, rows_v)
         self.decode_write.run(pool0)
         del rows_k, rows_v
-        self.pools = [pool0] + [pkv.KVPool(pool0.k.clone(), pool0.v.clone())
+        self.pools = [pool0] + [pkv.KVPool(pool0.k.clone(), pool0.v.clone(), wl.k_scale, wl.v_scale)
                                 for _ in range(replicas - 1)]
         tables, lens = alloc.batch_tables(wl.decode_seqs)
         self.lens = lens
@@ -320,7 +326,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-rows", action="store_true",
-                    help="skip the Llama-2-70B-shaped GQA decode and chunked-prefill rows")
+                    help="skip the Llama-2-70B-shaped GQA decode, chunked-prefill and FP8-KV decode rows")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -400,6 +406,16 @@ def main():
             g["pct_of_stream_ceiling"] = round(100 * g["decode_kv_gbps"] / ceiling["gbps"], 2)
         rows["prefill_llama70b"] = prefill_row(ld, max(10, args.steps // 10), min(args.warmup, 5))
         rows["workload_llama70b"] = WORKLOAD_TEXT["llama70b"] + "; prefill: 8 x 512-row causal chunks"
+        if args.workload != "llama13b_fp8":
+            del ld
+            gc.collect()
+            torch.cuda.empty_cache()
+            ld = Loaded("llama13b_fp8", args.replicas)
+            f = rows["decode_llama13b_fp8"] = decode_row(ld, max(20, args.steps // 4), args.warmup,
+                                                        args.workers)
+            f["tokens_per_s_model_equiv"] = round(f["tokens_per_s"] / MODEL_LAYERS["llama13b_fp8"], 1)
+            f["pct_of_stream_ceiling"] = round(100 * f["decode_kv_gbps"] / ceiling["gbps"], 2)
+            f["workload"] = WORKLOAD_TEXT["llama13b_fp8"]
         result["rows"] = rows
     print(json.dumps(result), flush=True)
 

@@ -51,8 +51,14 @@ typedef enum pa_status {
 } pa_status;
 
 typedef enum pa_dtype {
-  PA_F32 = 0,   /* IEEE float32                         */
-  PA_BF16 = 1   /* bfloat16 (upper 16 bits of float32)  */
+  PA_F32 = 0,      /* IEEE float32                                               */
+  PA_BF16 = 1,     /* bfloat16 (upper 16 bits of float32)                        */
+  PA_FP8_E4M3 = 2  /* KV pools only: 8-bit codes of the OCP E4M3 format (1 sign,
+                      4 exponent bits with bias 7, 3 mantissa bits, largest
+                      finite value 448, no infinities), one scale per pool.
+                      This is the FP8 KV cache of "vLLM PagedAttention
+                      explained", section 7 (the pages fix neither format nor
+                      scale; both are this library's reading).              */
 } pa_dtype;
 
 /* One layer's KV pool: two device arrays of identical shape and dtype. */
@@ -64,6 +70,8 @@ typedef struct pa_pool {
   int32_t block_size;      /* B: power of two, 1..256                                  */
   int32_t head_dim;        /* D: 64 or 128                                             */
   int32_t dtype;           /* pa_dtype                                                 */
+  float k_scale;           /* PA_FP8_E4M3: K code c stands for e4m3(c) * k_scale; finite, > 0 */
+  float v_scale;           /* PA_FP8_E4M3: the same for V. Both ignored for other dtypes.      */
 } pa_pool;
 
 const char* pa_status_string(pa_status s);
@@ -80,12 +88,16 @@ int32_t pa_version(void);
  * each generated token is written into the physical blocks the block table
  * maps; slot rule of "LLM inference engine internals", section 2.3.)
  *   k_new, v_new : device, [num_tokens][num_kv_heads][head_dim], pool dtype
+ *                  (bfloat16 for a PA_FP8_E4M3 pool)
  *   slot_mapping : device, int64 [num_tokens]; token i goes to block
  *                  slot / B, offset slot % B, for every KV head. A negative
  *                  slot means "skip this token" (padding).
- * The result is a byte copy: bit-exact. Slots must be distinct and
- * < num_blocks * B; nothing else in the pool is touched. num_tokens == 0 is a
- * no-op.
+ * For F32 and BF16 pools the result is a byte copy: bit-exact. For an FP8
+ * pool each value x is stored as the E4M3 code nearest to
+ * min(max(x / scale, -448), 448), x / scale an IEEE single-precision
+ * division, ties to the even mantissa (a deterministic function of x and the
+ * pool's k_scale / v_scale). Slots must be distinct and < num_blocks * B;
+ * nothing else in the pool is touched. num_tokens == 0 is a no-op.
  */
 pa_status pa_cache_write(const pa_pool* pool, const void* k_new, const void* v_new,
                          const int64_t* slot_mapping, int32_t num_tokens, void* stream);
@@ -133,7 +145,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * tiles — is split evenly over `num_workers` wavefronts; a sequence split
  * between wavefronts is recombined exactly with the log-sum-exp rule.
  *   out          : device, [num_seqs][num_q_heads][head_dim], dtype of the pool
- *   q            : device, [num_seqs][num_q_heads][head_dim], dtype of the pool
+ *                  (bfloat16 for a PA_FP8_E4M3 pool)
+ *   q            : device, [num_seqs][num_q_heads][head_dim], same dtype as out
  *   block_tables : device, int32 [num_seqs][max_blocks_per_seq]; only the first
  *                  ceil(seq_lens[s] / B) entries of a row are read
  *   seq_lens     : device, int32 [num_seqs], each in [0, max_blocks_per_seq * B];
@@ -147,7 +160,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                  after a call). Calls that share a workspace must not overlap.
  * Two kernels run on the stream: the split decode, then the combine of the
  * partials of sequences that were split between wavefronts.
- * Accumulation is fp32 for both dtypes; bf16 output is rounded to nearest even.
+ * Accumulation is fp32 for every dtype; bf16 output is rounded to nearest
+ * even. An FP8 pool is read as e4m3(code) * scale: the codes widen exactly
+ * to bfloat16 and the two scales are applied to the scores and the output.
  */
 pa_status pa_decode(void* out, const void* q, const pa_pool* pool,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,

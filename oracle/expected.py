@@ -4,7 +4,8 @@
   op script and apply its writes and copies to a host pool mirror that starts
   filled with a NaN bit pattern. Returns the mirror, the allocator and events.
 * ``decode_out(wl, idx)``: fp64 attention of the decode queries over each
-  sequence's logical K/V as the generator drew it (no block table involved).
+  sequence's logical K/V as the generator drew it (no block table involved);
+  for an FP8 pool, the values its codes stand for (``fp8``).
 * ``prefill_out(wl, which)``: fp64 causal attention of the prefill chunk rows.
 """
 
@@ -14,21 +15,41 @@ from typing import Iterable, Optional, Sequence
 
 import numpy as np
 
+from . import fp8
 from .allocator import BlockAllocator, run_ops
 from .attention import decode_attention, prefill_attention
 from .paging import PoolMirror
 
 # quiet NaN patterns: an unwritten slot read by mistake poisons the result
-NAN_BITS = {"f32": 0x7FC00001, "bf16": 0x7FC1}
+NAN_BITS = {"f32": 0x7FC00001, "bf16": 0x7FC1, "fp8_e4m3": 0x7F}
+_MIRROR_DTYPE = {"f32": np.float32, "bf16": np.uint16, "fp8_e4m3": np.uint8}
+
+
+def stored_rows(wl, rows_k, rows_v):
+    """What the pool holds for these K/V rows: the rows themselves, or their
+    FP8 codes under the pool's scales."""
+    if wl.pool_dtype != "fp8_e4m3":
+        return rows_k, rows_v
+    return (fp8.quantize(wl.values(rows_k), wl.k_scale),
+            fp8.quantize(wl.values(rows_v), wl.v_scale))
+
+
+def logical_kv(wl, seq):
+    """float64 K, V a sequence holds, as the pool represents them."""
+    r = wl.hist[seq]
+    if wl.pool_dtype != "fp8_e4m3":
+        k, v = wl.logical_kv(seq)
+        return k.astype(np.float64), v.astype(np.float64)
+    ck, cv = stored_rows(wl, wl.rows_k[r], wl.rows_v[r])
+    return fp8.dequantize(ck, wl.k_scale), fp8.dequantize(cv, wl.v_scale)
 
 
 def pool_after(wl, stop_before: Optional[str] = None):
     """Mirror of the pool after the op script (or up to phase ``stop_before``)."""
     alloc = BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
     events = run_ops(alloc, wl.ops)
-    np_dtype = np.float32 if wl.dtype == "f32" else np.uint16
     mirror = PoolMirror(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim,
-                        np_dtype, NAN_BITS[wl.dtype])
+                        _MIRROR_DTYPE[wl.pool_dtype], NAN_BITS[wl.pool_dtype])
     for ev in events:
         if ev[0] == "phase":
             if ev[1] == stop_before:
@@ -37,7 +58,7 @@ def pool_after(wl, stop_before: Optional[str] = None):
             mirror.copy(ev[1])
         else:
             _, slots, rows = ev
-            mirror.write(slots, wl.rows_k[rows], wl.rows_v[rows])
+            mirror.write(slots, *stored_rows(wl, wl.rows_k[rows], wl.rows_v[rows]))
     return mirror, alloc, events
 
 
@@ -50,9 +71,9 @@ def decode_out(wl, idx: Optional[Iterable[int]] = None) -> np.ndarray:
     idx = list(range(len(wl.decode_seqs))) if idx is None else list(idx)
     ks, vs = [], []
     for i in idx:
-        k, v = wl.logical_kv(wl.decode_seqs[i])
-        ks.append(k.astype(np.float64))
-        vs.append(v.astype(np.float64))
+        k, v = logical_kv(wl, wl.decode_seqs[i])
+        ks.append(k)
+        vs.append(v)
     return decode_attention(_f64(wl, wl.q[idx]), ks, vs, wl.scale)
 
 
@@ -67,7 +88,7 @@ def prefill_out(wl, which: Optional[Sequence[int]] = None,
     outs = []
     for j in which:
         seq = wl.prefill_seqs[j]
-        k, v = wl.logical_kv(seq)
+        k, v = logical_kv(wl, seq)
         start = int(wl.prefill_start[j])
         qj = _f64(wl, wl.prefill_q[j * C:(j + 1) * C])
         for i in rows:

@@ -56,4 +56,4 @@ class PoolMirror:
 
 
 def _uint_of(np_dtype):
-    return {2: np.uint16, 4: np.uint32, 8: np.uint64}[np.dtype(np_dtype).itemsize]
+    return {1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}[np.dtype(np_dtype).itemsize]

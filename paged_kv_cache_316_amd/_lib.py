@@ -10,13 +10,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_OOM = 0, -1, -2, -3
 PA_ERR_STATE, PA_ERR_WORKSPACE, PA_ERR_HIP = -4, -5, -6
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 
 
 class PaPool(ctypes.Structure):
     _fields_ = [("k_pool", c_void_p), ("v_pool", c_void_p), ("num_blocks", c_int32),
                 ("num_kv_heads", c_int32), ("block_size", c_int32), ("head_dim", c_int32),
-                ("dtype", c_int32)]
+                ("dtype", c_int32), ("k_scale", c_float), ("v_scale", c_float)]
 
 
 class PagedKVError(RuntimeError):

@@ -56,7 +56,7 @@ DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
 
 bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
-int32_t elt_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+int32_t elt_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
 
 pa_status check_pool(const pa_pool* p, const char* who) {
   if (!p) return fail(PA_ERR_INVALID, "%s: pool is NULL", who);
@@ -67,8 +67,12 @@ pa_status check_pool(const pa_pool* p, const char* who) {
   if (!pow2(p->block_size) || p->block_size > 256)
     return fail(PA_ERR_INVALID, "%s: block_size=%d must be a power of two in 1..256", who,
                 p->block_size);
-  if (p->dtype != PA_F32 && p->dtype != PA_BF16)
+  if (p->dtype != PA_F32 && p->dtype != PA_BF16 && p->dtype != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, p->dtype);
+  if (p->dtype == PA_FP8_E4M3 &&
+      !(p->k_scale > 0.f && p->k_scale <= 3.4e38f && p->v_scale > 0.f && p->v_scale <= 3.4e38f))
+    return fail(PA_ERR_INVALID, "%s: FP8 pool needs finite scales > 0 (k_scale=%g v_scale=%g)",
+                who, double(p->k_scale), double(p->v_scale));
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim=%d not supported (64, 128)", who, p->head_dim);
   return PA_OK;
@@ -222,6 +226,9 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t
   a.workers = lay.workers;
   a.num_cus = pa::device_cus();
   a.scale = scale;
+  const bool fp8 = pool->dtype == PA_FP8_E4M3;
+  a.k_scale = fp8 ? pool->k_scale : 1.f;
+  a.v_scale = fp8 ? pool->v_scale : 1.f;
   return pa::hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)), "pa_decode");
 }
 

@@ -1,5 +1,6 @@
-// Cache write (slot scatter) and whole-block copy. Both are byte copies in
-// 16-byte units, so they are bit-exact for every dtype.
+// Cache write (slot scatter) and whole-block copy. For F32 and BF16 pools both
+// are byte copies in 16-byte units, so they are bit-exact; an FP8 pool's cache
+// write quantizes bf16 rows to E4M3 codes (see cache_write_fp8_kernel).
 //
 // Slot rule ("LLM inference engine internals", section 2.3): slot =
 // block * B + offset. Pool layout [num_blocks][Hkv][B][D]: the row of token
@@ -31,6 +32,47 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   }
 }
 
+// Four values -> four E4M3 codes (first value in the low byte): x / scale (an
+// IEEE division), clamped to the largest finite code, rounded to nearest even
+// by v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float s) {
+  auto q = [s](float x) { return fminf(fmaxf(x / s, -448.f), 448.f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q(a), q(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q(c), q(d), w, true);
+  return uint32_t(w);
+}
+
+// 16 bf16 values (two 16-byte chunks) -> 16 codes.
+__device__ __forceinline__ uint4 e4m3x16(const uint4& lo, const uint4& hi, float s) {
+  return make_uint4(e4m3x4(bf16_lo(lo.x), bf16_hi(lo.x), bf16_lo(lo.y), bf16_hi(lo.y), s),
+                    e4m3x4(bf16_lo(lo.z), bf16_hi(lo.z), bf16_lo(lo.w), bf16_hi(lo.w), s),
+                    e4m3x4(bf16_lo(hi.x), bf16_hi(hi.x), bf16_lo(hi.y), bf16_hi(hi.y), s),
+                    e4m3x4(bf16_lo(hi.z), bf16_hi(hi.z), bf16_lo(hi.w), bf16_hi(hi.w), s));
+}
+
+// FP8 pools: one thread per 16 codes of one (token, head) row, i.e. 32 bytes of
+// bf16 input (input chunks 2i and 2i+1 of the flat [T][Hkv][D] rows); K and V.
+__global__ __launch_bounds__(256) void cache_write_fp8_kernel(
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+    const int64_t* __restrict__ slots, uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+    int64_t total_chunks, int32_t chunks_per_token, int32_t chunks_per_row, int32_t heads,
+    int32_t block_size, float k_scale, float v_scale) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total_chunks; i += stride) {
+    const int64_t t = i / chunks_per_token;
+    const int32_t rem = int32_t(i - t * chunks_per_token);
+    const int32_t h = rem / chunks_per_row;
+    const int32_t c = rem - h * chunks_per_row;
+    const int64_t slot = slots[t];
+    if (slot < 0) continue;  // padding token
+    const int64_t b = slot / block_size;
+    const int64_t o = slot - b * block_size;
+    const int64_t dst = ((b * heads + h) * block_size + o) * chunks_per_row + c;
+    k_pool[dst] = e4m3x16(k_new[2 * i], k_new[2 * i + 1], k_scale);
+    v_pool[dst] = e4m3x16(v_new[2 * i], v_new[2 * i + 1], v_scale);
+  }
+}
+
 // grid.y = pair index; each thread copies 16-byte chunks of one block, K and V.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
     const int32_t* __restrict__ src_dst, uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
@@ -48,7 +90,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
   }
 }
 
-int elt_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+int elt_bytes(int dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
 
 }  // namespace
 
@@ -59,6 +101,13 @@ hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void
   const int64_t total = int64_t(T) * cpt;
   const int64_t want = (total + 255) / 256;
   const int grid = int(want < 8192 ? want : 8192);
+  if (pool.dtype == PA_FP8_E4M3) {
+    cache_write_fp8_kernel<<<grid, 256, 0, stream>>>(
+        static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), slots,
+        static_cast<uint4*>(pool.k_pool), static_cast<uint4*>(pool.v_pool), total, cpt, cpr,
+        pool.num_kv_heads, pool.block_size, pool.k_scale, pool.v_scale);
+    return hipGetLastError();
+  }
   cache_write_kernel<<<grid, 256, 0, stream>>>(
       static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), slots,
       static_cast<uint4*>(pool.k_pool), static_cast<uint4*>(pool.v_pool), total, cpt, cpr,

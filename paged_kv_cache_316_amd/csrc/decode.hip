@@ -476,17 +476,35 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-template <int D, int HPW, bool BIG_B>
+// 16 E4M3 codes -> 16 bf16 values (exact) in two 16-byte chunks.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.f, HI));
+}
+__device__ __forceinline__ void widen_e4m3(const uint4& c, uint4& lo, uint4& hi) {
+  lo = make_uint4(e4m3_pair<false>(c.x), e4m3_pair<true>(c.x), e4m3_pair<false>(c.y),
+                  e4m3_pair<true>(c.y));
+  hi = make_uint4(e4m3_pair<false>(c.z), e4m3_pair<true>(c.z), e4m3_pair<false>(c.w),
+                  e4m3_pair<true>(c.w));
+}
+
+// KV = PA_BF16, or PA_FP8_E4M3: the pool holds E4M3 codes, which are widened
+// exactly to bf16 on their way into LDS; k_scale then multiplies the scores and
+// v_scale the output, and everything from LDS on is the bf16 kernel.
+template <int D, int HPW, bool BIG_B, int KV>
 __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
-  constexpr int ROW = 2 * D;        // bytes per K/V row
+  constexpr bool FP8 = KV == PA_FP8_E4M3;
+  constexpr int ROW = 2 * D;        // bytes per bf16 K/V row in LDS
+  constexpr int GROW = FP8 ? D : ROW;  // bytes per row in the pool
   constexpr int KS = D / 32;        // 16x16x32 k-steps over head_dim
   constexpr int DT = D / 16;        // 16-dim tiles of O^T
-  constexpr int CPR = ROW / 16;     // 16-byte chunks per row
-  constexpr int RPI = 1024 / ROW;   // rows per wave-wide 16-byte load
+  constexpr int CPR = ROW / 16;     // 16-byte chunks per LDS row
+  constexpr int GCPR = GROW / 16;   // 16-byte chunks per pool row
+  constexpr int RPI = 1024 / GROW;  // rows per wave-wide 16-byte load
   constexpr int NI = kTile / RPI;   // loads per lane per tile, for K and for V
   constexpr int RPL = 256 / ROW;    // rows per 256-byte LDS bank line
-  constexpr int TB = kTile * ROW;   // bytes of one K or V tile
+  constexpr int TB = kTile * ROW;   // bytes of one K or V tile in LDS
   static_assert(HPW <= 16, "one MFMA N tile holds the unit's heads");
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -502,13 +520,16 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   unsigned char* kt_lds = smem + wig * (2 * TB);  // this wave's K tile, then its V tile
   unsigned char* vt = kt_lds + TB;
   auto swz = [](int r) { return (r / RPL) % CPR; };
-  // load u of lane l: row u*RPI + l/CPR, chunk l%CPR (written to LDS the same way)
-  const int lrow = lane / CPR, lch = lane % CPR;
-  uint32_t wr[NI];
+  // load u of lane l: row u*RPI + l/GCPR, pool chunk l%GCPR; in LDS that is
+  // chunk l%GCPR of the bf16 row (two chunks, 2c and 2c+1, for FP8 codes)
+  const int lrow = lane / GCPR, lch = lane % GCPR;
+  uint32_t wr[NI], wr2[NI];
 #pragma unroll
   for (int u = 0; u < NI; ++u) {
     const int r = u * RPI + lrow;
-    wr[u] = uint32_t(r * ROW + ((lch ^ swz(r)) * 16));
+    const int c0 = FP8 ? 2 * lch : lch;
+    wr[u] = uint32_t(r * ROW + ((c0 ^ swz(r)) * 16));
+    wr2[u] = uint32_t(r * ROW + (((c0 + 1) ^ swz(r)) * 16));
   }
   // K operand of k-step ks: row i16, chunk 4ks + g  ->  kr0 ^ (64 ks)
   const uint32_t kr0 = uint32_t(i16 * ROW + ((g ^ swz(i16)) * 16));
@@ -518,12 +539,13 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
 
   const unsigned char* kp = static_cast<const unsigned char*>(a.k_pool);
   const unsigned char* vp = static_cast<const unsigned char*>(a.v_pool);
-  const int64_t block_bytes = int64_t(Hkv) * B * ROW;
+  const int64_t block_bytes = int64_t(Hkv) * B * GROW;
 
   uint4 qop[KS];
   f32x4_t o[DT];
   float m, lpart;
-  const float c2 = scale_log2;
+  const float c2 = FP8 ? scale_log2 * a.k_scale : scale_log2;
+  const float vsc = FP8 ? a.v_scale : 1.f;
   auto head_of = [&](const Cursor& x) { return x.kvh * G + x.hc * HPW; };
   auto begin_segment = [&](const Cursor& x) {
     // columns past the unit's heads multiply zeros (their load is clamped to a real head)
@@ -545,8 +567,18 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     // wave, and LDS serves one wave's accesses in order)
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-      *reinterpret_cast<uint4*>(kt_lds + wr[u]) = kr[u];
-      *reinterpret_cast<uint4*>(vt + wr[u]) = vr[u];
+      if constexpr (FP8) {
+        uint4 k0, k1, v0, v1;
+        widen_e4m3(kr[u], k0, k1);
+        widen_e4m3(vr[u], v0, v1);
+        *reinterpret_cast<uint4*>(kt_lds + wr[u]) = k0;
+        *reinterpret_cast<uint4*>(kt_lds + wr2[u]) = k1;
+        *reinterpret_cast<uint4*>(vt + wr[u]) = v0;
+        *reinterpret_cast<uint4*>(vt + wr2[u]) = v1;
+      } else {
+        *reinterpret_cast<uint4*>(kt_lds + wr[u]) = kr[u];
+        *reinterpret_cast<uint4*>(vt + wr[u]) = vr[u];
+      }
     }
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -593,7 +625,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     l += __shfl_xor(l, 32);
     if (i16 >= HPW) return;
     if (owns_start && owns_end) {
-      const float inv = 1.f / l;
+      const float inv = vsc / l;
       uint2* orow = reinterpret_cast<uint2*>(static_cast<unsigned char*>(a.out) +
                                              (int64_t(x.s) * Hq + head_of(x) + i16) * ROW);
 #pragma unroll
@@ -606,7 +638,8 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     float4* dst = reinterpret_cast<float4*>(a.ws_acc + (int64_t(slot) * HPW + i16) * D);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      dst[(16 * dt + 4 * g) / 4] = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+      dst[(16 * dt + 4 * g) / 4] =
+          make_float4(o[dt][0] * vsc, o[dt][1] * vsc, o[dt][2] * vsc, o[dt][3] * vsc);
     if (g == 0) a.ws_ml[int64_t(slot) * HPW + i16] = make_float2(m * c2, l);
   };
 
@@ -618,7 +651,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     const int32_t* row = a.block_tables + int64_t(x.s) * a.max_blocks_per_seq;
     const int nblk = (x.L + Bm1) >> b_shift;
     const int Lm1 = x.L - 1;
-    const int64_t head_off = int64_t(x.kvh) * B * ROW + lch * 16;
+    const int64_t head_off = int64_t(x.kvh) * B * GROW + lch * 16;
     for (int jc = j0; jc < j1;) {
       const int jb0 = (jc * kTile) >> b_shift;
       const int win = jb0 + lane < nblk ? row[jb0 + lane] : 0;
@@ -630,7 +663,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
         for (int u = 0; u < NI; ++u) {
           const int t = min(j * kTile + u * RPI + lrow, Lm1);
           if constexpr (!BIG_B) pb = __shfl(win, (t >> b_shift) - jb0);
-          const int64_t off = int64_t(pb) * block_bytes + head_off + int64_t(t & Bm1) * ROW;
+          const int64_t off = int64_t(pb) * block_bytes + head_off + int64_t(t & Bm1) * GROW;
           kr[u] = load_stream16(reinterpret_cast<const uint4*>(kp + off));
           vr[u] = load_stream16(reinterpret_cast<const uint4*>(vp + off));
         }
@@ -714,13 +747,14 @@ hipError_t run(const DecodeArgs& a, hipStream_t st) {
   wpg = wpg < 1 ? 1 : (wpg > kMaxWavesPerGroup ? kMaxWavesPerGroup : wpg);
   const int groups = (a.workers + wpg - 1) / wpg;
   const float scale_log2 = a.scale * kLog2e;
-  if constexpr (DTYPE == PA_BF16 && HPW >= 4) {
-    const size_t lds = size_t(wpg) * 2 * kTile * 2 * D;  // a K and a V tile per wave
+  // bf16 groups of >= 4 heads and every FP8 pool run on the matrix cores
+  if constexpr (DTYPE == PA_FP8_E4M3 || (DTYPE == PA_BF16 && HPW >= 4)) {
+    const size_t lds = size_t(wpg) * 2 * kTile * 2 * D;  // a K and a V tile per wave (bf16)
     if (a.block_size >= kTile)
-      decode_mfma_kernel<D, HPW, true>
+      decode_mfma_kernel<D, HPW, true, DTYPE>
           <<<groups, kWave * wpg, lds, st>>>(a, b_shift, n_hchunk, scale_log2);
     else
-      decode_mfma_kernel<D, HPW, false>
+      decode_mfma_kernel<D, HPW, false, DTYPE>
           <<<groups, kWave * wpg, lds, st>>>(a, b_shift, n_hchunk, scale_log2);
   } else {
     if (a.block_size >= kTile)
@@ -732,7 +766,8 @@ hipError_t run(const DecodeArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_combine_kernel<DTYPE, D, HPW><<<groups, kWave * wpg, 0, st>>>(a);
+  constexpr int OUT = DTYPE == PA_F32 ? PA_F32 : PA_BF16;  // FP8 pools give bf16 output
+  decode_combine_kernel<OUT, D, HPW><<<groups, kWave * wpg, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -755,8 +790,8 @@ int decode_heads_per_unit(int group) {
 }
 
 bool decode_supported(int dtype, int head_dim, int group) {
-  return (dtype == PA_F32 || dtype == PA_BF16) && (head_dim == 64 || head_dim == 128) &&
-         group >= 1;
+  return (dtype == PA_F32 || dtype == PA_BF16 || dtype == PA_FP8_E4M3) &&
+         (head_dim == 64 || head_dim == 128) && group >= 1;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
@@ -766,6 +801,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   } else if (a.dtype == PA_F32) {
     if (a.head_dim == 128) return run_d<PA_F32, 128>(a, st);
     if (a.head_dim == 64) return run_d<PA_F32, 64>(a, st);
+  } else if (a.dtype == PA_FP8_E4M3) {
+    if (a.head_dim == 128) return run_d<PA_FP8_E4M3, 128>(a, st);
+    if (a.head_dim == 64) return run_d<PA_FP8_E4M3, 64>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -15,6 +15,7 @@ constexpr int kWave = 64;
 template <int DTYPE> struct Elt;
 template <> struct Elt<PA_F32> { static constexpr int bytes = 4; };
 template <> struct Elt<PA_BF16> { static constexpr int bytes = 2; };
+template <> struct Elt<PA_FP8_E4M3> { static constexpr int bytes = 1; };
 
 template <int DTYPE, int D>
 struct RowShape {
@@ -83,6 +84,7 @@ struct DecodeArgs {
   int32_t workers;
   int32_t num_cus;  // compute units of the device (sizes the workgroups)
   float scale;
+  float k_scale, v_scale;  // FP8 pools: a code c stands for e4m3(c) * scale (1 otherwise)
 };
 
 hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void* v_new,

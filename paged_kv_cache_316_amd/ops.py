@@ -11,9 +11,9 @@ from typing import Optional
 
 import torch
 
-from ._lib import PA_BF16, PA_F32, PaPool, PagedKVError, check, lib
+from ._lib import PA_BF16, PA_F32, PA_FP8_E4M3, PaPool, PagedKVError, check, lib
 
-_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_FP8_E4M3}
 
 
 def _stream() -> ctypes.c_void_p:
@@ -34,9 +34,13 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=True) -> None:
 
 
 class KVPool:
-    """One layer's K and V pools: [num_blocks, num_kv_heads, block_size, head_dim]."""
+    """One layer's K and V pools: [num_blocks, num_kv_heads, block_size, head_dim].
 
-    def __init__(self, k: torch.Tensor, v: torch.Tensor):
+    float8_e4m3fn pools hold E4M3 codes; a code c of K stands for e4m3(c) * k_scale
+    (V likewise). New K/V are written, and queries and outputs given, in bfloat16."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, k_scale: float = 1.0,
+                 v_scale: float = 1.0):
         if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
             raise ValueError("k and v pools must be 4-D with equal shape and dtype")
         if k.dtype not in _DTYPES:
@@ -47,13 +51,21 @@ class KVPool:
         nb, h, b, d = k.shape
         self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim = nb, h, b, d
         self.dtype = k.dtype
-        self.c = PaPool(k.data_ptr(), v.data_ptr(), nb, h, b, d, _DTYPES[k.dtype])
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        self.c = PaPool(k.data_ptr(), v.data_ptr(), nb, h, b, d, _DTYPES[k.dtype],
+                        self.k_scale, self.v_scale)
+
+    @property
+    def io_dtype(self) -> torch.dtype:
+        """dtype of new K/V, queries and outputs: the pool's, bf16 for an FP8 pool."""
+        return torch.bfloat16 if self.dtype == torch.float8_e4m3fn else self.dtype
 
     @classmethod
-    def empty(cls, num_blocks, num_kv_heads, block_size, head_dim, dtype, device="cuda"):
+    def empty(cls, num_blocks, num_kv_heads, block_size, head_dim, dtype, device="cuda",
+              k_scale: float = 1.0, v_scale: float = 1.0):
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
         return cls(torch.empty(shape, dtype=dtype, device=device),
-                   torch.empty(shape, dtype=dtype, device=device))
+                   torch.empty(shape, dtype=dtype, device=device), k_scale, v_scale)
 
     @property
     def kv_bytes_per_token(self) -> int:
@@ -66,7 +78,7 @@ def cache_write(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
     T = slot_mapping.numel()
     _need(slot_mapping, "slot_mapping", torch.int64)
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
-        _need(t, n, pool.dtype)
+        _need(t, n, pool.io_dtype)
         if tuple(t.shape) != (T, pool.num_kv_heads, pool.head_dim):
             raise ValueError(f"{n} must be [{T}, {pool.num_kv_heads}, {pool.head_dim}]")
     check(lib().pa_cache_write(ctypes.byref(pool.c), k_new.data_ptr(), v_new.data_ptr(),
@@ -102,7 +114,7 @@ class DecodePlan:
     def __init__(self, pool: KVPool, num_seqs: int, num_q_heads: int, workers: int = 0):
         self.pool = pool
         self.num_seqs, self.num_q_heads, self.workers = num_seqs, num_q_heads, workers
-        self.out = torch.empty((num_seqs, num_q_heads, pool.head_dim), dtype=pool.dtype,
+        self.out = torch.empty((num_seqs, num_q_heads, pool.head_dim), dtype=pool.io_dtype,
                                device=pool.k.device)
         nbytes = decode_workspace_bytes(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim,
                                         workers)
@@ -113,7 +125,7 @@ def decode(q: torch.Tensor, pool: KVPool, block_tables: torch.Tensor, seq_lens: 
            scale: float, workers: int = 0, plan: Optional[DecodePlan] = None,
            out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Paged decode attention. q [S, Hq, D]; block_tables int32 [S, maxB]; seq_lens int32 [S]."""
-    _need(q, "q", pool.dtype)
+    _need(q, "q", pool.io_dtype)
     _need(block_tables, "block_tables", torch.int32)
     _need(seq_lens, "seq_lens", torch.int32)
     S, Hq, D = q.shape
@@ -126,7 +138,7 @@ def decode(q: torch.Tensor, pool: KVPool, block_tables: torch.Tensor, seq_lens: 
         raise ValueError("plan does not match this call")
     if out is None:
         out = plan.out
-    _need(out, "out", pool.dtype)
+    _need(out, "out", pool.io_dtype)
     ws = plan.workspace
     check(lib().pa_decode(out.data_ptr(), q.data_ptr(), ctypes.byref(pool.c),
                           block_tables.data_ptr(), block_tables.shape[1], seq_lens.data_ptr(), S,

@@ -10,8 +10,9 @@ import torch
 import paged_kv_cache_316_amd as pkv
 from paged_kv_cache_316_amd.runner import apply_events, run_script, split_phases
 
-NAN_BITS = {"f32": 0x7FC00001, "bf16": 0x7FC1}
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+NAN_BITS = {"f32": 0x7FC00001, "bf16": 0x7FC1, "fp8_e4m3": 0x7F}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.float8_e4m3fn}
+INT_VIEW = {torch.float32: torch.int32, torch.bfloat16: torch.int16, torch.float8_e4m3fn: torch.uint8}
 
 # bf16 inputs, fp32 accumulation: allclose per element with these; fp32: max-abs.
 BF16_RTOL, BF16_ATOL = 2e-2, 5e-3
@@ -26,7 +27,9 @@ def to_device(wl, a: np.ndarray) -> torch.Tensor:
 
 
 def pool_bits(t: torch.Tensor) -> np.ndarray:
-    """Raw bits of a device tensor as a host numpy array (uint16 or uint32)."""
+    """Raw bits of a device tensor as a host numpy array (uint8, uint16 or uint32)."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cpu().numpy()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.view(torch.int32).cpu().numpy().view(np.uint32)
@@ -41,12 +44,13 @@ class Loaded:
 
     def __init__(self, wl, upto_decode: bool = False):
         self.wl = wl
-        dt = TORCH_DTYPE[wl.dtype]
-        self.pool = pkv.KVPool.empty(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, dt)
-        ibits = torch.int16 if dt == torch.bfloat16 else torch.int32
+        dt = TORCH_DTYPE[wl.pool_dtype]
+        self.pool = pkv.KVPool.empty(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, dt,
+                                     k_scale=wl.k_scale, v_scale=wl.v_scale)
+        ibits = INT_VIEW[dt]
         # NaN bit pattern (fits the signed view): an unwritten slot read by mistake shows up
-        self.pool.k.view(ibits).fill_(NAN_BITS[wl.dtype])
-        self.pool.v.view(ibits).fill_(NAN_BITS[wl.dtype])
+        self.pool.k.view(ibits).fill_(NAN_BITS[wl.pool_dtype])
+        self.pool.v.view(ibits).fill_(NAN_BITS[wl.pool_dtype])
         self.alloc = pkv.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
         self.events = run_script(self.alloc, wl.ops)
         self.phases = split_phases(self.events)

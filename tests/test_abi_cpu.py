@@ -118,3 +118,20 @@ def test_stream_probe_rejects_bad_arguments():
     assert L.pa_probe_stream_read(16, 24, 0, 16, None) == -1  # bytes not a multiple of 16
     assert L.pa_probe_stream_read(8, 16, 0, 16, None) == -1  # unaligned buffer
     assert L.pa_last_error()
+
+
+def test_fp8_pool_validation():
+    L = lib()
+    ok = _pool(dtype=2)
+    ok.k_scale, ok.v_scale = 0.5, 2.0
+    # a valid FP8 pool passes the pool checks (then fails on the NULL arrays)
+    assert L.pa_cache_write(ctypes.byref(ok), None, None, None, 1, None) == -1
+    assert b"NULL" in L.pa_last_error()
+    for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("inf"), 1.0), (1.0, float("nan"))):
+        p = _pool(dtype=2)
+        p.k_scale, p.v_scale = ks, vs
+        assert L.pa_cache_write(ctypes.byref(p), 16, 16, 16, 1, None) == -1
+        assert b"scale" in L.pa_last_error()
+    # chunked prefill is built for bf16 pools only
+    assert L.pa_prefill_chunk(16, 16, 16, 16, ctypes.byref(ok), 16, 4, 1, 8, 16,
+                              ctypes.c_float(0.1), None) == -2

@@ -14,7 +14,7 @@ import torch
 
 import paged_kv_cache_316_amd as pkv
 import workloads
-from oracle.expected import decode_out, pool_after
+from oracle.expected import decode_out, pool_after, stored_rows
 
 from gpu_util import Loaded, assert_close, out_f64, pool_bits, to_device
 
@@ -60,7 +60,7 @@ def test_decode_matches_oracle_small(name):
 
 
 @pytest.mark.parametrize("workers", [1, 3, 7, 64, 333, 2048, 4096])
-@pytest.mark.parametrize("name", ["llama13b", "llama70b", "tiny", "cow504"])
+@pytest.mark.parametrize("name", ["llama13b", "llama70b", "tiny", "cow504", "llama13b_fp8"])
 def test_worker_splits_agree(name, workers):
     """Any number of wavefronts (one wave for everything, up to more waves than
     tiles, so segments split at arbitrary tiles and recombine by log-sum-exp)
@@ -140,9 +140,13 @@ def test_shared_blocks_equal_copied_blocks_bitwise(name):
     assert torch.equal(out2.view(torch.int16), base.view(torch.int16))
 
 
+FP8_SCALES = (2.0 ** -6, 0.0123)  # K: a power of two; V: not, so x / scale rounds
+
+
 def _single_seq(L, Hq, Hkv, D, B, dtype, seed, zero_keys=False):
-    """One sequence laid out in reverse block order, through the C ABI."""
-    import paged_kv_cache_316_amd as pkv
+    """One sequence laid out in reverse block order, through the C ABI. For
+    dtype "fp8" the pool holds E4M3 codes and the returned k, v are the values
+    those codes stand for (oracle quantization of the bf16 inputs)."""
     rng = np.random.default_rng(seed)
     nb = -(-L // B)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
@@ -151,18 +155,28 @@ def _single_seq(L, Hq, Hkv, D, B, dtype, seed, zero_keys=False):
     if zero_keys:
         k.zero_()
     q = torch.from_numpy(rng.standard_normal((1, Hq, D)).astype(np.float32)).to(tdt)
-    pool = pkv.KVPool.empty(nb + 3, Hkv, B, D, tdt)
-    pool.k.fill_(float("nan")); pool.v.fill_(float("nan"))
+    if dtype == "fp8":
+        pool = pkv.KVPool.empty(nb + 3, Hkv, B, D, torch.float8_e4m3fn, k_scale=FP8_SCALES[0],
+                                v_scale=FP8_SCALES[1])
+        pool.k.view(torch.uint8).fill_(0x7F); pool.v.view(torch.uint8).fill_(0x7F)  # NaN codes
+    else:
+        pool = pkv.KVPool.empty(nb + 3, Hkv, B, D, tdt)
+        pool.k.fill_(float("nan")); pool.v.fill_(float("nan"))
     table = np.arange(nb + 2, 2, -1)[:nb].astype(np.int32)  # reversed, offset placement
     slots = torch.from_numpy((table[np.arange(L) // B].astype(np.int64) * B + np.arange(L) % B)).cuda()
     pkv.cache_write(pool, k.cuda().contiguous(), v.cuda().contiguous(), slots)
     out = pkv.decode(q.cuda(), pool, torch.from_numpy(table[None]).cuda(),
                      torch.tensor([L], dtype=torch.int32, device="cuda"), 1 / np.sqrt(D))
     torch.cuda.synchronize()
+    if dtype == "fp8":
+        from oracle import fp8
+        kd = fp8.dequantize(fp8.quantize(k.float().numpy(), FP8_SCALES[0]), FP8_SCALES[0])
+        vd = fp8.dequantize(fp8.quantize(v.float().numpy(), FP8_SCALES[1]), FP8_SCALES[1])
+        return q.double().numpy(), kd, vd, out_f64(out)
     return q.double().numpy(), k.double().numpy(), v.double().numpy(), out_f64(out)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 @pytest.mark.parametrize("L", [1, 2, 15, 16, 17, 511, 512, 513, 1000, 4097])
 @pytest.mark.parametrize("D,B,Hq,Hkv", [
     (128, 16, 8, 1), (64, 4, 4, 4), (128, 32, 6, 2), (64, 8, 8, 8),
@@ -185,7 +199,7 @@ def test_edge_lengths(dtype, L, D, B, Hq, Hkv):
             assert np.array_equal(got, expect)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 def test_zero_keys_give_mean_of_values(dtype):
     q, k, v, got = _single_seq(300, 4, 2, 128, 16, dtype, seed=3, zero_keys=True)
     want = np.repeat(v.mean(axis=0), 2, axis=0)[None]
@@ -224,7 +238,7 @@ def test_cache_write_skips_negative_slots():
     assert torch.equal(pool.k.view(torch.int16), ref_k.view(torch.int16))
 
 
-FULL = ["tiny", "llama13b", "cow", "cow504", "beam", "prefix", "llama70b"]
+FULL = ["tiny", "llama13b", "cow", "cow504", "beam", "prefix", "llama70b", "llama13b_fp8"]
 
 
 @pytest.mark.slow
@@ -253,7 +267,8 @@ def test_full_size_sampled(name):
         L = int(lens[i])
         t = np.arange(L)
         rows = kb[tables[i, t // wl.block_size], :, t % wl.block_size, :]
-        assert np.array_equal(rows, wl.rows_k[wl.hist[seq]].view(rows.dtype))
+        stored_k, _ = stored_rows(wl, wl.rows_k[wl.hist[seq]], wl.rows_v[wl.hist[seq]][:0])
+        assert np.array_equal(rows, stored_k.view(rows.dtype))
 
 
 def test_stream_read_probe_runs():

@@ -149,6 +149,17 @@ def llama13b(rng, size):
     return _plain_decode("llama13b", rng, lens, Hq=40, Hkv=40, D=128, B=16, dtype="bf16")
 
 
+def llama13b_fp8(rng, size):
+    """The llama13b structure with an FP8 (E4M3) KV cache: queries and new K/V
+    rows are bf16 as drawn, and the pool stores them as 8-bit codes with one
+    scale per pool (2^-6, so N(0,1) values sit well inside the format's range)."""
+    wl = llama13b(rng, size)
+    wl.name = "llama13b_fp8"
+    wl.kv_dtype = "fp8_e4m3"
+    wl.k_scale = wl.v_scale = 2.0 ** -6
+    return wl
+
+
 def llama70b(rng, size):
     """Llama-2-70B-shaped GQA layer: 64 query / 8 KV heads of 128, bf16, blocks of 16,
     lengths log-uniform on [128, 8192]; 8 sequences also take a 512-row prefill chunk."""
@@ -312,6 +323,7 @@ CONFIGS: Dict[str, tuple] = {
     "beam": (32, beam),
     "prefix": (4, prefix),
     "llama70b": (5, llama70b),
+    "llama13b_fp8": (21, llama13b_fp8),
 }
 
 

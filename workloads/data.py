@@ -68,10 +68,20 @@ class Workload:
     prefill_len: int = 0
     prefill_q: Optional[np.ndarray] = None  # [len(prefill_seqs)*prefill_len, Hq, D]
     meta: Dict[str, Any] = field(default_factory=dict)
+    # KV pool storage type when it differs from ``dtype``: "fp8_e4m3" stores
+    # the K/V rows (drawn as ``dtype``) as 8-bit codes, one scale per pool
+    kv_dtype: str = ""
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def pool_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def elt_bytes(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        """Bytes per stored K/V element in the pool."""
+        return {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[self.pool_dtype]
 
     @property
     def seq_lens(self) -> np.ndarray:
