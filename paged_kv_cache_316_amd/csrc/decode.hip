@@ -428,6 +428,9 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
           }
         }
       };
+      // Every load is unconditional (a prefetch past the chunk re-reads its last
+      // tile, an L2 hit): with conditional loads the compiler cannot count the
+      // loads in flight and waits for all of them before each tile.
       uint4 kA[U], vA[U], kB[U], vB[U];
       int j = jc;
       load_tile(j, kA, vA);
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
         load_tile(j + 1, kB, vB);
         __builtin_amdgcn_sched_barrier(0);  // keep the next tile's loads ahead of this math
         compute(j, x.L, kA, vA);
-        if (j + 2 < jc_end) load_tile(j + 2, kA, vA);
+        load_tile(min(j + 2, jc_end - 1), kA, vA);
         __builtin_amdgcn_sched_barrier(0);
         compute(j + 1, x.L, kB, vB);
       }
@@ -505,6 +508,9 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   constexpr int NI = kTile / RPI;   // loads per lane per tile, for K and for V
   constexpr int RPL = 256 / ROW;    // rows per 256-byte LDS bank line
   constexpr int TB = kTile * ROW;   // bytes of one K or V tile in LDS
+  // tiles in flight per wave: an FP8 tile is half the bytes, so more of them
+  // are needed to keep as many bytes in flight
+  constexpr int NB = FP8 ? 4 : 2;
   static_assert(HPW <= 16, "one MFMA N tile holds the unit's heads");
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -592,8 +598,14 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     for (int i = 0; i < 4; ++i)
       if (key0 + i >= L) sc[i] = -INFINITY;
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    {  // max over lanes l, l^16, l^32, l^48 (the 4 lanes of head l%16), on the VALU
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                        false, false);
+      mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                        false, false);
+      mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    }
     const bool moved = m == -INFINITY ? mx != -INFINITY : (mx - m) * c2 > 8.f;
     const float mn = moved ? mx : m;
     const float nms = mn == -INFINITY ? 0.f : -mn * c2;
@@ -644,9 +656,9 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   };
 
   // Tiles [j0, j1) of one segment, in chunks whose blocks fit a 64-entry
-  // window of the block table; branch-free and double-buffered as in the
-  // VALU kernel. Keys past the end are clamped to the last token (a valid,
-  // written slot) and masked out in compute.
+  // window of the block table; branch-free, with NB tiles in flight. Keys
+  // past the end are clamped to the last token (a valid, written slot) and
+  // masked out in compute.
   auto run_tiles = [&](const Cursor& x, int j0, int j1) {
     const int32_t* row = a.block_tables + int64_t(x.s) * a.max_blocks_per_seq;
     const int nblk = (x.L + Bm1) >> b_shift;
@@ -668,18 +680,27 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
           vr[u] = load_stream16(reinterpret_cast<const uint4*>(vp + off));
         }
       };
-      uint4 kA[NI], vA[NI], kB[NI], vB[NI];
+      // NB tiles in flight: tile j + NB - 1 loads while tile j is computed
+      // (buffer b holds the tiles j with j % NB == b relative to jc). Every
+      // load is unconditional (past the chunk it re-reads the chunk's last
+      // tile, an L2 hit): with conditional loads the compiler cannot count the
+      // loads in flight and waits for all of them.
+      uint4 kb[NB][NI], vb[NB][NI];
       int j = jc;
-      load_tile(j, kA, vA);
-      for (; j + 2 <= jc_end; j += 2) {
-        load_tile(j + 1, kB, vB);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(j, x.L, kA, vA);
-        if (j + 2 < jc_end) load_tile(j + 2, kA, vA);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(j + 1, x.L, kB, vB);
+#pragma unroll
+      for (int b = 0; b < NB - 1; ++b) load_tile(min(j + b, jc_end - 1), kb[b], vb[b]);
+      for (; j + NB <= jc_end; j += NB) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int jl = min(j + b + NB - 1, jc_end - 1);
+          load_tile(jl, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+          __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this tile's math
+          compute(j + b, x.L, kb[b], vb[b]);
+        }
       }
-      if (j < jc_end) compute(j, x.L, kA, vA);
+#pragma unroll
+      for (int b = 0; b < NB - 1; ++b)  // the last tiles, already loaded
+        if (j + b < jc_end) compute(j + b, x.L, kb[b], vb[b]);
       jc = jc_end;
     }
   };
