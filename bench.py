@@ -256,6 +256,69 @@ def prefill_step_fn(ld):
     return step
 
 
+def shared_prefix_blocks(ld):
+    """Blocks every table row starts with (the prefix-cache hits), checked on the host."""
+    wl = ld.wl
+    P = wl.meta["prefix_tokens"] // wl.block_size
+    t = ld.tables_d.cpu().numpy()
+    if not ((t[:, :P] == t[0, :P]).all() and (ld.lens >= P * wl.block_size).all()):
+        raise RuntimeError("workload rows do not share their first blocks")
+    return P
+
+
+def shared_prefix_step_fn(ld, workers, P):
+    import torch
+    import paged_kv_cache_316_amd as pkv
+    wl = ld.wl
+    S = len(wl.decode_seqs)
+    out = torch.empty_like(ld.q)
+    n = pkv.decode_shared_prefix_workspace_bytes(S, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                                 wl.block_size, P, workers)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev):
+        p = ld.pools[i % len(ld.pools)]
+        if ev is not None:
+            ev[0].record(stream)
+        ld.decode_write.run(p)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.decode_shared_prefix(ld.q, p, ld.tables_d, ld.lens_d, P, wl.scale, workers, out=out,
+                                 workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+    return step
+
+
+def shared_prefix_row(ld, steps, warmup, workers):
+    """The prefix-cached batch through pa_decode_shared_prefix, beside pa_decode
+    on the same batch. Unique bytes: the shared blocks once plus every tail."""
+    wl = ld.wl
+    P = shared_prefix_blocks(ld)
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elt_bytes
+    Lp = P * wl.block_size
+    unique = float(Lp + (ld.lens.astype("int64") - Lp).sum()) * per_tok
+    plain = decode_row(ld, steps, warmup, workers)
+    ms_step, w_ms, d_ms = time_steps(shared_prefix_step_fn(ld, workers, P), steps, warmup)
+    t = float(d_ms.mean()) * 1e-3
+    achieved = unique / t / 1e9
+    S = len(wl.decode_seqs)
+    return {"workload": WORKLOAD_TEXT[ld.name], "shared_blocks": P,
+            "ms_per_step": round(ms_step, 5), "tokens_per_s": round(S / (ms_step * 1e-3), 1),
+            "decode_us": _stats_us(d_ms), "cache_write_us": round(float(w_ms.mean()) * 1e3, 2),
+            "logical_kv_bytes": int(ld.kv_bytes), "unique_kv_bytes": int(unique),
+            "logical_kv_gbps": round(ld.kv_bytes / t / 1e9, 2),
+            "plain_decode": {"ms_per_step": plain["ms_per_step"], "decode_us": plain["decode_us"],
+                             "logical_kv_gbps": plain["decode_kv_gbps"]},
+            "speedup_vs_plain_decode": round(plain["decode_us"]["mean"] / (t * 1e6), 3),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                         "traffic": None,
+                         "kernel": "pa_decode_shared_prefix (suffix decode + prefix MFMA pass + merge), "
+                                   "unique bytes over the whole call"}}
+
+
 def stream_read_ceiling(gib: int = 4):
     """Best streaming-read rate (GB/s) of pa_probe_stream_read over a few grid sizes."""
     import torch
@@ -326,7 +389,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-rows", action="store_true",
-                    help="skip the Llama-2-70B-shaped GQA decode, chunked-prefill and FP8-KV decode rows")
+                    help="skip the Llama-2-70B-shaped GQA decode, chunked-prefill, FP8-KV decode "
+                         "and shared-prefix decode rows")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -416,6 +480,13 @@ def main():
             f["tokens_per_s_model_equiv"] = round(f["tokens_per_s"] / MODEL_LAYERS["llama13b_fp8"], 1)
             f["pct_of_stream_ceiling"] = round(100 * f["decode_kv_gbps"] / ceiling["gbps"], 2)
             f["workload"] = WORKLOAD_TEXT["llama13b_fp8"]
+        if ld.name != "prefix":
+            del ld
+            gc.collect()
+            torch.cuda.empty_cache()
+            ld = Loaded("prefix", args.replicas)
+        rows["decode_prefix_shared"] = shared_prefix_row(ld, max(20, args.steps // 4), args.warmup,
+                                                         args.workers)
         result["rows"] = rows
     print(json.dumps(result), flush=True)
 

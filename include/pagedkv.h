@@ -171,6 +171,52 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Workspace needed by pa_decode_shared_prefix, in bytes (0 for invalid sizes).
+ * block_size and num_prefix_blocks size the partials of the shared part.
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t block_size, int32_t num_prefix_blocks,
+                                               int32_t num_workers);
+
+/*
+ * pa_decode_shared_prefix — pa_decode for a batch whose block tables all begin
+ * with the same num_prefix_blocks physical blocks, the case prefix caching
+ * produces when requests share a prompt start ("Why PagedAttention multiplies
+ * LLM serving throughput", section "Automatic prefix caching"; "LLM inference
+ * engine internals", section 2.3). The result is the same attention as
+ * pa_decode gives (every sequence attends over all seq_lens[s] tokens), but
+ * the shared blocks are read once per KV head for the whole batch instead of
+ * once per sequence:
+ *   1. the tail of each sequence (tokens P*B .. seq_lens[s]-1) runs through the
+ *      pa_decode kernels, which also record each row's log-sum-exp;
+ *   2. one pass on the matrix cores attends all num_seqs * G query rows of a KV
+ *      head to the P*B shared tokens, keys cut into ranges, and writes
+ *      unnormalised partials;
+ *   3. a merge combines the partials and the tail result by the log-sum-exp
+ *      rule into `out`.
+ * Arguments are those of pa_decode, plus:
+ *   num_prefix_blocks : host, P in [0, max_blocks_per_seq]. Precondition: for
+ *                  every s, block_tables[s][0..P-1] == block_tables[0][0..P-1]
+ *                  and seq_lens[s] >= P * B (the shared blocks are full). The
+ *                  library reads the shared blocks through row 0 only; a batch
+ *                  that breaks the precondition gets wrong results (tails
+ *                  shorter than 0 count as 0). P = 0 is the plain pa_decode.
+ *   workspace    : device, >= pa_decode_shared_prefix_workspace_bytes(...)
+ *                  bytes, 16-byte aligned, scratch; calls sharing one must
+ *                  not overlap.
+ * bf16 and PA_FP8_E4M3 pools, head_dim 64 or 128 (PA_ERR_UNSUPPORTED
+ * otherwise); output bf16. The tail result is rounded to bf16 once before the
+ * merge, which adds at most one bf16 rounding of the tail's share of each
+ * output element.
+ */
+pa_status pa_decode_shared_prefix(void* out, const void* q, const pa_pool* pool,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                  float scale, int32_t num_prefix_blocks, int32_t num_workers,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill_chunk — causal attention of a chunk of prompt rows per sequence
  * over that sequence's paged K/V ("vLLM PagedAttention explained", section
  * 7.2: a long prompt is processed in chunks that join the block table).

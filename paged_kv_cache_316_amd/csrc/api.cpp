@@ -54,6 +54,33 @@ DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
   return d;
 }
 
+size_t align16(size_t n) { return (n + 15) & ~size_t(15); }
+
+// Shared-prefix decode workspace: the decode's, then the suffix lengths, the
+// suffix log-sum-exp and the prefix partials.
+struct PrefixLayout {
+  DecodeLayout dec;
+  PrefixPlan plan;
+  size_t sfx_off, lse_off, ml_off, acc_off, end;
+  size_t total() const { return end; }
+};
+
+PrefixLayout prefix_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_prefix_blocks,
+                           int32_t workers) {
+  PrefixLayout p{};
+  p.dec = decode_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, workers);
+  p.plan = prefix_plan(num_seqs, num_q_heads, num_kv_heads, block_size, num_prefix_blocks,
+                       device_cus());
+  const size_t rows = size_t(num_seqs) * num_q_heads;
+  p.sfx_off = align16(p.dec.total());
+  p.lse_off = p.sfx_off + align16(size_t(num_seqs) * 4);
+  p.ml_off = p.lse_off + align16(rows * 4);
+  p.acc_off = p.ml_off + align16(size_t(p.plan.n_split) * rows * 8);
+  p.end = p.acc_off + size_t(p.plan.n_split) * rows * head_dim * 4;
+  return p;
+}
+
 bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int32_t elt_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
@@ -81,6 +108,37 @@ pa_status check_pool(const pa_pool* p, const char* who) {
 pa_status hip_status(hipError_t e, const char* who) {
   if (e == hipSuccess) return PA_OK;
   return fail(PA_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
+}
+
+DecodeArgs decode_args(void* out, const void* q, const pa_pool* pool, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                       int32_t num_q_heads, float scale, const DecodeLayout& lay, void* workspace) {
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = pool->k_pool;
+  a.v_pool = pool->v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_acc = reinterpret_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float2*>(ws + lay.acc_bytes);
+  a.ws_seg = reinterpret_cast<int4*>(ws + lay.acc_bytes + lay.ml_bytes);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.block_size = pool->block_size;
+  a.dtype = pool->dtype;
+  a.workers = lay.workers;
+  a.num_cus = device_cus();
+  a.scale = scale;
+  const bool fp8 = pool->dtype == PA_FP8_E4M3;
+  a.k_scale = fp8 ? pool->k_scale : 1.f;
+  a.v_scale = fp8 ? pool->v_scale : 1.f;
+  a.lse = nullptr;
+  return a;
 }
 
 }  // namespace
@@ -205,31 +263,103 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t
                 workspace ? workspace_bytes : size_t(0), lay.total());
   if (reinterpret_cast<uintptr_t>(workspace) & 15)
     return fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
-  pa::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_pool = pool->k_pool;
-  a.v_pool = pool->v_pool;
-  a.block_tables = block_tables;
-  a.seq_lens = seq_lens;
-  char* ws = static_cast<char*>(workspace);
-  a.ws_acc = reinterpret_cast<float*>(ws);
-  a.ws_ml = reinterpret_cast<float2*>(ws + lay.acc_bytes);
-  a.ws_seg = reinterpret_cast<int4*>(ws + lay.acc_bytes + lay.ml_bytes);
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = pool->num_kv_heads;
-  a.head_dim = pool->head_dim;
-  a.block_size = pool->block_size;
-  a.dtype = pool->dtype;
-  a.workers = lay.workers;
-  a.num_cus = pa::device_cus();
-  a.scale = scale;
-  const bool fp8 = pool->dtype == PA_FP8_E4M3;
-  a.k_scale = fp8 ? pool->k_scale : 1.f;
-  a.v_scale = fp8 ? pool->v_scale : 1.f;
+  const pa::DecodeArgs a = pa::decode_args(out, q, pool, block_tables, max_blocks_per_seq,
+                                           seq_lens, num_seqs, num_q_heads, scale, lay, workspace);
   return pa::hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)), "pa_decode");
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t block_size, int32_t num_prefix_blocks,
+                                               int32_t num_workers) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_prefix_blocks < 0 || num_workers < 0 || num_q_heads % num_kv_heads)
+    return 0;
+  return pa::prefix_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           num_prefix_blocks, num_workers).total();
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* q, const pa_pool* pool,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                  float scale, int32_t num_prefix_blocks, int32_t num_workers,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  const char* who = "pa_decode_shared_prefix";
+  if (pa_status s = pa::check_pool(pool, who)) return s;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0)
+    return fail(PA_ERR_INVALID, "%s: num_seqs=%d max_blocks_per_seq=%d num_q_heads=%d", who,
+                num_seqs, max_blocks_per_seq, num_q_heads);
+  if (num_prefix_blocks < 0 || num_prefix_blocks > max_blocks_per_seq)
+    return fail(PA_ERR_INVALID, "%s: num_prefix_blocks=%d outside [0, max_blocks_per_seq=%d]", who,
+                num_prefix_blocks, max_blocks_per_seq);
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !block_tables || !seq_lens)
+    return fail(PA_ERR_INVALID, "%s: out/q/block_tables/seq_lens is NULL", who);
+  if (num_q_heads % pool->num_kv_heads)
+    return fail(PA_ERR_INVALID, "%s: num_q_heads=%d not a multiple of num_kv_heads=%d", who,
+                num_q_heads, pool->num_kv_heads);
+  if (!(scale == scale)) return fail(PA_ERR_INVALID, "%s: scale is NaN", who);
+  if (num_workers < 0 || num_workers > (1 << 24))
+    return fail(PA_ERR_INVALID, "%s: num_workers=%d out of range", who, num_workers);
+  if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
+       reinterpret_cast<uintptr_t>(pool->k_pool) | reinterpret_cast<uintptr_t>(pool->v_pool)) & 15)
+    return fail(PA_ERR_INVALID, "%s: out/q/pools must be 16-byte aligned", who);
+  const int32_t G = num_q_heads / pool->num_kv_heads;
+  if ((pool->dtype != PA_BF16 && pool->dtype != PA_FP8_E4M3) ||
+      (pool->head_dim != 64 && pool->head_dim != 128))
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype=%d head_dim=%d not built (bf16 or fp8, 64 or 128)",
+                who, pool->dtype, pool->head_dim);
+  if (int64_t(num_seqs) * G >= (int64_t(1) << 30))
+    return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs * group too large", who);
+  const pa::PrefixLayout lay =
+      pa::prefix_layout(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim,
+                        pool->block_size, num_prefix_blocks, num_workers);
+  if (!workspace || workspace_bytes < lay.total())
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who,
+                workspace ? workspace_bytes : size_t(0), lay.total());
+  if (reinterpret_cast<uintptr_t>(workspace) & 15)
+    return fail(PA_ERR_INVALID, "%s: workspace must be 16-byte aligned", who);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (num_prefix_blocks == 0) {  // nothing shared: the plain decode
+    const pa::DecodeArgs a = pa::decode_args(out, q, pool, block_tables, max_blocks_per_seq,
+                                             seq_lens, num_seqs, num_q_heads, scale, lay.dec, ws);
+    return pa::hip_status(pa::launch_decode(a, st), who);
+  }
+  int32_t* sfx = reinterpret_cast<int32_t*>(ws + lay.sfx_off);
+  float* lse = reinterpret_cast<float*>(ws + lay.lse_off);
+  const int32_t prefix_tokens = num_prefix_blocks * pool->block_size;
+  if (pa_status s = pa::hip_status(
+          pa::launch_suffix_lens(seq_lens, sfx, num_seqs, prefix_tokens, st), who))
+    return s;
+  // the suffix: table rows start after the shared blocks (same row stride)
+  pa::DecodeArgs a = pa::decode_args(out, q, pool, block_tables + num_prefix_blocks,
+                                     max_blocks_per_seq, sfx, num_seqs, num_q_heads, scale,
+                                     lay.dec, ws);
+  a.lse = lse;
+  if (pa_status s = pa::hip_status(pa::launch_decode(a, st), who)) return s;
+  pa::PrefixArgs p{};
+  p.out = out;
+  p.q = q;
+  p.k_pool = pool->k_pool;
+  p.v_pool = pool->v_pool;
+  p.block_tables = block_tables;
+  p.lse = lse;
+  p.p_acc = reinterpret_cast<float*>(ws + lay.acc_off);
+  p.p_ml = reinterpret_cast<float2*>(ws + lay.ml_off);
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.head_dim = pool->head_dim;
+  p.block_size = pool->block_size;
+  p.dtype = pool->dtype;
+  p.num_prefix_blocks = num_prefix_blocks;
+  p.n_split = lay.plan.n_split;
+  p.scale = scale;
+  p.k_scale = a.k_scale;
+  p.v_scale = a.v_scale;
+  return pa::hip_status(pa::launch_prefix(p, lay.plan, st), who);
 }
 
 pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,

@@ -171,6 +171,8 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
     if (a.seq_lens[s] > 0) continue;
     uint4* o = static_cast<uint4*>(a.out) + (int64_t(s) * Hq * D) / VEC;
     for (int i = lane; i < Hq * D / VEC; i += kWave) o[i] = make_uint4(0, 0, 0, 0);
+    if (a.lse)
+      for (int h = lane; h < Hq; h += kWave) a.lse[int64_t(s) * Hq + h] = -INFINITY;
   }
   if (w >= W) {
     if (lane == 0) a.ws_seg[w] = make_int4(-1, 0, 0, 0);
@@ -366,6 +368,8 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
       if (r == 0) {
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
+          if (a.lse && c == 0)
+            a.lse[int64_t(x.s) * Hq + head_of(x) + hh] = m[hh] + __builtin_amdgcn_logf(l[hh]);
           const float inv = 1.f / l[hh];
           float f[VEC];
 #pragma unroll
@@ -473,24 +477,6 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
 // The MFMA work is a small fraction of the time the tile's bytes take to
 // arrive, so the kernel streams K/V like the MHA kernel while the per-head
 // VALU work of that kernel (dot products, reductions) disappears.
-typedef short bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-
-// 16 E4M3 codes -> 16 bf16 values (exact) in two 16-byte chunks.
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.f, HI));
-}
-__device__ __forceinline__ void widen_e4m3(const uint4& c, uint4& lo, uint4& hi) {
-  lo = make_uint4(e4m3_pair<false>(c.x), e4m3_pair<true>(c.x), e4m3_pair<false>(c.y),
-                  e4m3_pair<true>(c.y));
-  hi = make_uint4(e4m3_pair<false>(c.z), e4m3_pair<true>(c.z), e4m3_pair<false>(c.w),
-                  e4m3_pair<true>(c.w));
-}
-
 // KV = PA_BF16, or PA_FP8_E4M3: the pool holds E4M3 codes, which are widened
 // exactly to bf16 on their way into LDS; k_scale then multiplies the scores and
 // v_scale the output, and everything from LDS on is the bf16 kernel.
@@ -637,6 +623,8 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     l += __shfl_xor(l, 32);
     if (i16 >= HPW) return;
     if (owns_start && owns_end) {
+      if (a.lse && g == 0)
+        a.lse[int64_t(x.s) * Hq + head_of(x) + i16] = m * c2 + __builtin_amdgcn_logf(l);
       const float inv = vsc / l;
       uint2* orow = reinterpret_cast<uint2*>(static_cast<unsigned char*>(a.out) +
                                              (int64_t(x.s) * Hq + head_of(x) + i16) * ROW);
@@ -749,6 +737,8 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kern
       }
     }
     const float inv = 1.f / den;
+    if (a.lse && c == 0)
+      a.lse[int64_t(seg.x) * a.num_q_heads + head0 + hh] = M + __builtin_amdgcn_logf(den);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) num[e] *= inv;
     uint4* o = static_cast<uint4*>(a.out) + ((int64_t(seg.x) * a.num_q_heads + head0 + hh) * D) / VEC + c;

@@ -68,6 +68,25 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// MFMA operand types.
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// 16 E4M3 codes -> 16 bf16 values (exact) in two 16-byte chunks.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.f, HI));
+}
+__device__ __forceinline__ void widen_e4m3(const uint4& c, uint4& lo, uint4& hi) {
+  lo = make_uint4(e4m3_pair<false>(c.x), e4m3_pair<true>(c.x), e4m3_pair<false>(c.y),
+                  e4m3_pair<true>(c.y));
+  hi = make_uint4(e4m3_pair<false>(c.z), e4m3_pair<true>(c.z), e4m3_pair<false>(c.w),
+                  e4m3_pair<true>(c.w));
+}
+
 // ---------------------------------------------------------------- launches --
 struct DecodeArgs {
   void* out;
@@ -85,6 +104,8 @@ struct DecodeArgs {
   int32_t num_cus;  // compute units of the device (sizes the workgroups)
   float scale;
   float k_scale, v_scale;  // FP8 pools: a code c stands for e4m3(c) * scale (1 otherwise)
+  float* lse;  // optional [num_seqs][num_q_heads]: log2 of each row's softmax denominator
+               // in log2-scaled score units (-inf for an empty sequence)
 };
 
 hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void* v_new,
@@ -98,6 +119,34 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 bool decode_supported(int dtype, int head_dim, int group);
 // Query heads handled together with their KV head by one wave (divides the group size).
 int decode_heads_per_unit(int group);
+
+// Shared-prefix decode: the regular decode runs over the suffixes (table rows
+// offset by the shared blocks, lengths from launch_suffix_lens, lse on), then
+// launch_prefix computes the shared part once and merges it into `out`.
+struct PrefixArgs {
+  void* out;                    // [S][Hq][D] bf16: suffix output in, final output out
+  const void* q;                // [S][Hq][D] bf16
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;  // row 0's first num_prefix_blocks entries: the shared blocks
+  const float* lse;             // [S][Hq] suffix log-sum-exp (log2 units, -inf if empty)
+  float* p_acc;                 // [n_split][S][Hq][D] unnormalised prefix partials
+  float2* p_ml;                 // [n_split][S][Hq] (max in log2 units, denominator)
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
+  int32_t num_prefix_blocks, n_split;
+  float scale, k_scale, v_scale;
+};
+struct PrefixPlan {
+  int32_t n_cblk;           // 16-column blocks per KV head (S * G columns)
+  int32_t n_tiles;          // 16-key tiles of the shared part
+  int32_t tiles_per_split;  // tiles per key range
+  int32_t n_split;          // key ranges (partials per row)
+};
+PrefixPlan prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t block_size, int32_t num_prefix_blocks, int32_t num_cus);
+hipError_t launch_suffix_lens(const int32_t* seq_lens, int32_t* sfx, int32_t n,
+                              int32_t prefix_tokens, hipStream_t stream);
+hipError_t launch_prefix(const PrefixArgs& a, const PrefixPlan& p, hipStream_t stream);
 
 struct PrefillArgs {
   void* out;

@@ -1,0 +1,348 @@
+// Decode for a batch whose block tables all begin with the same full blocks.
+//
+// Prefix caching maps an identical prompt start of many requests onto the same
+// physical blocks ("Why PagedAttention multiplies LLM serving throughput",
+// section "Automatic prefix caching"; "LLM inference engine internals",
+// section 2.3). Plain decode still reads those blocks once per sequence. Here
+// the shared part is read once per KV head for all sequences, and the
+// softmax over the whole sequence is put back together exactly:
+//
+//  1. suffix_lens_kernel: L_s - P*B, the tokens after the shared blocks.
+//  2. the regular decode over the suffixes (table rows offset by P), which also
+//     writes each row's log-sum-exp;
+//  3. prefix_partial_kernel: for every KV head, the queries of all sequences
+//     (S * G columns: sequence s, query head kvh*G + hh is column s*G + hh)
+//     against the P*B shared keys, on the matrix cores. The keys are cut into
+//     n_split ranges; each (KV head, 16-column block, key range) is one wave,
+//     which writes unnormalised partials (sum_t 2^(x_t - m) v_t, m, l).
+//  4. prefix_merge_kernel: per row, M = max of the partial maxima and the
+//     suffix log-sum-exp, and out = (sum_c acc_c 2^(m_c-M) + o_s l_s 2^(m_s-M)) /
+//     (sum_c l_c 2^(m_c-M) + l_s 2^(m_s-M)), o_s being the suffix output.
+// Scores are kept in log2 units (scale * log2(e) folded into the exponent).
+#include "device.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kPTile = 16;           // keys per tile
+constexpr int kPWavesPerGroup = 8;   // column blocks of one (KV head, key range) per workgroup
+constexpr float kPLog2e = 1.4426950408889634f;
+
+__global__ void suffix_lens_kernel(const int32_t* seq_lens, int32_t* sfx, int32_t n, int32_t Lp) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) sfx[i] = max(seq_lens[i] - Lp, 0);
+}
+
+// One wave: KV head kvh, columns 16*cb .. 16*cb + 15, key tiles [t0, t1).
+// Same operand layouts as the GQA decode kernel: K and V tiles go through the
+// wave's own LDS (rows swizzled so that the reads below are conflict-free);
+// S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 keys x 16 columns); the
+// accumulator is already the B operand of O^T = V^T P^T
+// (v_mfma_f32_16x16x16_bf16, V^T read with ds_read_b64_tr_b16); the
+// exponent base of a column moves only when its max grows by more than 2^8.
+template <int D, bool BIG_B, int KV>
+__global__ __launch_bounds__(kWave * kPWavesPerGroup) void prefix_partial_kernel(
+    PrefixArgs a, int32_t b_shift, int32_t n_cblk, int32_t n_cgrp, int32_t tiles_per_split,
+    float scale_log2) {
+  constexpr bool FP8 = KV == PA_FP8_E4M3;
+  constexpr int ROW = 2 * D;           // bytes per bf16 row in LDS
+  constexpr int GROW = FP8 ? D : ROW;  // bytes per row in the pool
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int CPR = ROW / 16;
+  constexpr int GCPR = GROW / 16;
+  constexpr int RPI = 1024 / GROW;     // rows per wave-wide 16-byte load
+  constexpr int NI = kPTile / RPI;
+  constexpr int RPL = 256 / ROW;
+  constexpr int TB = kPTile * ROW;
+  constexpr int NB = FP8 ? 4 : 2;      // tiles in flight per wave
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int lane = threadIdx.x % kWave;
+  const int wig = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wpg = blockDim.x / kWave;
+  // Workgroup i runs on XCD i % 8: renumber so that neighbouring work items
+  // (same KV head and key range, hence the same K/V) share an XCD's L2.
+  int wg = blockIdx.x;
+  if (gridDim.x % 8 == 0) wg = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const int cg = wg % n_cgrp;
+  const int rest = wg / n_cgrp;
+  const int sp = rest % a.n_split;
+  const int kvh = rest / a.n_split;
+  const int cb = cg * wpg + wig;
+  if (cb >= n_cblk) return;
+
+  const int S = a.num_seqs, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int N = S * G;
+  const int g = lane / 16, i16 = lane % 16;
+  const int B = a.block_size, Bm1 = B - 1;
+  const int Lp = a.num_prefix_blocks * B;
+  const int n_tiles = (Lp + kPTile - 1) / kPTile;
+  const int t0 = sp * tiles_per_split;
+  const int t1 = min(t0 + tiles_per_split, n_tiles);
+
+  unsigned char* kt_lds = smem + wig * (2 * TB);
+  unsigned char* vt = kt_lds + TB;
+  auto swz = [](int r) { return (r / RPL) % CPR; };
+  const int lrow = lane / GCPR, lch = lane % GCPR;
+  uint32_t wr[NI], wr2[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int r = u * RPI + lrow;
+    const int c0 = FP8 ? 2 * lch : lch;
+    wr[u] = uint32_t(r * ROW + ((c0 ^ swz(r)) * 16));
+    wr2[u] = uint32_t(r * ROW + (((c0 + 1) ^ swz(r)) * 16));
+  }
+  const uint32_t kr0 = uint32_t(i16 * ROW + ((g ^ swz(i16)) * 16));
+  const int rr = 4 * g + i16 / 4;
+  const uint32_t rd0 = uint32_t(rr * ROW + 8 * (i16 % 2) + (((i16 % 4) / 2) ^ swz(rr)) * 16);
+
+  // this lane's column: sequence s, query head kvh*G + hh (clamped to a real
+  // column; columns past N multiply zeros and write nothing)
+  const int col = cb * 16 + i16;
+  const bool valid = col < N;
+  const int cc = min(col, N - 1);
+  const int s = cc / G;
+  const int head = kvh * G + cc % G;
+  const int64_t orow = int64_t(s) * Hq + head;  // row of out / lse / partials
+
+  uint4 qop[KS];
+  {
+    const unsigned char* qp = static_cast<const unsigned char*>(a.q) + orow * ROW + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 qv = *reinterpret_cast<const uint4*>(qp + 64 * ks);
+      qop[ks] = valid ? qv : make_uint4(0, 0, 0, 0);
+    }
+  }
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lpart = 0.f;
+  const float c2 = FP8 ? scale_log2 * a.k_scale : scale_log2;
+  const float vsc = FP8 ? a.v_scale : 1.f;
+
+  auto compute = [&](int j, const uint4* kr, const uint4* vr) {
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      if constexpr (FP8) {
+        uint4 k0, k1, v0, v1;
+        widen_e4m3(kr[u], k0, k1);
+        widen_e4m3(vr[u], v0, v1);
+        *reinterpret_cast<uint4*>(kt_lds + wr[u]) = k0;
+        *reinterpret_cast<uint4*>(kt_lds + wr2[u]) = k1;
+        *reinterpret_cast<uint4*>(vt + wr[u]) = v0;
+        *reinterpret_cast<uint4*>(vt + wr2[u]) = v1;
+      } else {
+        *reinterpret_cast<uint4*>(kt_lds + wr[u]) = kr[u];
+        *reinterpret_cast<uint4*>(vt + wr[u]) = vr[u];
+      }
+    }
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 kop = *reinterpret_cast<const uint4*>(kt_lds + (kr0 ^ (64u * ks)));
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop),
+                                                  __builtin_bit_cast(bf16x8_t, qop[ks]), sc, 0, 0, 0);
+    }
+    const int key0 = j * kPTile + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (key0 + i >= Lp) sc[i] = -INFINITY;
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    {  // max over the 4 lanes of column l%16
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                        false, false);
+      mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                        false, false);
+      mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    }
+    const bool moved = m == -INFINITY ? mx != -INFINITY : (mx - m) * c2 > 8.f;
+    const float mn = moved ? mx : m;
+    const float nms = mn == -INFINITY ? 0.f : -mn * c2;
+    const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m, c2, nms)) : 1.f;
+    m = mn;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, nms));
+    const uint2 pb = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
+    typedef short bf16x2_v __attribute__((ext_vector_type(2)));
+    const bf16x2_v ones = __builtin_bit_cast(bf16x2_v, 0x3f803f80u);
+    float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pb.x), ones, 0.f, false);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pb.y), ones, ps, false);
+    lpart = lpart * alpha + ps;
+    if (__ballot(moved)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)(vt + (rd0 ^ (32u * dt))));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(bf16x4_t, pb),
+                                                      o[dt], 0, 0, 0);
+    }
+  };
+
+  // Row 0 of the block tables holds the shared blocks. Tiles are walked in
+  // chunks whose blocks fit a 64-entry window of that row (one entry per
+  // lane); keys past the prefix are clamped to its last token and masked.
+  const int32_t* row = a.block_tables;
+  const int nblk = a.num_prefix_blocks;
+  const unsigned char* kp = static_cast<const unsigned char*>(a.k_pool);
+  const unsigned char* vp = static_cast<const unsigned char*>(a.v_pool);
+  const int64_t block_bytes = int64_t(Hkv) * B * GROW;
+  const int64_t head_off = int64_t(kvh) * B * GROW + lch * 16;
+  const int Lm1 = Lp - 1;
+  for (int jc = t0; jc < t1;) {
+    const int jb0 = (jc * kPTile) >> b_shift;
+    const int win = jb0 + lane < nblk ? row[jb0 + lane] : 0;
+    const int jc_end = min(t1, ((jb0 + kWave) << b_shift) / kPTile);
+    auto load_tile = [&](int j, uint4* kr, uint4* vr) {
+      int pb = 0;
+      if constexpr (BIG_B) pb = __builtin_amdgcn_readlane(win, ((j * kPTile) >> b_shift) - jb0);
+#pragma unroll
+      for (int u = 0; u < NI; ++u) {
+        const int t = min(j * kPTile + u * RPI + lrow, Lm1);
+        if constexpr (!BIG_B) pb = __shfl(win, (t >> b_shift) - jb0);
+        const int64_t off = int64_t(pb) * block_bytes + head_off + int64_t(t & Bm1) * GROW;
+        kr[u] = load_stream16(reinterpret_cast<const uint4*>(kp + off));
+        vr[u] = load_stream16(reinterpret_cast<const uint4*>(vp + off));
+      }
+    };
+    // NB tiles in flight; every load is unconditional (past the chunk it
+    // re-reads the chunk's last tile) so the compiler can count them
+    uint4 kb[NB][NI], vb[NB][NI];
+    int j = jc;
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b) load_tile(min(j + b, jc_end - 1), kb[b], vb[b]);
+    for (; j + NB <= jc_end; j += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int jl = min(j + b + NB - 1, jc_end - 1);
+        load_tile(jl, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(j + b, kb[b], vb[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b)
+      if (j + b < jc_end) compute(j + b, kb[b], vb[b]);
+    jc = jc_end;
+  }
+
+  float l = lpart + __shfl_xor(lpart, 16);
+  l += __shfl_xor(l, 32);
+  if (!valid) return;
+  const int64_t prow = int64_t(sp) * S * Hq + orow;
+  float4* dst = reinterpret_cast<float4*>(a.p_acc + prow * D);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    dst[(16 * dt + 4 * g) / 4] =
+        make_float4(o[dt][0] * vsc, o[dt][1] * vsc, o[dt][2] * vsc, o[dt][3] * vsc);
+  if (g == 0) a.p_ml[prow] = make_float2(m * c2, l);
+}
+
+// One thread per 8 output elements of one (sequence, query head) row.
+template <int D>
+__global__ __launch_bounds__(256) void prefix_merge_kernel(PrefixArgs a) {
+  constexpr int C = D / 8;
+  const int64_t rows = int64_t(a.num_seqs) * a.num_q_heads;
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t r = i / C;
+  const int c = int(i % C);
+  if (r >= rows) return;
+  const float lse = a.lse[r];
+  float M = lse;
+  for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, a.p_ml[sp * rows + r].x);
+  const float Ms = M == -INFINITY ? 0.f : M;
+  // the suffix output is normalised: its weight is l_s 2^(m_s - M) = 2^(lse - M)
+  const float fs = __builtin_amdgcn_exp2f(lse - Ms);
+  uint4* o = static_cast<uint4*>(a.out) + r * C + c;
+  const uint4 os = *o;
+  float num[8] = {bf16_lo(os.x) * fs, bf16_hi(os.x) * fs, bf16_lo(os.y) * fs, bf16_hi(os.y) * fs,
+                  bf16_lo(os.z) * fs, bf16_hi(os.z) * fs, bf16_lo(os.w) * fs, bf16_hi(os.w) * fs};
+  float den = fs;
+  for (int sp = 0; sp < a.n_split; ++sp) {
+    const float2 ml = a.p_ml[sp * rows + r];
+    const float f = __builtin_amdgcn_exp2f(ml.x - Ms);
+    den = fmaf(ml.y, f, den);
+    const float4* src = reinterpret_cast<const float4*>(a.p_acc + (sp * rows + r) * D + c * 8);
+    const float4 x0 = src[0], x1 = src[1];
+    num[0] = fmaf(x0.x, f, num[0]);
+    num[1] = fmaf(x0.y, f, num[1]);
+    num[2] = fmaf(x0.z, f, num[2]);
+    num[3] = fmaf(x0.w, f, num[3]);
+    num[4] = fmaf(x1.x, f, num[4]);
+    num[5] = fmaf(x1.y, f, num[5]);
+    num[6] = fmaf(x1.z, f, num[6]);
+    num[7] = fmaf(x1.w, f, num[7]);
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  *o = make_uint4(pack_bf16(num[0] * inv, num[1] * inv), pack_bf16(num[2] * inv, num[3] * inv),
+                  pack_bf16(num[4] * inv, num[5] * inv), pack_bf16(num[6] * inv, num[7] * inv));
+}
+
+template <int D, int KV>
+hipError_t run_prefix(const PrefixArgs& a, const PrefixPlan& p, hipStream_t st) {
+  int b_shift = 0;
+  while ((1 << b_shift) < a.block_size) ++b_shift;
+  const int wpg = p.n_cblk < kPWavesPerGroup ? p.n_cblk : kPWavesPerGroup;
+  const int n_cgrp = (p.n_cblk + wpg - 1) / wpg;
+  const int groups = a.num_kv_heads * a.n_split * n_cgrp;
+  const size_t lds = size_t(wpg) * 2 * kPTile * 2 * D;
+  const float scale_log2 = a.scale * kPLog2e;
+  if (a.block_size >= kPTile)
+    prefix_partial_kernel<D, true, KV><<<groups, kWave * wpg, lds, st>>>(
+        a, b_shift, p.n_cblk, n_cgrp, p.tiles_per_split, scale_log2);
+  else
+    prefix_partial_kernel<D, false, KV><<<groups, kWave * wpg, lds, st>>>(
+        a, b_shift, p.n_cblk, n_cgrp, p.tiles_per_split, scale_log2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = int64_t(a.num_seqs) * a.num_q_heads * (D / 8);
+  prefix_merge_kernel<D><<<int((threads + 255) / 256), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+PrefixPlan prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t block_size, int32_t num_prefix_blocks, int32_t num_cus) {
+  PrefixPlan p{};
+  const int64_t cols = int64_t(num_seqs) * (num_q_heads / num_kv_heads);
+  p.n_cblk = int32_t((cols + 15) / 16);
+  p.n_tiles = int32_t((int64_t(num_prefix_blocks) * block_size + kPTile - 1) / kPTile);
+  if (p.n_tiles <= 0) return p;
+  // about four waves per compute unit, but no key range under 8 tiles
+  const int64_t per_split = int64_t(num_kv_heads) * p.n_cblk;
+  const int64_t want = (int64_t(4) * (num_cus > 0 ? num_cus : 256) + per_split - 1) / per_split;
+  const int64_t cap = p.n_tiles / 8 > 1 ? p.n_tiles / 8 : 1;
+  const int64_t n = want < 1 ? 1 : (want > cap ? cap : want);
+  p.tiles_per_split = int32_t((p.n_tiles + n - 1) / n);
+  p.n_split = (p.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  return p;
+}
+
+hipError_t launch_suffix_lens(const int32_t* seq_lens, int32_t* sfx, int32_t n, int32_t prefix_tokens,
+                              hipStream_t st) {
+  suffix_lens_kernel<<<(n + 255) / 256, 256, 0, st>>>(seq_lens, sfx, n, prefix_tokens);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix(const PrefixArgs& a, const PrefixPlan& p, hipStream_t st) {
+  if (a.n_split != p.n_split || p.n_split <= 0) return hipErrorInvalidValue;
+  if (a.dtype == PA_BF16) {
+    if (a.head_dim == 128) return run_prefix<128, PA_BF16>(a, p, st);
+    if (a.head_dim == 64) return run_prefix<64, PA_BF16>(a, p, st);
+  } else if (a.dtype == PA_FP8_E4M3) {
+    if (a.head_dim == 128) return run_prefix<128, PA_FP8_E4M3>(a, p, st);
+    if (a.head_dim == 64) return run_prefix<64, PA_FP8_E4M3>(a, p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

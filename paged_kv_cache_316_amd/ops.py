@@ -146,6 +146,41 @@ def decode(q: torch.Tensor, pool: KVPool, block_tables: torch.Tensor, seq_lens: 
     return out
 
 
+def decode_shared_prefix_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                         head_dim: int, block_size: int, num_prefix_blocks: int,
+                                         workers: int = 0) -> int:
+    return int(lib().pa_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_prefix_blocks, workers))
+
+
+def decode_shared_prefix(q: torch.Tensor, pool: KVPool, block_tables: torch.Tensor,
+                         seq_lens: torch.Tensor, num_prefix_blocks: int, scale: float,
+                         workers: int = 0, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention for a batch whose table rows all start with the same
+    ``num_prefix_blocks`` full blocks; the shared blocks are read once."""
+    _need(q, "q", pool.io_dtype)
+    _need(block_tables, "block_tables", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    S, Hq, D = q.shape
+    if D != pool.head_dim or block_tables.dim() != 2 or block_tables.shape[0] != S \
+            or seq_lens.shape != (S,):
+        raise ValueError("shape mismatch between q, block_tables and seq_lens")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", pool.io_dtype)
+    if workspace is None:
+        n = decode_shared_prefix_workspace_bytes(S, Hq, pool.num_kv_heads, D, pool.block_size,
+                                                 num_prefix_blocks, workers)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    check(lib().pa_decode_shared_prefix(out.data_ptr(), q.data_ptr(), ctypes.byref(pool.c),
+                                        block_tables.data_ptr(), block_tables.shape[1],
+                                        seq_lens.data_ptr(), S, Hq, float(scale),
+                                        int(num_prefix_blocks), int(workers),
+                                        workspace.data_ptr(), workspace.numel(), _stream()))
+    return out
+
+
 def prefill_chunk(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.Tensor,
                   pool: KVPool, block_tables: torch.Tensor, max_q_len: int, scale: float,
                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -168,4 +203,5 @@ def prefill_chunk(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.Te
 
 
 __all__ = ["KVPool", "DecodePlan", "cache_write", "copy_blocks", "decode",
-           "decode_workspace_bytes", "prefill_chunk", "PagedKVError"]
+           "decode_workspace_bytes", "decode_shared_prefix", "decode_shared_prefix_workspace_bytes",
+           "prefill_chunk", "PagedKVError"]

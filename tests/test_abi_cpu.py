@@ -135,3 +135,39 @@ def test_fp8_pool_validation():
     # chunked prefill is built for bf16 pools only
     assert L.pa_prefill_chunk(16, 16, 16, 16, ctypes.byref(ok), 16, 4, 1, 8, 16,
                               ctypes.c_float(0.1), None) == -2
+
+
+def test_shared_prefix_argument_checks():
+    L = lib()
+    p = _pool(num_kv_heads=8)
+    need = L.pa_decode_shared_prefix_workspace_bytes(2, 8, 8, 128, 16, 3, 0)
+    assert need > L.pa_decode_workspace_bytes(2, 8, 8, 128, 0)
+    args = lambda **kw: [kw.get("out", 16), kw.get("q", 16), ctypes.byref(kw.get("pool", p)), 16,
+                         kw.get("maxb", 4), 16, kw.get("S", 2), kw.get("Hq", 8),
+                         ctypes.c_float(0.1), kw.get("P", 3), kw.get("workers", 0),
+                         kw.get("ws", 16), kw.get("wsb", need), None]
+    call = lambda **kw: L.pa_decode_shared_prefix(*args(**kw))
+    assert call(P=5) == -1 and b"num_prefix_blocks" in L.pa_last_error()  # P > max_blocks
+    assert call(P=-1) == -1
+    assert call(Hq=12) == -1 and b"multiple" in L.pa_last_error()
+    assert call(ws=None) == -5
+    assert call(wsb=need - 1) == -5
+    assert call(out=None) == -1
+    assert call(q=18) == -1  # misaligned
+    assert call(pool=_pool(num_kv_heads=8, dtype=0)) == -2  # fp32 pools: not built
+    assert call(S=0, out=None, q=None) == 0  # no sequences: no-op
+    # workspace sizes grow with the prefix partials and are 0 for bad sizes
+    assert L.pa_decode_shared_prefix_workspace_bytes(2, 6, 4, 128, 16, 3, 0) == 0
+    assert L.pa_decode_shared_prefix_workspace_bytes(2, 8, 8, 128, 16, -1, 0) == 0
+
+
+def test_shared_prefix_workspace_formula():
+    L = lib()
+    # 2 seqs, 2 heads (MHA), D 128, 10 workers, 256 blocks of 16: 256 tiles of 16
+    # keys, 1 column block per KV head -> 2 waves per key range; about 4 waves
+    # per CU on 256 CUs wants 512 ranges, capped at 256/8 = 32 ranges of 8 tiles
+    dec = L.pa_decode_workspace_bytes(2, 2, 2, 128, 10)
+    assert dec == 2 * 10 * 128 * 4 + 20 * 8 + 10 * 16
+    n = L.pa_decode_shared_prefix_workspace_bytes(2, 2, 2, 128, 16, 256, 10)
+    # suffix lengths (2 ints), lse (4 floats), 32 x (m, l) and 32 x 128 floats per row
+    assert n == dec + 16 + 16 + 32 * 4 * 8 + 32 * 4 * 128 * 4
