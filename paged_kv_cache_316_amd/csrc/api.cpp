@@ -56,12 +56,12 @@ DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
 
 size_t align16(size_t n) { return (n + 15) & ~size_t(15); }
 
-// Shared-prefix decode workspace: the decode's, then the suffix lengths, the
-// suffix log-sum-exp and the prefix partials.
+// Shared-prefix decode workspace: the decode's, then the tail log-sum-exp and
+// the prefix partials.
 struct PrefixLayout {
   DecodeLayout dec;
   PrefixPlan plan;
-  size_t sfx_off, lse_off, ml_off, acc_off, end;
+  size_t lse_off, ml_off, acc_off, end;
   size_t total() const { return end; }
 };
 
@@ -73,8 +73,7 @@ PrefixLayout prefix_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
   p.plan = prefix_plan(num_seqs, num_q_heads, num_kv_heads, block_size, num_prefix_blocks,
                        device_cus());
   const size_t rows = size_t(num_seqs) * num_q_heads;
-  p.sfx_off = align16(p.dec.total());
-  p.lse_off = p.sfx_off + align16(size_t(num_seqs) * 4);
+  p.lse_off = align16(p.dec.total());
   p.ml_off = p.lse_off + align16(rows * 4);
   p.acc_off = p.ml_off + align16(size_t(p.plan.n_split) * rows * 8);
   p.end = p.acc_off + size_t(p.plan.n_split) * rows * head_dim * 4;
@@ -138,6 +137,7 @@ DecodeArgs decode_args(void* out, const void* q, const pa_pool* pool, const int3
   a.k_scale = fp8 ? pool->k_scale : 1.f;
   a.v_scale = fp8 ? pool->v_scale : 1.f;
   a.lse = nullptr;
+  a.len_offset = 0;
   return a;
 }
 
@@ -327,16 +327,13 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const pa_pool* pool,
                                              seq_lens, num_seqs, num_q_heads, scale, lay.dec, ws);
     return pa::hip_status(pa::launch_decode(a, st), who);
   }
-  int32_t* sfx = reinterpret_cast<int32_t*>(ws + lay.sfx_off);
   float* lse = reinterpret_cast<float*>(ws + lay.lse_off);
-  const int32_t prefix_tokens = num_prefix_blocks * pool->block_size;
-  if (pa_status s = pa::hip_status(
-          pa::launch_suffix_lens(seq_lens, sfx, num_seqs, prefix_tokens, st), who))
-    return s;
-  // the suffix: table rows start after the shared blocks (same row stride)
+  // the tails: tokens after the shared blocks, table rows from entry P on
+  // (same row stride)
   pa::DecodeArgs a = pa::decode_args(out, q, pool, block_tables + num_prefix_blocks,
-                                     max_blocks_per_seq, sfx, num_seqs, num_q_heads, scale,
+                                     max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale,
                                      lay.dec, ws);
+  a.len_offset = num_prefix_blocks * pool->block_size;
   a.lse = lse;
   if (pa_status s = pa::hip_status(pa::launch_decode(a, st), who)) return s;
   pa::PrefixArgs p{};

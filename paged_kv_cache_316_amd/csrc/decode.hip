@@ -149,6 +149,11 @@ struct Cursor {
 // then records the segment the slice starts and leaves open (if any) for the
 // combine kernel. Also writes zeros for empty sequences. VEC: elements of the
 // output dtype per 16 bytes; hpw: query heads per unit.
+// tokens of sequence s this call attends to: those after the first len_offset
+__device__ __forceinline__ int len_of(const DecodeArgs& a, int s) {
+  return max(a.seq_lens[s] - a.len_offset, 0);
+}
+
 template <int D, int VEC, class Begin, class Run, class End>
 __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane, int n_hchunk,
                                            int hpw, Begin begin, Run run, End end) {
@@ -160,7 +165,7 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
   int64_t total = 0;
   for (int base = 0; base < S; base += kWave) {
     const int s = base + lane;
-    total += wave_sum_i32(s < S ? tiles_of(a.seq_lens[s]) : 0);
+    total += wave_sum_i32(s < S ? tiles_of(len_of(a, s)) : 0);
   }
   total = uniform64(total * units);
   const int64_t W = total < a.workers ? total : a.workers;  // every active wave gets >= 1 tile
@@ -168,7 +173,7 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
   // empty sequences: zeros, written by wave (s mod Wz)
   const int Wz = W > 0 ? int(W) : a.workers;
   for (int s = w; s < S; s += Wz) {
-    if (a.seq_lens[s] > 0) continue;
+    if (len_of(a, s) > 0) continue;
     uint4* o = static_cast<uint4*>(a.out) + (int64_t(s) * Hq * D) / VEC;
     for (int i = lane; i < Hq * D / VEC; i += kWave) o[i] = make_uint4(0, 0, 0, 0);
     if (a.lse)
@@ -186,7 +191,7 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
   auto seq_len = [&](int s) -> int {
     if (s - lwin_base >= kWave || s < lwin_base) {
       lwin_base = s;
-      lwin = s + lane < S ? a.seq_lens[s + lane] : 0;
+      lwin = s + lane < S ? len_of(a, s + lane) : 0;
     }
     return __builtin_amdgcn_readlane(lwin, s - lwin_base);
   };
@@ -197,7 +202,7 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
     int64_t before = 0;  // tiles x units before this chunk of sequences
     for (int base = 0; base < S; base += kWave) {
       const int s = base + lane;
-      const int t = s < S ? tiles_of(a.seq_lens[s]) : 0;
+      const int t = s < S ? tiles_of(len_of(a, s)) : 0;
       const int64_t incl = before + int64_t(wave_incl_scan_i32(t, lane)) * units;
       const int64_t excl = incl - int64_t(t) * units;
       const unsigned long long hit = __ballot(s < S && t > 0 && excl <= g_begin && g_begin < incl);

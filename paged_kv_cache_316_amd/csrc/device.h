@@ -106,6 +106,8 @@ struct DecodeArgs {
   float k_scale, v_scale;  // FP8 pools: a code c stands for e4m3(c) * scale (1 otherwise)
   float* lse;  // optional [num_seqs][num_q_heads]: log2 of each row's softmax denominator
                // in log2-scaled score units (-inf for an empty sequence)
+  int32_t len_offset;  // attend to tokens len_offset .. seq_lens[s]-1; block_tables then
+                       // points at the row entry of block len_offset / block_size
 };
 
 hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void* v_new,
@@ -121,7 +123,7 @@ bool decode_supported(int dtype, int head_dim, int group);
 int decode_heads_per_unit(int group);
 
 // Shared-prefix decode: the regular decode runs over the suffixes (table rows
-// offset by the shared blocks, lengths from launch_suffix_lens, lse on), then
+// offset by the shared blocks, len_offset = their tokens, lse on), then
 // launch_prefix computes the shared part once and merges it into `out`.
 struct PrefixArgs {
   void* out;                    // [S][Hq][D] bf16: suffix output in, final output out
@@ -137,15 +139,14 @@ struct PrefixArgs {
   float scale, k_scale, v_scale;
 };
 struct PrefixPlan {
-  int32_t n_cblk;           // 16-column blocks per KV head (S * G columns)
+  int32_t groups_per_wave;  // 16-column groups one wave computes (1 or 2)
+  int32_t n_cblk;           // column blocks (one per wave) per KV head (S * G columns)
   int32_t n_tiles;          // 16-key tiles of the shared part
   int32_t tiles_per_split;  // tiles per key range
   int32_t n_split;          // key ranges (partials per row)
 };
 PrefixPlan prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t block_size, int32_t num_prefix_blocks, int32_t num_cus);
-hipError_t launch_suffix_lens(const int32_t* seq_lens, int32_t* sfx, int32_t n,
-                              int32_t prefix_tokens, hipStream_t stream);
 hipError_t launch_prefix(const PrefixArgs& a, const PrefixPlan& p, hipStream_t stream);
 
 struct PrefillArgs {

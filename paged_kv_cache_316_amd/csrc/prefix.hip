@@ -7,15 +7,14 @@
 // the shared part is read once per KV head for all sequences, and the
 // softmax over the whole sequence is put back together exactly:
 //
-//  1. suffix_lens_kernel: L_s - P*B, the tokens after the shared blocks.
-//  2. the regular decode over the suffixes (table rows offset by P), which also
-//     writes each row's log-sum-exp;
-//  3. prefix_partial_kernel: for every KV head, the queries of all sequences
+//  1. the regular decode over the tails (tokens P*B .. L_s - 1, table rows
+//     offset by P), which also writes each row's log-sum-exp;
+//  2. prefix_partial_kernel: for every KV head, the queries of all sequences
 //     (S * G columns: sequence s, query head kvh*G + hh is column s*G + hh)
 //     against the P*B shared keys, on the matrix cores. The keys are cut into
 //     n_split ranges; each (KV head, 16-column block, key range) is one wave,
 //     which writes unnormalised partials (sum_t 2^(x_t - m) v_t, m, l).
-//  4. prefix_merge_kernel: per row, M = max of the partial maxima and the
+//  3. prefix_merge_kernel: per row, M = max of the partial maxima and the
 //     suffix log-sum-exp, and out = (sum_c acc_c 2^(m_c-M) + o_s l_s 2^(m_s-M)) /
 //     (sum_c l_c 2^(m_c-M) + l_s 2^(m_s-M)), o_s being the suffix output.
 // Scores are kept in log2 units (scale * log2(e) folded into the exponent).
@@ -26,23 +25,25 @@ namespace pa {
 namespace {
 
 constexpr int kPTile = 16;           // keys per tile
-constexpr int kPWavesPerGroup = 8;   // column blocks of one (KV head, key range) per workgroup
+// 16-column groups per wave, at most. More groups share each K/V tile among
+// more columns, but the pass is bound by the per-score softmax work, not by
+// re-reading tiles: two groups measured best on the prefix-cached batch.
+constexpr int kPMaxGroups = 2;
+// column blocks of one (KV head, key range) per workgroup: 8 waves, or 4 when
+// a wave needs more than 256 registers (more groups, or FP8 widening)
+constexpr int waves_per_group(int ng, bool fp8) { return ng >= 4 || (ng >= 2 && fp8) ? 4 : 8; }
 constexpr float kPLog2e = 1.4426950408889634f;
 
-__global__ void suffix_lens_kernel(const int32_t* seq_lens, int32_t* sfx, int32_t n, int32_t Lp) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) sfx[i] = max(seq_lens[i] - Lp, 0);
-}
-
-// One wave: KV head kvh, columns 16*cb .. 16*cb + 15, key tiles [t0, t1).
+// One wave: KV head kvh, NG groups of 16 columns (columns 16*NG*cb onwards),
+// key tiles [t0, t1).
 // Same operand layouts as the GQA decode kernel: K and V tiles go through the
 // wave's own LDS (rows swizzled so that the reads below are conflict-free);
 // S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 keys x 16 columns); the
 // accumulator is already the B operand of O^T = V^T P^T
 // (v_mfma_f32_16x16x16_bf16, V^T read with ds_read_b64_tr_b16); the
 // exponent base of a column moves only when its max grows by more than 2^8.
-template <int D, bool BIG_B, int KV>
-__global__ __launch_bounds__(kWave * kPWavesPerGroup) void prefix_partial_kernel(
+template <int D, int NG, bool BIG_B, int KV>
+__global__ __launch_bounds__(kWave * waves_per_group(NG, KV == PA_FP8_E4M3)) void prefix_partial_kernel(
     PrefixArgs a, int32_t b_shift, int32_t n_cblk, int32_t n_cgrp, int32_t tiles_per_split,
     float scale_log2) {
   constexpr bool FP8 = KV == PA_FP8_E4M3;
@@ -99,31 +100,38 @@ __global__ __launch_bounds__(kWave * kPWavesPerGroup) void prefix_partial_kernel
   const int rr = 4 * g + i16 / 4;
   const uint32_t rd0 = uint32_t(rr * ROW + 8 * (i16 % 2) + (((i16 % 4) / 2) ^ swz(rr)) * 16);
 
-  // this lane's column: sequence s, query head kvh*G + hh (clamped to a real
-  // column; columns past N multiply zeros and write nothing)
-  const int col = cb * 16 + i16;
-  const bool valid = col < N;
-  const int cc = min(col, N - 1);
-  const int s = cc / G;
-  const int head = kvh * G + cc % G;
-  const int64_t orow = int64_t(s) * Hq + head;  // row of out / lse / partials
-
-  uint4 qop[KS];
-  {
-    const unsigned char* qp = static_cast<const unsigned char*>(a.q) + orow * ROW + 16 * g;
+  // this lane's column in group q: sequence s, query head kvh*G + hh
+  // (clamped to a real column; columns past N multiply zeros and write nothing)
+  bool valid[NG];
+  int64_t orow[NG];  // row of out / lse / partials
+  uint4 qop[NG][KS];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int col = (cb * NG + q) * 16 + i16;
+    valid[q] = col < N;
+    const int cc = min(col, N - 1);
+    orow[q] = int64_t(cc / G) * Hq + kvh * G + cc % G;
+    const unsigned char* qp = static_cast<const unsigned char*>(a.q) + orow[q] * ROW + 16 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint4 qv = *reinterpret_cast<const uint4*>(qp + 64 * ks);
-      qop[ks] = valid ? qv : make_uint4(0, 0, 0, 0);
+      qop[q][ks] = valid[q] ? qv : make_uint4(0, 0, 0, 0);
     }
   }
-  f32x4_t o[DT];
+  f32x4_t o[NG][DT];
+  float m[NG], lpart[NG];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lpart = 0.f;
+  for (int q = 0; q < NG; ++q) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[q][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m[q] = -INFINITY;
+    lpart[q] = 0.f;
+  }
   const float c2 = FP8 ? scale_log2 * a.k_scale : scale_log2;
   const float vsc = FP8 ? a.v_scale : 1.f;
 
+  // one 16-key tile for the NG column groups: the K and V operands are read
+  // from LDS once and shared by the groups
   auto compute = [&](int j, const uint4* kr, const uint4* vr) {
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
@@ -140,50 +148,56 @@ __global__ __launch_bounds__(kWave * kPWavesPerGroup) void prefix_partial_kernel
         *reinterpret_cast<uint4*>(vt + wr[u]) = vr[u];
       }
     }
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    uint4 kop[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 kop = *reinterpret_cast<const uint4*>(kt_lds + (kr0 ^ (64u * ks)));
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop),
-                                                  __builtin_bit_cast(bf16x8_t, qop[ks]), sc, 0, 0, 0);
-    }
+    for (int ks = 0; ks < KS; ++ks) kop[ks] = *reinterpret_cast<const uint4*>(kt_lds + (kr0 ^ (64u * ks)));
+    v4i16_t va[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      va[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vt + (rd0 ^ (32u * dt))));
     const int key0 = j * kPTile + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (key0 + i >= Lp) sc[i] = -INFINITY;
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    {  // max over the 4 lanes of column l%16
-      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                        false, false);
-      mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                        false, false);
-      mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-    }
-    const bool moved = m == -INFINITY ? mx != -INFINITY : (mx - m) * c2 > 8.f;
-    const float mn = moved ? mx : m;
-    const float nms = mn == -INFINITY ? 0.f : -mn * c2;
-    const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m, c2, nms)) : 1.f;
-    m = mn;
-    float p[4];
+    for (int q = 0; q < NG; ++q) {
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, nms));
-    const uint2 pb = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
-    typedef short bf16x2_v __attribute__((ext_vector_type(2)));
-    const bf16x2_v ones = __builtin_bit_cast(bf16x2_v, 0x3f803f80u);
-    float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pb.x), ones, 0.f, false);
-    ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pb.y), ones, ps, false);
-    lpart = lpart * alpha + ps;
-    if (__ballot(moved)) {
+      for (int ks = 0; ks < KS; ++ks)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[ks]),
+                                                    __builtin_bit_cast(bf16x8_t, qop[q][ks]), sc,
+                                                    0, 0, 0);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
+      for (int i = 0; i < 4; ++i)
+        if (key0 + i >= Lp) sc[i] = -INFINITY;
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      {  // max over the 4 lanes of column l%16
+        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                          false, false);
+        mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                          false, false);
+        mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+      }
+      const bool moved = m[q] == -INFINITY ? mx != -INFINITY : (mx - m[q]) * c2 > 8.f;
+      const float mn = moved ? mx : m[q];
+      const float nms = mn == -INFINITY ? 0.f : -mn * c2;
+      const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m[q], c2, nms)) : 1.f;
+      m[q] = mn;
+      float p[4];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4i16_t*)(vt + (rd0 ^ (32u * dt))));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(bf16x4_t, pb),
-                                                      o[dt], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, nms));
+      const uint2 pb = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
+      typedef short bf16x2_v __attribute__((ext_vector_type(2)));
+      const bf16x2_v ones = __builtin_bit_cast(bf16x2_v, 0x3f803f80u);
+      float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pb.x), ones, 0.f, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, pb.y), ones, ps, false);
+      lpart[q] = lpart[q] * alpha + ps;
+      if (__ballot(moved)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[q][dt] *= alpha;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        o[q][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], __builtin_bit_cast(bf16x4_t, pb),
+                                                           o[q][dt], 0, 0, 0);
     }
   };
 
@@ -234,16 +248,19 @@ __global__ __launch_bounds__(kWave * kPWavesPerGroup) void prefix_partial_kernel
     jc = jc_end;
   }
 
-  float l = lpart + __shfl_xor(lpart, 16);
-  l += __shfl_xor(l, 32);
-  if (!valid) return;
-  const int64_t prow = int64_t(sp) * S * Hq + orow;
-  float4* dst = reinterpret_cast<float4*>(a.p_acc + prow * D);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    dst[(16 * dt + 4 * g) / 4] =
-        make_float4(o[dt][0] * vsc, o[dt][1] * vsc, o[dt][2] * vsc, o[dt][3] * vsc);
-  if (g == 0) a.p_ml[prow] = make_float2(m * c2, l);
+  for (int q = 0; q < NG; ++q) {
+    float l = lpart[q] + __shfl_xor(lpart[q], 16);
+    l += __shfl_xor(l, 32);
+    if (!valid[q]) continue;
+    const int64_t prow = int64_t(sp) * S * Hq + orow[q];
+    float4* dst = reinterpret_cast<float4*>(a.p_acc + prow * D);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      dst[(16 * dt + 4 * g) / 4] = make_float4(o[q][dt][0] * vsc, o[q][dt][1] * vsc,
+                                               o[q][dt][2] * vsc, o[q][dt][3] * vsc);
+    if (g == 0) a.p_ml[prow] = make_float2(m[q] * c2, l);
+  }
 }
 
 // One thread per 8 output elements of one (sequence, query head) row.
@@ -286,20 +303,21 @@ __global__ __launch_bounds__(256) void prefix_merge_kernel(PrefixArgs a) {
                   pack_bf16(num[4] * inv, num[5] * inv), pack_bf16(num[6] * inv, num[7] * inv));
 }
 
-template <int D, int KV>
+template <int D, int NG, int KV>
 hipError_t run_prefix(const PrefixArgs& a, const PrefixPlan& p, hipStream_t st) {
   int b_shift = 0;
   while ((1 << b_shift) < a.block_size) ++b_shift;
-  const int wpg = p.n_cblk < kPWavesPerGroup ? p.n_cblk : kPWavesPerGroup;
+  constexpr int WPG = waves_per_group(NG, KV == PA_FP8_E4M3);
+  const int wpg = p.n_cblk < WPG ? p.n_cblk : WPG;
   const int n_cgrp = (p.n_cblk + wpg - 1) / wpg;
   const int groups = a.num_kv_heads * a.n_split * n_cgrp;
   const size_t lds = size_t(wpg) * 2 * kPTile * 2 * D;
   const float scale_log2 = a.scale * kPLog2e;
   if (a.block_size >= kPTile)
-    prefix_partial_kernel<D, true, KV><<<groups, kWave * wpg, lds, st>>>(
+    prefix_partial_kernel<D, NG, true, KV><<<groups, kWave * wpg, lds, st>>>(
         a, b_shift, p.n_cblk, n_cgrp, p.tiles_per_split, scale_log2);
   else
-    prefix_partial_kernel<D, false, KV><<<groups, kWave * wpg, lds, st>>>(
+    prefix_partial_kernel<D, NG, false, KV><<<groups, kWave * wpg, lds, st>>>(
         a, b_shift, p.n_cblk, n_cgrp, p.tiles_per_split, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -308,13 +326,22 @@ hipError_t run_prefix(const PrefixArgs& a, const PrefixPlan& p, hipStream_t st) 
   return hipGetLastError();
 }
 
+template <int D, int KV>
+hipError_t run_prefix_ng(const PrefixArgs& a, const PrefixPlan& p, hipStream_t st) {
+  static_assert(kPMaxGroups == 2, "one instantiation per group count");
+  return p.groups_per_wave == 2 ? run_prefix<D, 2, KV>(a, p, st) : run_prefix<D, 1, KV>(a, p, st);
+}
+
 }  // namespace
 
 PrefixPlan prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t block_size, int32_t num_prefix_blocks, int32_t num_cus) {
   PrefixPlan p{};
   const int64_t cols = int64_t(num_seqs) * (num_q_heads / num_kv_heads);
-  p.n_cblk = int32_t((cols + 15) / 16);
+  // column groups per wave: as many as the columns fill, up to kPMaxGroups
+  p.groups_per_wave = 1;
+  while (p.groups_per_wave < kPMaxGroups && cols >= 32 * p.groups_per_wave) p.groups_per_wave *= 2;
+  p.n_cblk = int32_t((cols + 16 * p.groups_per_wave - 1) / (16 * p.groups_per_wave));
   p.n_tiles = int32_t((int64_t(num_prefix_blocks) * block_size + kPTile - 1) / kPTile);
   if (p.n_tiles <= 0) return p;
   // about four waves per compute unit, but no key range under 8 tiles
@@ -327,20 +354,14 @@ PrefixPlan prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   return p;
 }
 
-hipError_t launch_suffix_lens(const int32_t* seq_lens, int32_t* sfx, int32_t n, int32_t prefix_tokens,
-                              hipStream_t st) {
-  suffix_lens_kernel<<<(n + 255) / 256, 256, 0, st>>>(seq_lens, sfx, n, prefix_tokens);
-  return hipGetLastError();
-}
-
 hipError_t launch_prefix(const PrefixArgs& a, const PrefixPlan& p, hipStream_t st) {
   if (a.n_split != p.n_split || p.n_split <= 0) return hipErrorInvalidValue;
   if (a.dtype == PA_BF16) {
-    if (a.head_dim == 128) return run_prefix<128, PA_BF16>(a, p, st);
-    if (a.head_dim == 64) return run_prefix<64, PA_BF16>(a, p, st);
+    if (a.head_dim == 128) return run_prefix_ng<128, PA_BF16>(a, p, st);
+    if (a.head_dim == 64) return run_prefix_ng<64, PA_BF16>(a, p, st);
   } else if (a.dtype == PA_FP8_E4M3) {
-    if (a.head_dim == 128) return run_prefix<128, PA_FP8_E4M3>(a, p, st);
-    if (a.head_dim == 64) return run_prefix<64, PA_FP8_E4M3>(a, p, st);
+    if (a.head_dim == 128) return run_prefix_ng<128, PA_FP8_E4M3>(a, p, st);
+    if (a.head_dim == 64) return run_prefix_ng<64, PA_FP8_E4M3>(a, p, st);
   }
   return hipErrorInvalidValue;
 }

@@ -169,5 +169,5 @@ def test_shared_prefix_workspace_formula():
     dec = L.pa_decode_workspace_bytes(2, 2, 2, 128, 10)
     assert dec == 2 * 10 * 128 * 4 + 20 * 8 + 10 * 16
     n = L.pa_decode_shared_prefix_workspace_bytes(2, 2, 2, 128, 16, 256, 10)
-    # suffix lengths (2 ints), lse (4 floats), 32 x (m, l) and 32 x 128 floats per row
-    assert n == dec + 16 + 16 + 32 * 4 * 8 + 32 * 4 * 128 * 4
+    # tail lse (4 floats), 32 x (m, l) and 32 x 128 floats per row
+    assert n == dec + 16 + 32 * 4 * 8 + 32 * 4 * 128 * 4
