@@ -319,6 +319,81 @@ def shared_prefix_row(ld, steps, warmup, workers):
                                    "unique bytes over the whole call"}}
 
 
+def mixed_step_inputs(ld):
+    """One scheduler step of a workload with prefill chunks: the chunked
+    sequences give their chunk rows, every other sequence its decode row
+    (decode sequences first)."""
+    import torch
+    wl = ld.wl
+    C = wl.prefill_len
+    pre = [wl.decode_seqs.index(x) for x in wl.prefill_seqs]
+    dec = [i for i in range(len(wl.decode_seqs)) if i not in pre]
+    nd = len(dec)
+    order = torch.tensor(dec + pre, device="cuda")
+    q = torch.cat([ld.q[order[:nd]], ld.p_q]).contiguous()
+    loc = torch.tensor(list(range(nd + 1)) + [nd + C * (j + 1) for j in range(len(pre))],
+                       dtype=torch.int32, device="cuda")
+    lens = torch.cat([ld.lens_d[order[:nd]], ld.p_lens_d]).contiguous()
+    tables = ld.tables_d[order].contiguous()
+    return q, loc, lens, tables, nd, dec
+
+
+def mixed_row(ld, steps, warmup, workers):
+    """pa_attention_mixed on one step of the Llama-2-70B-shaped batch: 248
+    decode rows and 8 prefill chunks of 512 rows, beside the two separate calls."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_316_amd as pkv
+    wl = ld.wl
+    q, loc, lens, tables, nd, dec = mixed_step_inputs(ld)
+    C = wl.prefill_len
+    out = torch.empty_like(q)
+    ws = torch.empty(pkv.decode_workspace_bytes(nd, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                                workers), dtype=torch.uint8, device="cuda")
+    qd, td, lsd = q[:nd].contiguous(), tables[:nd].contiguous(), lens[:nd].contiguous()
+    qp, tp, lsp = q[nd:].contiguous(), tables[nd:].contiguous(), lens[nd:].contiguous()
+    locp = (loc[nd:] - nd).contiguous()
+    dplans = {id(p): pkv.DecodePlan(p, nd, wl.num_q_heads, workers) for p in ld.pools}
+    pout = torch.empty_like(qp)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        def step(i, ev):
+            p = ld.pools[i % len(ld.pools)]
+            if ev is not None:
+                ev[0].record(stream)
+                ev[1].record(stream)
+            fn(p)
+            if ev is not None:
+                ev[2].record(stream)
+        return time_steps(step, steps, warmup)[2]
+
+    m_ms = timed(lambda p: pkv.attention_mixed(q, loc, lens, p, tables, nd, C, wl.scale, workers,
+                                               out=out, workspace=ws))
+    d_ms = timed(lambda p: pkv.decode(qd, p, td, lsd, wl.scale, workers, plan=dplans[id(p)]))
+    p_ms = timed(lambda p: pkv.prefill_chunk(qp, locp, lsp, p, tp, C, wl.scale, out=pout))
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elt_bytes
+    kv_bytes = float(ld.lens[dec].astype("int64").sum()) * per_tok
+    flops = 4.0 * wl.head_dim * wl.num_q_heads * ld.p_keys
+    t = float(m_ms.mean()) * 1e-3
+    t_hbm = kv_bytes / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    rows = nd + len(wl.prefill_seqs) * C
+    return {"workload": WORKLOAD_TEXT[ld.name] + "; one step: the 8 chunked sequences give "
+                        "512-row chunks, the other 248 their decode row",
+            "decode_rows": nd, "prefill_rows": rows - nd, "mixed_us": _stats_us(m_ms),
+            "rows_per_s": round(rows / t, 1),
+            "separate_calls_us": {"decode": _stats_us(d_ms), "prefill": _stats_us(p_ms),
+                                  "sum_mean": round(float(d_ms.mean() + p_ms.mean()) * 1e3, 2)},
+            "decode_kv_bytes": int(kv_bytes), "prefill_flops": flops,
+            "roofline": {"bound": "hbm+mfma", "ideal_us": round(max(t_hbm, t_mfma) * 1e6, 2),
+                         "hbm_us_at_peak": round(t_hbm * 1e6, 2),
+                         "mfma_us_at_peak": round(t_mfma * 1e6, 2),
+                         "frac": round(max(t_hbm, t_mfma) / t, 4),
+                         "note": "ideal = the larger of the decode rows' bytes at 8 TB/s and the "
+                                 "chunks' flops at 2.5 PFLOP/s (perfect overlap)"}}
+
+
 def stream_read_ceiling(gib: int = 4):
     """Best streaming-read rate (GB/s) of pa_probe_stream_read over a few grid sizes."""
     import torch
@@ -389,8 +464,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-rows", action="store_true",
-                    help="skip the Llama-2-70B-shaped GQA decode, chunked-prefill, FP8-KV decode "
-                         "and shared-prefix decode rows")
+                    help="skip the Llama-2-70B-shaped GQA decode, chunked-prefill, mixed-step, "
+                         "FP8-KV decode and shared-prefix decode rows")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -469,6 +544,8 @@ def main():
             g["tokens_per_s_model_equiv"] = round(g["tokens_per_s"] / MODEL_LAYERS["llama70b"], 1)
             g["pct_of_stream_ceiling"] = round(100 * g["decode_kv_gbps"] / ceiling["gbps"], 2)
         rows["prefill_llama70b"] = prefill_row(ld, max(10, args.steps // 10), min(args.warmup, 5))
+        rows["mixed_llama70b_step"] = mixed_row(ld, max(10, args.steps // 10), min(args.warmup, 5),
+                                                args.workers)
         rows["workload_llama70b"] = WORKLOAD_TEXT["llama70b"] + "; prefill: 8 x 512-row causal chunks"
         if args.workload != "llama13b_fp8":
             del ld

@@ -236,6 +236,37 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,
                            int32_t num_seqs, int32_t num_q_heads, int32_t max_q_len,
                            float scale, void* stream);
 
+/*
+ * pa_attention_mixed — one call for a batch that mixes decode sequences and
+ * chunked-prefill sequences, as a scheduler with chunked prefill forms it
+ * ("vLLM PagedAttention explained", section 7.2: a prompt chunk joins the
+ * decode requests of the same step). Every query row attends causally over its
+ * own sequence's paged K/V; the row's position is seq_lens[s] - q_len_s + i.
+ * Sequences 0 .. num_decode-1 are decode sequences with one row each (rows
+ * 0 .. num_decode-1, the pa_decode kernels); sequences num_decode ..
+ * num_decode+num_prefill-1 are prefill chunks (the pa_prefill_chunk kernel).
+ *   out, q       : device, [total_rows][num_q_heads][head_dim], the pool's dtype
+ *                  (bf16 for a PA_FP8_E4M3 pool)
+ *   q_start_loc  : device, int32 [num_decode + num_prefill + 1]; q_start_loc[i]
+ *                  = i for i <= num_decode (only entries num_decode.. are read,
+ *                  and only when num_prefill > 0)
+ *   seq_lens     : device, int32 [num_decode + num_prefill], tokens in the pool
+ *                  for each sequence, its rows of this call included
+ *   block_tables : device, int32 [num_decode + num_prefill][max_blocks_per_seq]
+ *   max_q_len    : host, >= every prefill chunk's row count
+ *   workspace    : device, >= pa_decode_workspace_bytes(num_decode, ...)
+ *                  bytes (unused when num_decode is 0)
+ * Prefill rows need a bf16 pool (PA_ERR_UNSUPPORTED otherwise); decode rows
+ * take every pa_decode dtype. The result of each row is what pa_decode or
+ * pa_prefill_chunk gives for it alone.
+ */
+pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_loc,
+                             const int32_t* seq_lens, const pa_pool* pool,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             int32_t num_decode, int32_t num_prefill, int32_t num_q_heads,
+                             int32_t max_q_len, float scale, int32_t num_workers, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ host --- */
 
 /*

@@ -9,11 +9,11 @@ those calls, and wraps the C++ host block allocator.
 
 from ._lib import (AllocatorStateError, OutOfBlocks, PagedKVError, LIB_PATH, SIGNATURES, lib)
 from .allocator import BlockAllocator
-from .ops import (DecodePlan, KVPool, cache_write, copy_blocks, decode, decode_shared_prefix,
+from .ops import (DecodePlan, KVPool, attention_mixed, cache_write, copy_blocks, decode, decode_shared_prefix,
                   decode_shared_prefix_workspace_bytes, decode_workspace_bytes, prefill_chunk,
                   probe_stream_read)
 
 __all__ = ["AllocatorStateError", "OutOfBlocks", "PagedKVError", "LIB_PATH", "SIGNATURES", "lib",
-           "BlockAllocator", "DecodePlan", "KVPool", "cache_write", "copy_blocks", "decode",
+           "BlockAllocator", "DecodePlan", "KVPool", "attention_mixed", "cache_write", "copy_blocks", "decode",
            "decode_shared_prefix", "decode_shared_prefix_workspace_bytes",
            "decode_workspace_bytes", "prefill_chunk", "probe_stream_read"]

@@ -48,6 +48,9 @@ SIGNATURES = {
     "pa_decode_shared_prefix": (c_int32, [c_void_p, c_void_p, _P(PaPool), c_void_p, c_int32,
                                           c_void_p, c_int32, c_int32, c_float, c_int32, c_int32,
                                           c_void_p, c_size_t, c_void_p]),
+    "pa_attention_mixed": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, _P(PaPool), c_void_p,
+                                     c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_int32,
+                                     c_void_p, c_size_t, c_void_p]),
     "pa_prefill_chunk": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, _P(PaPool), c_void_p,
                                    c_int32, c_int32, c_int32, c_int32, c_float, c_void_p]),
     "pa_alloc_create": (c_int32, [c_int32, c_int32, c_void_p, _P(c_void_p)]),

@@ -82,6 +82,32 @@ PrefixLayout prefix_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
 
 bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// Second stream for work that may overlap the caller's (default priority),
+// with the two events of a fork / join; one set per host thread and device,
+// created on first use and kept until the process ends.
+constexpr int32_t kMixedDecodeWavesPerCU = 3;  // default decode workers beside prefill chunks
+constexpr bool kMixedDecodeFirst = false;      // launch order of the two kernels
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+hipError_t side_stream(SideStream** out) {
+  constexpr int kMaxDevices = 64;
+  thread_local SideStream per_device[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& s = per_device[dev];
+  if (!s.stream) {
+    if ((e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+  }
+  *out = &s;
+  return hipSuccess;
+}
+
 int32_t elt_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
 
 pa_status check_pool(const pa_pool* p, const char* who) {
@@ -357,6 +383,108 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const pa_pool* pool,
   p.k_scale = a.k_scale;
   p.v_scale = a.v_scale;
   return pa::hip_status(pa::launch_prefix(p, lay.plan, st), who);
+}
+
+pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_loc,
+                             const int32_t* seq_lens, const pa_pool* pool,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             int32_t num_decode, int32_t num_prefill, int32_t num_q_heads,
+                             int32_t max_q_len, float scale, int32_t num_workers, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  const char* who = "pa_attention_mixed";
+  if (pa_status s = pa::check_pool(pool, who)) return s;
+  if (num_decode < 0 || num_prefill < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 ||
+      max_q_len < 0)
+    return fail(PA_ERR_INVALID, "%s: bad sizes", who);
+  if (num_decode == 0 && num_prefill == 0) return PA_OK;
+  if (num_prefill > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: num_prefill > 65535", who);
+  if (!out || !q || !seq_lens || !block_tables || (num_prefill > 0 && !q_start_loc))
+    return fail(PA_ERR_INVALID, "%s: NULL pointer argument", who);
+  if (num_q_heads % pool->num_kv_heads)
+    return fail(PA_ERR_INVALID, "%s: num_q_heads=%d not a multiple of num_kv_heads=%d", who,
+                num_q_heads, pool->num_kv_heads);
+  if (!(scale == scale)) return fail(PA_ERR_INVALID, "%s: scale is NaN", who);
+  if (num_workers < 0 || num_workers > (1 << 24))
+    return fail(PA_ERR_INVALID, "%s: num_workers=%d out of range", who, num_workers);
+  if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
+       reinterpret_cast<uintptr_t>(pool->k_pool) | reinterpret_cast<uintptr_t>(pool->v_pool)) & 15)
+    return fail(PA_ERR_INVALID, "%s: out/q/pools must be 16-byte aligned", who);
+  const int32_t G = num_q_heads / pool->num_kv_heads;
+  if (num_prefill > 0 && !pa::prefill_supported(pool->dtype, pool->head_dim, pool->block_size, G))
+    return fail(PA_ERR_UNSUPPORTED, "%s: prefill rows need a bf16 pool (dtype=%d head_dim=%d)",
+                who, pool->dtype, pool->head_dim);
+  if (num_decode > 0 && !pa::decode_supported(pool->dtype, pool->head_dim, G))
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype=%d head_dim=%d group=%d not built", who,
+                pool->dtype, pool->head_dim, G);
+  const bool chunks = num_prefill > 0 && max_q_len > 0;
+  const bool both = chunks && num_decode > 0;
+  // With both kinds of rows, the chunks (bound by the compute units) run on a
+  // second stream beside the decode rows (bound by HBM), joined before return.
+  // The decode then takes fewer waves per compute unit by default, which
+  // leaves each SIMD room for a prefill wave: the two kernels share the chip
+  // instead of queueing behind each other.
+  const int32_t workers =
+      num_workers > 0 ? num_workers : (both ? pa::device_cus() * pa::kMixedDecodeWavesPerCU : 0);
+  const pa::DecodeLayout lay = pa::decode_layout(num_decode > 0 ? num_decode : 1, num_q_heads,
+                                                 pool->num_kv_heads, pool->head_dim, workers);
+  if (num_decode > 0) {
+    if (!workspace || workspace_bytes < lay.total())
+      return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who,
+                  workspace ? workspace_bytes : size_t(0), lay.total());
+    if (reinterpret_cast<uintptr_t>(workspace) & 15)
+      return fail(PA_ERR_INVALID, "%s: workspace must be 16-byte aligned", who);
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  pa::SideStream* side = nullptr;
+  if (both) {
+    if (pa_status s = pa::hip_status(pa::side_stream(&side), who)) return s;
+    if (pa_status s = pa::hip_status(hipEventRecord(side->fork, st), who)) return s;
+    if (pa_status s = pa::hip_status(hipStreamWaitEvent(side->stream, side->fork, 0), who))
+      return s;
+  }
+  auto run_decode = [&]() -> pa_status {  // rows 0 .. num_decode-1, one per sequence
+    const pa::DecodeArgs a = pa::decode_args(out, q, pool, block_tables, max_blocks_per_seq,
+                                             seq_lens, num_decode, num_q_heads, scale, lay,
+                                             workspace);
+    return pa::hip_status(pa::launch_decode(a, st), who);
+  };
+  auto run_chunks = [&]() -> pa_status {
+    // sequences num_decode.. : their rows start at q_start_loc[num_decode]
+    pa::PrefillArgs a{};
+    a.out = out;
+    a.q = q;
+    a.q_start_loc = q_start_loc + num_decode;
+    a.seq_lens = seq_lens + num_decode;
+    a.k_pool = pool->k_pool;
+    a.v_pool = pool->v_pool;
+    a.block_tables = block_tables + int64_t(num_decode) * max_blocks_per_seq;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_seqs = num_prefill;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = pool->num_kv_heads;
+    a.head_dim = pool->head_dim;
+    a.block_size = pool->block_size;
+    a.max_q_len = max_q_len;
+    a.scale = scale;
+    const hipStream_t pst = side ? side->stream : st;
+    if (pa_status s = pa::hip_status(pa::launch_prefill(a, pst), who)) return s;
+    if (side) return pa::hip_status(hipEventRecord(side->join, pst), who);
+    return PA_OK;
+  };
+  if (pa::kMixedDecodeFirst) {
+    if (num_decode > 0)
+      if (pa_status s = run_decode()) return s;
+    if (chunks)
+      if (pa_status s = run_chunks()) return s;
+  } else {
+    if (chunks)
+      if (pa_status s = run_chunks()) return s;
+    if (num_decode > 0)
+      if (pa_status s = run_decode()) return s;
+  }
+  if (side) return pa::hip_status(hipStreamWaitEvent(st, side->join, 0), who);
+  return PA_OK;
 }
 
 pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,

@@ -181,6 +181,37 @@ def decode_shared_prefix(q: torch.Tensor, pool: KVPool, block_tables: torch.Tens
     return out
 
 
+def attention_mixed(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.Tensor,
+                    pool: KVPool, block_tables: torch.Tensor, num_decode: int, max_q_len: int,
+                    scale: float, workers: int = 0, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention for a batch of ``num_decode`` decode sequences (one row each,
+    first) followed by chunked-prefill sequences. q [rows, Hq, D];
+    q_start_loc int32 [S+1] with q_start_loc[i] = i for i <= num_decode."""
+    _need(q, "q", pool.io_dtype)
+    _need(q_start_loc, "q_start_loc", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(block_tables, "block_tables", torch.int32)
+    S = seq_lens.shape[0]
+    if q_start_loc.shape != (S + 1,) or block_tables.shape[0] != S or not 0 <= num_decode <= S:
+        raise ValueError("shape mismatch between q_start_loc, seq_lens, block_tables, num_decode")
+    if q.shape[2] != pool.head_dim:
+        raise ValueError("q head_dim does not match the pool")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", pool.io_dtype)
+    if workspace is None:
+        n = decode_workspace_bytes(max(num_decode, 1), q.shape[1], pool.num_kv_heads,
+                                   pool.head_dim, workers)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    check(lib().pa_attention_mixed(out.data_ptr(), q.data_ptr(), q_start_loc.data_ptr(),
+                                   seq_lens.data_ptr(), ctypes.byref(pool.c),
+                                   block_tables.data_ptr(), block_tables.shape[1], int(num_decode),
+                                   S - int(num_decode), q.shape[1], int(max_q_len), float(scale),
+                                   int(workers), workspace.data_ptr(), workspace.numel(), _stream()))
+    return out
+
+
 def prefill_chunk(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.Tensor,
                   pool: KVPool, block_tables: torch.Tensor, max_q_len: int, scale: float,
                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -202,6 +233,6 @@ def prefill_chunk(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.Te
     return out
 
 
-__all__ = ["KVPool", "DecodePlan", "cache_write", "copy_blocks", "decode",
+__all__ = ["KVPool", "DecodePlan", "attention_mixed", "cache_write", "copy_blocks", "decode",
            "decode_workspace_bytes", "decode_shared_prefix", "decode_shared_prefix_workspace_bytes",
            "prefill_chunk", "PagedKVError"]

@@ -171,3 +171,23 @@ def test_shared_prefix_workspace_formula():
     n = L.pa_decode_shared_prefix_workspace_bytes(2, 2, 2, 128, 16, 256, 10)
     # tail lse (4 floats), 32 x (m, l) and 32 x 128 floats per row
     assert n == dec + 16 + 32 * 4 * 8 + 32 * 4 * 128 * 4
+
+
+def test_mixed_argument_checks():
+    L = lib()
+    p = _pool(num_kv_heads=8)
+    need = L.pa_decode_workspace_bytes(3, 8, 8, 128, 0)
+    f = ctypes.c_float(0.1)
+    call = lambda pool=p, nd=3, npf=2, ws=16, wsb=need, out=16, loc=16, mq=64: \
+        L.pa_attention_mixed(out, 16, loc, 16, ctypes.byref(pool), 16, 4, nd, npf, 8, mq, f, 0, ws,
+                             wsb, None)
+    assert call(nd=0, npf=0, out=None) == 0               # empty batch: no-op
+    assert call(nd=-1) == -1
+    assert call(mq=-1) == -1
+    assert call(out=None) == -1
+    assert call(loc=None) == -1                            # chunks need q_start_loc
+    assert call(ws=None) == -5                             # decode rows need the workspace
+    assert call(wsb=need - 1) == -5
+    fp8 = _pool(num_kv_heads=8, dtype=2)
+    fp8.k_scale, fp8.v_scale = 1.0, 1.0
+    assert call(pool=fp8) == -2 and b"bf16" in L.pa_last_error()  # FP8 chunks: not built
