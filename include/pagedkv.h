@@ -254,11 +254,17 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,
  *                  for each sequence, its rows of this call included
  *   block_tables : device, int32 [num_decode + num_prefill][max_blocks_per_seq]
  *   max_q_len    : host, >= every prefill chunk's row count
- *   workspace    : device, >= pa_decode_workspace_bytes(num_decode, ...)
- *                  bytes (unused when num_decode is 0)
+ *   num_workers  : decode wavefronts; 0 = default (3 per compute unit when the
+ *                  batch also has chunks, else pa_decode's default)
+ *   workspace    : device, pa_decode_workspace_bytes(num_decode, num_q_heads,
+ *                  num_kv_heads, head_dim, num_workers) bytes suffice (unused
+ *                  when num_decode is 0)
+ * With both kinds of rows, the chunks run on a second stream of the library's
+ * (one per host thread and device, default priority) that forks from and joins
+ * back into `stream`, so that the two kernels share the chip.
  * Prefill rows need a bf16 pool (PA_ERR_UNSUPPORTED otherwise); decode rows
- * take every pa_decode dtype. The result of each row is what pa_decode or
- * pa_prefill_chunk gives for it alone.
+ * take every pa_decode dtype. Each row's result is that of pa_decode or
+ * pa_prefill_chunk for it alone (up to the decode's worker count).
  */
 pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_loc,
                              const int32_t* seq_lens, const pa_pool* pool,
