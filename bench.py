@@ -394,6 +394,67 @@ def mixed_row(ld, steps, warmup, workers):
                                  "chunks' flops at 2.5 PFLOP/s (perfect overlap)"}}
 
 
+HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def swap_row(ld, reps=5):
+    """pa_swap_blocks of a preemption-sized batch of blocks (the longest
+    sequences' blocks until 1024 blocks, ~335 MB) out to a pinned host pool and
+    back in, beside one contiguous device<->pinned copy of the same bytes by
+    the copy engine (torch's copy_)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_316_amd as pkv
+    wl = ld.wl
+    tables = ld.tables_d.cpu().numpy()
+    B = wl.block_size
+    blocks = []
+    for i in np.argsort(-ld.lens):
+        blocks += [int(b) for b in tables[i, :-(-int(ld.lens[i]) // B)]]
+        if len(blocks) >= 1024:
+            break
+    blocks = sorted(set(blocks))[:1024]
+    n = len(blocks)
+    pool = ld.pools[0]
+    host = pkv.KVPool.empty_host(n, wl.num_kv_heads, B, wl.head_dim, pool.dtype)
+    out_pairs = np.array([(b, j) for j, b in enumerate(blocks)], dtype=np.int32)
+    in_pairs = out_pairs[:, ::-1].copy()
+    block_bytes = 2 * wl.num_kv_heads * B * wl.head_dim * pool.k.element_size()
+    nbytes = n * block_bytes
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    t_out = timed(lambda: pkv.swap_out(pool, host, out_pairs))
+    t_in = timed(lambda: pkv.swap_in(pool, host, in_pairs))
+    dbuf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    hbuf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    t_d2h = timed(lambda: hbuf.copy_(dbuf, non_blocking=True))
+    t_h2d = timed(lambda: dbuf.copy_(hbuf, non_blocking=True))
+    del dbuf, hbuf, host
+    gbps = lambda ms: round(nbytes / (ms * 1e-3) / 1e9, 2)
+    return {"blocks": n, "bytes": nbytes, "block_bytes": block_bytes,
+            "swap_out_ms": round(t_out, 3), "swap_in_ms": round(t_in, 3),
+            "swap_out_gbps": gbps(t_out), "swap_in_gbps": gbps(t_in),
+            "copy_engine_contiguous_gbps": {"d2h": gbps(t_d2h), "h2d": gbps(t_h2d)},
+            "roofline": {"bound": "host link", "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                         "frac_out": round(gbps(t_out) / HOST_LINK_PEAK_GBPS, 4),
+                         "frac_in": round(gbps(t_in) / HOST_LINK_PEAK_GBPS, 4),
+                         "note": "peak = PCIe 5.0 x16 per direction; the copy engine's contiguous "
+                                 "rate is the practical ceiling"}}
+
+
 def stream_read_ceiling(gib: int = 4):
     """Best streaming-read rate (GB/s) of pa_probe_stream_read over a few grid sizes."""
     import torch
@@ -465,7 +526,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-rows", action="store_true",
                     help="skip the Llama-2-70B-shaped GQA decode, chunked-prefill, mixed-step, "
-                         "FP8-KV decode and shared-prefix decode rows")
+                         "FP8-KV decode, block-swap and shared-prefix decode rows")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -533,6 +594,11 @@ def main():
         result["cpu_baseline"] = None
     if not args.no_extra_rows:
         rows = {}
+        if ld.name == "llama13b":  # block swap of the default batch (before it is released)
+            rows["swap_llama13b"] = swap_row(ld)
+            rows["swap_llama13b"]["workload"] = (
+                "preemption by swapping: the longest sequences' blocks of the LLaMA-13B-shaped "
+                "batch, up to 1024 blocks of 16 tokens x 40 heads x 128, bf16")
         if args.workload != "llama70b":
             del ld
             gc.collect()

@@ -114,6 +114,36 @@ pa_status pa_cache_write(const pa_pool* pool, const void* k_new, const void* v_n
 pa_status pa_copy_blocks(const pa_pool* pool, const int32_t* src_dst, int32_t num_pairs,
                          void* stream);
 
+/* Direction of pa_swap_blocks. */
+enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 };
+
+/*
+ * pa_swap_blocks — move whole blocks between the device pool and a CPU swap
+ * space, the device side of preemption by swapping ("LLM inference engine
+ * internals", sections 3.1 and 3.2: the scheduler's blocks_to_swap_out /
+ * blocks_to_swap_in; "Why PagedAttention multiplies LLM serving throughput",
+ * section "Scheduling and preemption"). One kernel per 256 pairs reads and
+ * writes the host pool across the host link directly (no staging copy).
+ *   device_pool : the pool in device memory
+ *   host_pool   : a pool of the same num_kv_heads, block_size, head_dim, dtype
+ *                 (and FP8 scales) whose k_pool / v_pool are pinned host memory
+ *                 the device can address (hipHostMalloc, or a pinned torch
+ *                 tensor); num_blocks is its own
+ *   src_dst     : HOST, int32 [num_pairs][2] = {src, dst}, read during the
+ *                 call. PA_SWAP_OUT: host[dst] = device[src]; PA_SWAP_IN:
+ *                 device[dst] = host[src]. Every id must lie in its pool and no
+ *                 destination may appear twice (PA_ERR_INVALID otherwise,
+ *                 checked before anything is launched)
+ *   direction   : PA_SWAP_OUT or PA_SWAP_IN
+ * Bit-exact. Asynchronous on `stream`: synchronize it before the host reads a
+ * swapped-out block, and keep the host pool allocated and unchanged until the
+ * stream has passed the call. Memory that HIP does not know as pinned host
+ * memory (e.g. plain malloc) is rejected with PA_ERR_INVALID.
+ */
+pa_status pa_swap_blocks(const pa_pool* device_pool, const pa_pool* host_pool,
+                         const int32_t* src_dst, int32_t num_pairs, int32_t direction,
+                         void* stream);
+
 /*
  * pa_probe_stream_read — measurement aid, not part of the attention path:
  * reads `bytes` of device memory once, with 16-byte non-temporal loads from

@@ -55,5 +55,19 @@ class PoolMirror:
         return self.k[blocks, :, offs, :], self.v[blocks, :, offs, :]
 
 
+def swap(dst: "PoolMirror", src: "PoolMirror", pairs: Iterable[Sequence[int]]) -> None:
+    """Block swapping between two pools of one geometry (a device pool and its
+    CPU swap space): block d of ``dst`` becomes a copy of block s of ``src``
+    for each (s, d), all KV heads, K and V. Preemption by swapping moves a
+    request's blocks out to CPU memory and back ("LLM inference engine
+    internals", section 3.2; "Why PagedAttention multiplies LLM serving
+    throughput", section "Scheduling and preemption"); the scheduler names the
+    moves as blocks_to_swap_in / blocks_to_swap_out ("LLM inference engine
+    internals", section 3.1)."""
+    for s, d in pairs:
+        dst.k[d] = src.k[s]
+        dst.v[d] = src.v[s]
+
+
 def _uint_of(np_dtype):
     return {1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}[np.dtype(np_dtype).itemsize]

@@ -11,9 +11,10 @@ from ._lib import (AllocatorStateError, OutOfBlocks, PagedKVError, LIB_PATH, SIG
 from .allocator import BlockAllocator
 from .ops import (DecodePlan, KVPool, attention_mixed, cache_write, copy_blocks, decode, decode_shared_prefix,
                   decode_shared_prefix_workspace_bytes, decode_workspace_bytes, prefill_chunk,
-                  probe_stream_read)
+                  probe_stream_read, swap_blocks, swap_in, swap_out, PA_SWAP_IN, PA_SWAP_OUT)
 
 __all__ = ["AllocatorStateError", "OutOfBlocks", "PagedKVError", "LIB_PATH", "SIGNATURES", "lib",
            "BlockAllocator", "DecodePlan", "KVPool", "attention_mixed", "cache_write", "copy_blocks", "decode",
            "decode_shared_prefix", "decode_shared_prefix_workspace_bytes",
-           "decode_workspace_bytes", "prefill_chunk", "probe_stream_read"]
+           "decode_workspace_bytes", "prefill_chunk", "probe_stream_read", "swap_blocks", "swap_in",
+           "swap_out", "PA_SWAP_IN", "PA_SWAP_OUT"]

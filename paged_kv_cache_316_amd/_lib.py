@@ -51,6 +51,7 @@ SIGNATURES = {
     "pa_attention_mixed": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, _P(PaPool), c_void_p,
                                      c_int32, c_int32, c_int32, c_int32, c_int32, c_float, c_int32,
                                      c_void_p, c_size_t, c_void_p]),
+    "pa_swap_blocks": (c_int32, [_P(PaPool), _P(PaPool), c_void_p, c_int32, c_int32, c_void_p]),
     "pa_prefill_chunk": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, _P(PaPool), c_void_p,
                                    c_int32, c_int32, c_int32, c_int32, c_float, c_void_p]),
     "pa_alloc_create": (c_int32, [c_int32, c_int32, c_void_p, _P(c_void_p)]),

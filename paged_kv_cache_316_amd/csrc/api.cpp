@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "device.h"
 #include "pagedkv.h"
@@ -233,6 +234,78 @@ pa_status pa_copy_blocks(const pa_pool* pool, const int32_t* src_dst, int32_t nu
     hipError_t e = pa::launch_copy_blocks(*pool, src_dst + 2 * int64_t(off), n,
                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return pa::hip_status(e, "pa_copy_blocks");
+  }
+  return PA_OK;
+}
+
+pa_status pa_swap_blocks(const pa_pool* device_pool, const pa_pool* host_pool,
+                         const int32_t* src_dst, int32_t num_pairs, int32_t direction,
+                         void* stream) {
+  pa::clear_error();
+  const char* who = "pa_swap_blocks";
+  if (pa_status s = pa::check_pool(device_pool, who)) return s;
+  if (pa_status s = pa::check_pool(host_pool, who)) return s;
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return fail(PA_ERR_INVALID, "%s: direction=%d (PA_SWAP_OUT or PA_SWAP_IN)", who, direction);
+  if (host_pool->num_kv_heads != device_pool->num_kv_heads ||
+      host_pool->block_size != device_pool->block_size ||
+      host_pool->head_dim != device_pool->head_dim || host_pool->dtype != device_pool->dtype)
+    return fail(PA_ERR_INVALID, "%s: host and device pools differ in block geometry or dtype", who);
+  if (device_pool->dtype == PA_FP8_E4M3 && (host_pool->k_scale != device_pool->k_scale ||
+                                            host_pool->v_scale != device_pool->v_scale))
+    return fail(PA_ERR_INVALID, "%s: FP8 pools with different scales", who);
+  if (num_pairs < 0) return fail(PA_ERR_INVALID, "%s: num_pairs=%d", who, num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!src_dst) return fail(PA_ERR_INVALID, "%s: src_dst is NULL", who);
+  const bool out = direction == PA_SWAP_OUT;
+  const pa_pool* src = out ? device_pool : host_pool;
+  const pa_pool* dst = out ? host_pool : device_pool;
+  // every id in range and no destination twice (host array, read here)
+  std::vector<unsigned char> taken(size_t(dst->num_blocks), 0);
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    const int32_t s = src_dst[2 * i], d = src_dst[2 * i + 1];
+    if (s < 0 || s >= src->num_blocks || d < 0 || d >= dst->num_blocks)
+      return fail(PA_ERR_INVALID, "%s: pair %d = (%d, %d) outside the pools (%d source, %d "
+                  "destination blocks)", who, i, s, d, src->num_blocks, dst->num_blocks);
+    if (taken[d]) return fail(PA_ERR_INVALID, "%s: destination block %d named twice", who, d);
+    taken[d] = 1;
+  }
+  // the device pool must be device memory, the host pool pinned host memory
+  // that the device can address (hipHostMalloc); its device address is used
+  void* host_k = nullptr;
+  void* host_v = nullptr;
+  for (int which = 0; which < 4; ++which) {
+    const void* ptr = which == 0 ? device_pool->k_pool : which == 1 ? device_pool->v_pool
+                    : which == 2 ? host_pool->k_pool : host_pool->v_pool;
+    hipPointerAttribute_t attr{};
+    const hipError_t e = hipPointerGetAttributes(&attr, ptr);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_INVALID, "%s: %s pool memory unknown to HIP (%s)", who,
+                  which < 2 ? "device" : "host (needs pinned memory)", hipGetErrorString(e));
+    }
+    if (which < 2 && attr.type != hipMemoryTypeDevice)
+      return fail(PA_ERR_INVALID, "%s: device_pool is not device memory", who);
+    if (which >= 2) {
+      if (attr.type != hipMemoryTypeHost || !attr.devicePointer)
+        return fail(PA_ERR_INVALID, "%s: host_pool is not pinned, device-mapped host memory", who);
+      (which == 2 ? host_k : host_v) = attr.devicePointer;
+    }
+  }
+  const int64_t block_bytes = int64_t(device_pool->num_kv_heads) * device_pool->block_size *
+                              device_pool->head_dim * pa::elt_bytes(device_pool->dtype);
+  const void* sk = out ? device_pool->k_pool : host_k;
+  const void* sv = out ? device_pool->v_pool : host_v;
+  void* dk = out ? host_k : device_pool->k_pool;
+  void* dv = out ? host_v : device_pool->v_pool;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int32_t i0 = 0; i0 < num_pairs; i0 += pa::kSwapBatch) {
+    const int32_t n = num_pairs - i0 < pa::kSwapBatch ? num_pairs - i0 : pa::kSwapBatch;
+    pa::SwapBatch b{};
+    std::memcpy(b.pairs, src_dst + 2 * i0, sizeof(int32_t) * 2 * n);
+    if (pa_status s = pa::hip_status(pa::launch_swap_blocks(b, n, sk, sv, dk, dv, block_bytes, st),
+                                     who))
+      return s;
   }
   return PA_OK;
 }

@@ -90,6 +90,43 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
   }
 }
 
+// Block swap between the device pool and a pool in pinned host memory: one
+// launch moves up to kSwapBatch blocks, whose (src, dst) ids travel in the
+// kernel arguments (checked on the host). grid.y = pair; 4 independent 16-byte
+// chunks per thread keep many transfers across the host link in flight.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    SwapBatch b, const uint4* __restrict__ src_k, const uint4* __restrict__ src_v,
+    uint4* __restrict__ dst_k, uint4* __restrict__ dst_v, int64_t chunks_per_block) {
+  constexpr int U = 4;
+  const int64_t src = b.pairs[2 * blockIdx.y];
+  const int64_t dst = b.pairs[2 * blockIdx.y + 1];
+  const uint4* ks = src_k + src * chunks_per_block;
+  const uint4* vs = src_v + src * chunks_per_block;
+  uint4* kd = dst_k + dst * chunks_per_block;
+  uint4* vd = dst_v + dst * chunks_per_block;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i0 < chunks_per_block;
+       i0 += U * stride) {
+    uint4 k[U], v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < chunks_per_block) {
+        k[u] = ks[i];
+        v[u] = vs[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < chunks_per_block) {
+        kd[i] = k[u];
+        vd[i] = v[u];
+      }
+    }
+  }
+}
+
 int elt_bytes(int dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
 
 }  // namespace
@@ -138,6 +175,18 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, int grid, uint32_t*
                               hipStream_t stream) {
   stream_read_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint4*>(buf),
                                                int64_t(bytes / 16), sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(const SwapBatch& b, int32_t n, const void* src_k, const void* src_v,
+                              void* dst_k, void* dst_v, int64_t block_bytes, hipStream_t stream) {
+  if (n <= 0 || n > kSwapBatch || block_bytes % 16) return hipErrorInvalidValue;
+  const int64_t cpb = block_bytes / 16;
+  const int64_t want = (cpb + 4 * 256 - 1) / (4 * 256);
+  const int gx = int(want < 64 ? want : 64);
+  swap_blocks_kernel<<<dim3(gx, n), 256, 0, stream>>>(
+      b, static_cast<const uint4*>(src_k), static_cast<const uint4*>(src_v),
+      static_cast<uint4*>(dst_k), static_cast<uint4*>(dst_v), cpb);
   return hipGetLastError();
 }
 

@@ -114,6 +114,15 @@ hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void
                               const int64_t* slots, int32_t T, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int grid, uint32_t* sink,
                               hipStream_t stream);
+constexpr int kSwapBatch = 256;  // block pairs per swap launch (kernel argument size)
+struct SwapBatch {
+  int32_t pairs[2 * kSwapBatch];  // (src, dst) block ids, checked on the host
+};
+// Copies n <= kSwapBatch whole blocks (block_bytes per block, K and V) from
+// the src pool to the dst pool; either side may be pinned host memory given
+// by its device-accessible address.
+hipError_t launch_swap_blocks(const SwapBatch& b, int32_t n, const void* src_k, const void* src_v,
+                              void* dst_k, void* dst_v, int64_t block_bytes, hipStream_t stream);
 hipError_t launch_copy_blocks(const pa_pool& pool, const int32_t* src_dst, int32_t n,
                               hipStream_t stream);
 // Returns hipErrorInvalidValue for shapes without a compiled kernel.

@@ -40,13 +40,16 @@ class KVPool:
     (V likewise). New K/V are written, and queries and outputs given, in bfloat16."""
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, k_scale: float = 1.0,
-                 v_scale: float = 1.0):
+                 v_scale: float = 1.0, host: bool = False):
         if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
             raise ValueError("k and v pools must be 4-D with equal shape and dtype")
         if k.dtype not in _DTYPES:
             raise ValueError(f"pool dtype {k.dtype} not supported")
-        _need(k, "k_pool")
-        _need(v, "v_pool")
+        _need(k, "k_pool", device=not host)
+        _need(v, "v_pool", device=not host)
+        if host and not (k.is_pinned() and v.is_pinned()):
+            raise ValueError("a host pool (swap space) must be pinned host memory")
+        self.host = host
         self.k, self.v = k, v
         nb, h, b, d = k.shape
         self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim = nb, h, b, d
@@ -66,6 +69,14 @@ class KVPool:
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
         return cls(torch.empty(shape, dtype=dtype, device=device),
                    torch.empty(shape, dtype=dtype, device=device), k_scale, v_scale)
+
+    @classmethod
+    def empty_host(cls, num_blocks, num_kv_heads, block_size, head_dim, dtype,
+                   k_scale: float = 1.0, v_scale: float = 1.0):
+        """A CPU swap space: a pool in pinned host memory the device can address."""
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        return cls(torch.empty(shape, dtype=dtype, pin_memory=True),
+                   torch.empty(shape, dtype=dtype, pin_memory=True), k_scale, v_scale, host=True)
 
     @property
     def kv_bytes_per_token(self) -> int:
@@ -92,6 +103,36 @@ def copy_blocks(pool: KVPool, src_dst: torch.Tensor) -> None:
     if src_dst.numel() and tuple(src_dst.shape) != (n, 2):
         raise ValueError("src_dst must be [n, 2]")
     check(lib().pa_copy_blocks(ctypes.byref(pool.c), _ptr(src_dst), n, _stream()))
+
+
+PA_SWAP_OUT, PA_SWAP_IN = 0, 1
+
+
+def swap_blocks(device_pool: KVPool, host_pool: KVPool, pairs, direction: int) -> None:
+    """Move whole blocks between the device pool and a pinned host pool.
+    pairs: host int32 [n, 2] of (src, dst); PA_SWAP_OUT copies device -> host,
+    PA_SWAP_IN host -> device. Asynchronous on the current stream."""
+    import numpy as np
+    if device_pool.host or not host_pool.host:
+        raise ValueError("swap_blocks takes a device pool and a host pool")
+    if isinstance(pairs, torch.Tensor):
+        if pairs.is_cuda:
+            raise ValueError("pairs must be host memory")
+        pairs = pairs.numpy()
+    arr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    check(lib().pa_swap_blocks(ctypes.byref(device_pool.c), ctypes.byref(host_pool.c),
+                               arr.ctypes.data if arr.size else None, arr.shape[0], int(direction),
+                               _stream()))
+
+
+def swap_out(device_pool: KVPool, host_pool: KVPool, pairs) -> None:
+    """host_pool[dst] = device_pool[src] for each (src, dst)."""
+    swap_blocks(device_pool, host_pool, pairs, PA_SWAP_OUT)
+
+
+def swap_in(device_pool: KVPool, host_pool: KVPool, pairs) -> None:
+    """device_pool[dst] = host_pool[src] for each (src, dst)."""
+    swap_blocks(device_pool, host_pool, pairs, PA_SWAP_IN)
 
 
 def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, grid: int = 0) -> None:
@@ -235,4 +276,5 @@ def prefill_chunk(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.Te
 
 __all__ = ["KVPool", "DecodePlan", "attention_mixed", "cache_write", "copy_blocks", "decode",
            "decode_workspace_bytes", "decode_shared_prefix", "decode_shared_prefix_workspace_bytes",
-           "prefill_chunk", "PagedKVError"]
+           "prefill_chunk", "swap_blocks", "swap_in", "swap_out", "PA_SWAP_IN", "PA_SWAP_OUT",
+           "PagedKVError"]

@@ -192,3 +192,30 @@ def test_mixed_argument_checks():
     fp8 = _pool(num_kv_heads=8, dtype=2)
     fp8.k_scale, fp8.v_scale = 1.0, 1.0
     assert call(pool=fp8) == -2 and b"bf16" in L.pa_last_error()  # FP8 chunks: not built
+
+
+def test_swap_argument_checks():
+    L = lib()
+    dev = _pool(num_blocks=4)
+    host = _pool(num_blocks=6)
+    pairs = lambda *ps: (ctypes.c_int32 * (2 * len(ps)))(*[x for p in ps for x in p])
+    call = lambda d=dev, h=host, pr=pairs((0, 5), (3, 1)), n=2, dirn=0: \
+        L.pa_swap_blocks(ctypes.byref(d), ctypes.byref(h), pr, n, dirn, None)
+    assert call(n=0, pr=None) == 0                                  # nothing to move
+    assert call(dirn=2) == -1 and b"direction" in L.pa_last_error()
+    assert call(h=_pool(num_blocks=6, head_dim=64)) == -1             # geometry differs
+    assert call(h=_pool(num_blocks=6, dtype=0)) == -1                 # dtype differs
+    assert call(pr=None) == -1
+    assert call(pr=pairs((0, 6), (3, 1))) == -1 and b"outside" in L.pa_last_error()  # host id 6
+    assert call(pr=pairs((4, 0), (3, 1))) == -1                       # device id 4
+    # swap in: sources are host ids (0..5), destinations device ids (0..3)
+    assert call(pr=pairs((5, 4)), n=1, dirn=1) == -1 and b"outside" in L.pa_last_error()
+    assert call(pr=pairs((5, 3), (4, 1)), dirn=1) == -1 and b"pool memory" in L.pa_last_error()
+    assert call(pr=pairs((0, 5), (3, 5))) == -1 and b"twice" in L.pa_last_error()
+    # fp8 pools must agree on their scales
+    d8, h8 = _pool(dtype=2), _pool(dtype=2, num_blocks=6)
+    d8.k_scale = d8.v_scale = h8.k_scale = 1.0
+    h8.v_scale = 2.0
+    assert call(d=d8, h=h8) == -1 and b"scale" in L.pa_last_error()
+    # past the host checks the pointers are looked up: fake addresses are refused
+    assert call() == -1 and b"pool memory" in L.pa_last_error()
