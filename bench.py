@@ -256,6 +256,41 @@ def prefill_step_fn(ld):
     return step
 
 
+def unique_kv_bytes(ld):
+    """Bytes of the distinct physical blocks the batch reads (each block's
+    filled tokens once), against the logical bytes of the per-sequence reads."""
+    import numpy as np
+    wl = ld.wl
+    B = wl.block_size
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elt_bytes
+    tables = ld.tables_d.cpu().numpy()
+    filled = {}
+    for i, L in enumerate(ld.lens):
+        L = int(L)
+        for j in range(-(-L // B)):
+            b = int(tables[i, j])
+            filled[b] = max(filled.get(b, 0), min(B, L - j * B))
+    return float(sum(filled.values())) * per_tok
+
+
+def shared_block_row(ld, steps, warmup, workers):
+    """Plain decode of a batch with shared blocks: logical and unique bytes."""
+    row = decode_row(ld, steps, warmup, workers)
+    uniq = unique_kv_bytes(ld)
+    t = row["decode_us"]["mean"] * 1e-6
+    return {"workload": WORKLOAD_TEXT[ld.name], "num_seqs": len(ld.wl.decode_seqs),
+            "ms_per_step": row["ms_per_step"], "tokens_per_s": row["tokens_per_s"],
+            "decode_us": row["decode_us"], "logical_kv_bytes": int(ld.kv_bytes),
+            "unique_kv_bytes": int(uniq), "shared_read_share": round(1 - uniq / ld.kv_bytes, 4),
+            "logical_kv_gbps": round(ld.kv_bytes / t / 1e9, 2),
+            "unique_kv_gbps": round(uniq / t / 1e9, 2),
+            "roofline": {"bound": "hbm", "achieved": round(uniq / t / 1e9, 2),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(uniq / t / 1e9 / HBM_PEAK_GBPS, 4),
+                         "note": "achieved on unique physical bytes (re-reads of shared "
+                                 "blocks hit the caches)"}}
+
+
 def shared_prefix_blocks(ld):
     """Blocks every table row starts with (the prefix-cache hits), checked on the host."""
     wl = ld.wl
@@ -310,7 +345,9 @@ def shared_prefix_row(ld, steps, warmup, workers):
             "logical_kv_bytes": int(ld.kv_bytes), "unique_kv_bytes": int(unique),
             "logical_kv_gbps": round(ld.kv_bytes / t / 1e9, 2),
             "plain_decode": {"ms_per_step": plain["ms_per_step"], "decode_us": plain["decode_us"],
-                             "logical_kv_gbps": plain["decode_kv_gbps"]},
+                             "logical_kv_gbps": plain["decode_kv_gbps"],
+                             "unique_kv_gbps": round(unique / (plain["decode_us"]["mean"] * 1e-6)
+                                                     / 1e9, 2)},
             "speedup_vs_plain_decode": round(plain["decode_us"]["mean"] / (t * 1e6), 3),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -526,7 +563,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-rows", action="store_true",
                     help="skip the Llama-2-70B-shaped GQA decode, chunked-prefill, mixed-step, "
-                         "FP8-KV decode, block-swap and shared-prefix decode rows")
+                         "FP8-KV decode, block-swap, shared-block and shared-prefix decode rows")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -623,6 +660,13 @@ def main():
             f["tokens_per_s_model_equiv"] = round(f["tokens_per_s"] / MODEL_LAYERS["llama13b_fp8"], 1)
             f["pct_of_stream_ceiling"] = round(100 * f["decode_kv_gbps"] / ceiling["gbps"], 2)
             f["workload"] = WORKLOAD_TEXT["llama13b_fp8"]
+        for name in ("cow", "cow504", "beam"):  # shared blocks, plain decode
+            del ld
+            gc.collect()
+            torch.cuda.empty_cache()
+            ld = Loaded(name, args.replicas)
+            rows[f"decode_{name}"] = shared_block_row(ld, max(20, args.steps // 4), args.warmup,
+                                                      args.workers)
         if ld.name != "prefix":
             del ld
             gc.collect()

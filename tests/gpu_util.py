@@ -83,8 +83,11 @@ def assert_close(wl, got: np.ndarray, want: np.ndarray, what: str = "") -> dict:
     stats = dict(max_abs=float(err.max(initial=0.0)),
                  max_rel=float((err / np.maximum(np.abs(want), 1e-30)).max(initial=0.0)))
     if wl.dtype == "f32":
+        stats["bar_frac"] = stats["max_abs"] / F32_ATOL
         assert stats["max_abs"] <= F32_ATOL, f"{what}: {stats}"
     else:
-        bad = err > BF16_ATOL + BF16_RTOL * np.abs(want)
+        bar = BF16_ATOL + BF16_RTOL * np.abs(want)
+        stats["bar_frac"] = float((err / bar).max(initial=0.0))  # worst element's share of its bar
+        bad = err > bar
         assert not bad.any(), f"{what}: {int(bad.sum())} elements out of tolerance, {stats}"
     return stats
