@@ -59,6 +59,7 @@ def log(msg):
 KERNEL_SOURCES = {
     "decode": ("decode.hip", "cache_ops.hip", "device.h"),
     "prefill": ("prefill.hip", "device.h"),
+    "prefix_shared": ("prefix.hip", "decode.hip", "device.h"),
 }
 
 
@@ -351,7 +352,7 @@ def shared_prefix_row(ld, steps, warmup, workers):
             "speedup_vs_plain_decode": round(plain["decode_us"]["mean"] / (t * 1e6), 3),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                         "traffic": None,
+                         "traffic": load_traffic(ld.name, "prefix_shared"),
                          "kernel": "pa_decode_shared_prefix (suffix decode + prefix MFMA pass + merge), "
                                    "unique bytes over the whole call"}}
 
@@ -518,8 +519,10 @@ def stream_read_ceiling(gib: int = 4):
             "kernel": "pa_probe_stream_read (16-byte non-temporal loads, 4 in flight per lane)"}
 
 
-def decode_row(ld, steps, warmup, workers):
-    ms_step, w_ms, d_ms = time_steps(decode_step_fn(ld, workers), steps, warmup)
+def decode_row(ld, steps, warmup, workers, path="plain"):
+    step = (decode_step_fn(ld, workers) if path == "plain"
+            else shared_prefix_step_fn(ld, workers, shared_prefix_blocks(ld)))
+    ms_step, w_ms, d_ms = time_steps(step, steps, warmup)
     S = len(ld.wl.decode_seqs)
     achieved = ld.kv_bytes / (float(d_ms.mean()) * 1e-3) / 1e9
     return {"ms_per_step": round(ms_step, 5),
@@ -530,8 +533,9 @@ def decode_row(ld, steps, warmup, workers):
             "kv_bytes_per_step": int(ld.kv_bytes), "tokens": int(ld.lens.sum()),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                         "traffic": load_traffic(ld.name),
-                         "kernel": "pa_decode (balanced split kernel + LSE combine kernel)"}}
+                         "traffic": load_traffic(ld.name) if path == "plain" else None,
+                         "kernel": "pa_decode (balanced split kernel + LSE combine kernel)"
+                                   if path == "plain" else "pa_decode_shared_prefix (logical bytes)"}}
 
 
 def prefill_row(ld, steps, warmup):
@@ -564,6 +568,12 @@ def main():
     ap.add_argument("--no-extra-rows", action="store_true",
                     help="skip the Llama-2-70B-shaped GQA decode, chunked-prefill, mixed-step, "
                          "FP8-KV decode, block-swap, shared-block and shared-prefix decode rows")
+    ap.add_argument("--rows", default="",
+                    help="comma-separated extra rows to run (default: all), e.g. "
+                         "prefill_llama70b,swap_llama13b")
+    ap.add_argument("--decode-path", default="plain", choices=("plain", "shared-prefix"),
+                    help="entry point the main row times: pa_decode, or pa_decode_shared_prefix "
+                         "(prefix workload only)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -588,7 +598,10 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    row = decode_row(ld, args.steps, args.warmup, args.workers)
+    if args.decode_path == "shared-prefix" and args.workload != "prefix":
+        print("--decode-path shared-prefix needs --workload prefix", file=sys.stderr)
+        sys.exit(2)
+    row = decode_row(ld, args.steps, args.warmup, args.workers, args.decode_path)
     ceiling = stream_read_ceiling()
     wl = ld.wl
     S = len(wl.decode_seqs)
@@ -609,7 +622,8 @@ def main():
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "block_size": wl.block_size, "tokens": row["tokens"],
                    "kv_bytes_per_step": row["kv_bytes_per_step"], "pool_replicas": args.replicas,
-                   "accumulation": "fp32", "decode_workers": args.workers or "default (8 per CU)"},
+                   "accumulation": "fp32", "decode_workers": args.workers or "default (8 per CU)",
+                   "decode_path": args.decode_path},
         "pct_hbm_peak": round(100 * row["kv_gbps_step"] / HBM_PEAK_GBPS, 2),
         "tokens_per_s": row["tokens_per_s"],
         "tokens_per_s_model_equiv": {"layers": MODEL_LAYERS[args.workload],
@@ -630,50 +644,56 @@ def main():
     else:
         result["cpu_baseline"] = None
     if not args.no_extra_rows:
+        wanted = set(args.rows.split(",")) if args.rows else None
         rows = {}
-        if ld.name == "llama13b":  # block swap of the default batch (before it is released)
+
+        def want(name):
+            return wanted is None or name in wanted
+
+        def switch(name, replicas=args.replicas):
+            nonlocal ld
+            if ld is not None and ld.name == name:
+                return
+            ld = None
+            gc.collect()
+            torch.cuda.empty_cache()
+            ld = Loaded(name, replicas)
+
+        short = max(20, args.steps // 4)
+        if want("swap_llama13b"):
+            switch("llama13b", 1)
             rows["swap_llama13b"] = swap_row(ld)
             rows["swap_llama13b"]["workload"] = (
                 "preemption by swapping: the longest sequences' blocks of the LLaMA-13B-shaped "
                 "batch, up to 1024 blocks of 16 tokens x 40 heads x 128, bf16")
-        if args.workload != "llama70b":
-            del ld
-            gc.collect()
-            torch.cuda.empty_cache()
-            ld = Loaded("llama70b", args.replicas)
-            rows["decode_llama70b_gqa"] = decode_row(ld, max(20, args.steps // 4), args.warmup,
-                                                    args.workers)
-            g = rows["decode_llama70b_gqa"]
+        if want("decode_llama70b_gqa") and args.workload != "llama70b":
+            switch("llama70b")
+            g = rows["decode_llama70b_gqa"] = decode_row(ld, short, args.warmup, args.workers)
             g["tokens_per_s_model_equiv"] = round(g["tokens_per_s"] / MODEL_LAYERS["llama70b"], 1)
             g["pct_of_stream_ceiling"] = round(100 * g["decode_kv_gbps"] / ceiling["gbps"], 2)
-        rows["prefill_llama70b"] = prefill_row(ld, max(10, args.steps // 10), min(args.warmup, 5))
-        rows["mixed_llama70b_step"] = mixed_row(ld, max(10, args.steps // 10), min(args.warmup, 5),
-                                                args.workers)
-        rows["workload_llama70b"] = WORKLOAD_TEXT["llama70b"] + "; prefill: 8 x 512-row causal chunks"
-        if args.workload != "llama13b_fp8":
-            del ld
-            gc.collect()
-            torch.cuda.empty_cache()
-            ld = Loaded("llama13b_fp8", args.replicas)
-            f = rows["decode_llama13b_fp8"] = decode_row(ld, max(20, args.steps // 4), args.warmup,
-                                                        args.workers)
+        if want("prefill_llama70b"):
+            switch("llama70b")
+            rows["prefill_llama70b"] = prefill_row(ld, max(10, args.steps // 10),
+                                                   min(args.warmup, 5))
+            rows["workload_llama70b"] = (WORKLOAD_TEXT["llama70b"] +
+                                         "; prefill: 8 x 512-row causal chunks")
+        if want("mixed_llama70b_step"):
+            switch("llama70b")
+            rows["mixed_llama70b_step"] = mixed_row(ld, max(10, args.steps // 10),
+                                                    min(args.warmup, 5), args.workers)
+        if want("decode_llama13b_fp8") and args.workload != "llama13b_fp8":
+            switch("llama13b_fp8")
+            f = rows["decode_llama13b_fp8"] = decode_row(ld, short, args.warmup, args.workers)
             f["tokens_per_s_model_equiv"] = round(f["tokens_per_s"] / MODEL_LAYERS["llama13b_fp8"], 1)
             f["pct_of_stream_ceiling"] = round(100 * f["decode_kv_gbps"] / ceiling["gbps"], 2)
             f["workload"] = WORKLOAD_TEXT["llama13b_fp8"]
         for name in ("cow", "cow504", "beam"):  # shared blocks, plain decode
-            del ld
-            gc.collect()
-            torch.cuda.empty_cache()
-            ld = Loaded(name, args.replicas)
-            rows[f"decode_{name}"] = shared_block_row(ld, max(20, args.steps // 4), args.warmup,
-                                                      args.workers)
-        if ld.name != "prefix":
-            del ld
-            gc.collect()
-            torch.cuda.empty_cache()
-            ld = Loaded("prefix", args.replicas)
-        rows["decode_prefix_shared"] = shared_prefix_row(ld, max(20, args.steps // 4), args.warmup,
-                                                         args.workers)
+            if want(f"decode_{name}"):
+                switch(name)
+                rows[f"decode_{name}"] = shared_block_row(ld, short, args.warmup, args.workers)
+        if want("decode_prefix_shared"):
+            switch("prefix")
+            rows["decode_prefix_shared"] = shared_prefix_row(ld, short, args.warmup, args.workers)
         result["rows"] = rows
     print(json.dumps(result), flush=True)
 
