@@ -45,7 +45,10 @@ DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
                            int32_t head_dim, int32_t workers) {
   DecodeLayout d{};
   d.workers = workers > 0 ? workers : default_workers();
-  d.heads_per_unit = decode_heads_per_unit(num_q_heads / num_kv_heads);
+  // partial slots are sized for the largest unit a launch may use: FP8 MHA
+  // pools pair KV heads (2 heads per unit), which dtype-free sizing covers
+  const int32_t G = num_q_heads / num_kv_heads;
+  d.heads_per_unit = G == 1 ? 2 : decode_heads_per_unit(G);
   d.units = num_q_heads / d.heads_per_unit;
   const size_t slots = size_t(2) * d.workers * d.heads_per_unit;
   d.acc_bytes = slots * head_dim * 4;

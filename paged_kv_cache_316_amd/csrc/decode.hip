@@ -136,7 +136,7 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 }
 
 // Position of one tile in the work list: tile j of segment (sequence s, unit u);
-// unit u reads KV head kvh; the sequence has n tiles and L tokens; seg0 = list
+// unit u reads KV heads kvh .. kvh+kvp-1; the sequence has n tiles and L tokens; seg0 = list
 // index of the segment's tile 0. All fields are wave-uniform.
 struct Cursor {
   int s, u, kvh, hc, j, n, L;
@@ -156,11 +156,11 @@ __device__ __forceinline__ int len_of(const DecodeArgs& a, int s) {
 
 template <int D, int VEC, class Begin, class Run, class End>
 __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane, int n_hchunk,
-                                           int hpw, Begin begin, Run run, End end) {
+                                           int hpw, int kvp, Begin begin, Run run, End end) {
   const int S = a.num_seqs;
   const int Hq = a.num_q_heads;
   const int G = Hq / a.num_kv_heads;
-  const int units = a.num_kv_heads * n_hchunk;
+  const int units = (a.num_kv_heads / kvp) * n_hchunk;
 
   int64_t total = 0;
   for (int base = 0; base < S; base += kWave) {
@@ -215,8 +215,8 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
         const int64_t off = g_begin - seq0;
         cur.u = int(off / cur.n);
         cur.j = int(off - int64_t(cur.u) * cur.n);
-        cur.kvh = cur.u / n_hchunk;
-        cur.hc = cur.u - cur.kvh * n_hchunk;
+        cur.kvh = (cur.u / n_hchunk) * kvp;
+        cur.hc = cur.u % n_hchunk;
         cur.seg0 = seq0 + int64_t(cur.u) * cur.n;
         break;
       }
@@ -247,7 +247,7 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
     ++cur.u;
     if (++cur.hc == n_hchunk) {
       cur.hc = 0;
-      ++cur.kvh;
+      cur.kvh += kvp;
     }
     if (cur.u == units) {
       cur.u = cur.kvh = cur.hc = 0;
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
     }
   };
 
-  walk_slice<D, VEC>(a, w, lane, n_hchunk, HPW, begin_segment, run_tiles, end_segment);
+  walk_slice<D, VEC>(a, w, lane, n_hchunk, HPW, 1, begin_segment, run_tiles, end_segment);
 }
 
 // GQA decode on the matrix cores (bf16, HPW >= 4 query heads per KV head).
@@ -485,7 +485,13 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
 // KV = PA_BF16, or PA_FP8_E4M3: the pool holds E4M3 codes, which are widened
 // exactly to bf16 on their way into LDS; k_scale then multiplies the scores and
 // v_scale the output, and everything from LDS on is the bf16 kernel.
-template <int D, int HPW, bool BIG_B, int KV>
+// KVP = 2 (MHA, HPW = 2): a unit is two consecutive KV heads with their one
+// query head each. Column c of the MFMA tiles is head kvh + c and is scored
+// against, and weights, that head's own K and V tiles. The two heads' rows of a
+// block are adjacent in the pool, so each tile reads one contiguous run of
+// 2*16 rows per pool instead of two of 16: with FP8 rows (128 B) a 16-row run
+// is only 2 KB, and the memory system serves such short runs much more slowly.
+template <int D, int HPW, bool BIG_B, int KV, int KVP>
 __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
   constexpr bool FP8 = KV == PA_FP8_E4M3;
@@ -496,12 +502,14 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   constexpr int CPR = ROW / 16;     // 16-byte chunks per LDS row
   constexpr int GCPR = GROW / 16;   // 16-byte chunks per pool row
   constexpr int RPI = 1024 / GROW;  // rows per wave-wide 16-byte load
-  constexpr int NI = kTile / RPI;   // loads per lane per tile, for K and for V
+  constexpr int NI = kTile / RPI;   // loads per lane per tile and KV head, for K and for V
+  constexpr int NIT = NI * KVP;     // loads per lane per tile, for K and for V
+  static_assert(KVP == 1 || HPW == KVP, "paired KV heads carry one query head each");
   constexpr int RPL = 256 / ROW;    // rows per 256-byte LDS bank line
   constexpr int TB = kTile * ROW;   // bytes of one K or V tile in LDS
   // tiles in flight per wave: an FP8 tile is half the bytes, so more of them
-  // are needed to keep as many bytes in flight
-  constexpr int NB = FP8 ? 4 : 2;
+  // are needed to keep as many bytes in flight (a paired tile is twice the bytes)
+  constexpr int NB = FP8 && KVP == 1 ? 4 : 2;
   static_assert(HPW <= 16, "one MFMA N tile holds the unit's heads");
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -514,8 +522,9 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   const int B = a.block_size, Bm1 = B - 1;
   if (w >= a.workers) return;
 
-  unsigned char* kt_lds = smem + wig * (2 * TB);  // this wave's K tile, then its V tile
-  unsigned char* vt = kt_lds + TB;
+  // this wave's K tiles (one per KV head of the unit), then its V tiles
+  unsigned char* kt_lds = smem + wig * (2 * KVP * TB);
+  unsigned char* vt = kt_lds + KVP * TB;
   auto swz = [](int r) { return (r / RPL) % CPR; };
   // load u of lane l: row u*RPI + l/GCPR, pool chunk l%GCPR; in LDS that is
   // chunk l%GCPR of the bf16 row (two chunks, 2c and 2c+1, for FP8 codes)
@@ -539,7 +548,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   const int64_t block_bytes = int64_t(Hkv) * B * GROW;
 
   uint4 qop[KS];
-  f32x4_t o[DT];
+  f32x4_t o[KVP][DT];
   float m, lpart;
   const float c2 = FP8 ? scale_log2 * a.k_scale : scale_log2;
   const float vsc = FP8 ? a.v_scale : 1.f;
@@ -554,7 +563,9 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
       qop[ks] = i16 < HPW ? qv : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < KVP; ++p)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[p][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m = -INFINITY;
     lpart = 0.f;
   };
@@ -563,27 +574,38 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     // tiles -> LDS (the previous tile's reads were issued earlier by this
     // wave, and LDS serves one wave's accesses in order)
 #pragma unroll
-    for (int u = 0; u < NI; ++u) {
+    for (int ut = 0; ut < NIT; ++ut) {
+      const int u = ut % NI;
+      unsigned char* kd = kt_lds + (ut / NI) * TB;  // tile of KV head ut / NI
+      unsigned char* vd = vt + (ut / NI) * TB;
       if constexpr (FP8) {
         uint4 k0, k1, v0, v1;
-        widen_e4m3(kr[u], k0, k1);
-        widen_e4m3(vr[u], v0, v1);
-        *reinterpret_cast<uint4*>(kt_lds + wr[u]) = k0;
-        *reinterpret_cast<uint4*>(kt_lds + wr2[u]) = k1;
-        *reinterpret_cast<uint4*>(vt + wr[u]) = v0;
-        *reinterpret_cast<uint4*>(vt + wr2[u]) = v1;
+        widen_e4m3(kr[ut], k0, k1);
+        widen_e4m3(vr[ut], v0, v1);
+        *reinterpret_cast<uint4*>(kd + wr[u]) = k0;
+        *reinterpret_cast<uint4*>(kd + wr2[u]) = k1;
+        *reinterpret_cast<uint4*>(vd + wr[u]) = v0;
+        *reinterpret_cast<uint4*>(vd + wr2[u]) = v1;
       } else {
-        *reinterpret_cast<uint4*>(kt_lds + wr[u]) = kr[u];
-        *reinterpret_cast<uint4*>(vt + wr[u]) = vr[u];
+        *reinterpret_cast<uint4*>(kd + wr[u]) = kr[ut];
+        *reinterpret_cast<uint4*>(vd + wr[u]) = vr[ut];
       }
     }
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t scp[KVP];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 kop = *reinterpret_cast<const uint4*>(kt_lds + (kr0 ^ (64u * ks)));
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop),
-                                                  __builtin_bit_cast(bf16x8_t, qop[ks]), sc, 0, 0, 0);
+    for (int p = 0; p < KVP; ++p) {
+      scp[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 kop = *reinterpret_cast<const uint4*>(kt_lds + p * TB + (kr0 ^ (64u * ks)));
+        scp[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop),
+                                                        __builtin_bit_cast(bf16x8_t, qop[ks]),
+                                                        scp[p], 0, 0, 0);
+      }
     }
+    // column i16 is scored against the K tile of its own KV head
+    f32x4_t sc = scp[0];
+    if constexpr (KVP == 2) sc = i16 == 1 ? scp[1] : scp[0];
     const int key0 = j * kTile + 4 * g;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -612,21 +634,30 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     lpart = lpart * alpha + ps;
     if (__ballot(moved)) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
+      for (int p = 0; p < KVP; ++p)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4i16_t*)(vt + (rd0 ^ (32u * dt))));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(bf16x4_t, pb),
-                                                      o[dt], 0, 0, 0);
+        for (int dt = 0; dt < DT; ++dt) o[p][dt] *= alpha;
     }
+    // O^T of KV head p weights that head's V tile (its column is the one kept)
+#pragma unroll
+    for (int p = 0; p < KVP; ++p)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)(vt + p * TB + (rd0 ^ (32u * dt))));
+        o[p][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(bf16x4_t, pb),
+                                                           o[p][dt], 0, 0, 0);
+      }
   };
 
   auto end_segment = [&](const Cursor& x, bool owns_start, bool owns_end) {
     float l = lpart + __shfl_xor(lpart, 16);
     l += __shfl_xor(l, 32);
     if (i16 >= HPW) return;
+    // this lane's column: with paired KV heads, column 1 is in the second set
+    f32x4_t oc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oc[dt] = KVP == 2 && i16 == 1 ? o[KVP - 1][dt] : o[0][dt];
     if (owns_start && owns_end) {
       if (a.lse && g == 0)
         a.lse[int64_t(x.s) * Hq + head_of(x) + i16] = m * c2 + __builtin_amdgcn_logf(l);
@@ -635,8 +666,8 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
                                              (int64_t(x.s) * Hq + head_of(x) + i16) * ROW);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        orow[(16 * dt + 4 * g) / 4] = make_uint2(pack_bf16(o[dt][0] * inv, o[dt][1] * inv),
-                                                 pack_bf16(o[dt][2] * inv, o[dt][3] * inv));
+        orow[(16 * dt + 4 * g) / 4] = make_uint2(pack_bf16(oc[dt][0] * inv, oc[dt][1] * inv),
+                                                 pack_bf16(oc[dt][2] * inv, oc[dt][3] * inv));
       return;
     }
     const int slot = 2 * w + (owns_start ? 1 : 0);
@@ -644,7 +675,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       dst[(16 * dt + 4 * g) / 4] =
-          make_float4(o[dt][0] * vsc, o[dt][1] * vsc, o[dt][2] * vsc, o[dt][3] * vsc);
+          make_float4(oc[dt][0] * vsc, oc[dt][1] * vsc, oc[dt][2] * vsc, oc[dt][3] * vsc);
     if (g == 0) a.ws_ml[int64_t(slot) * HPW + i16] = make_float2(m * c2, l);
   };
 
@@ -665,12 +696,13 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
         int pb = 0;
         if constexpr (BIG_B) pb = __builtin_amdgcn_readlane(win, ((j * kTile) >> b_shift) - jb0);
 #pragma unroll
-        for (int u = 0; u < NI; ++u) {
-          const int t = min(j * kTile + u * RPI + lrow, Lm1);
+        for (int ut = 0; ut < NIT; ++ut) {  // rows of KV head kvh + ut / NI
+          const int t = min(j * kTile + (ut % NI) * RPI + lrow, Lm1);
           if constexpr (!BIG_B) pb = __shfl(win, (t >> b_shift) - jb0);
-          const int64_t off = int64_t(pb) * block_bytes + head_off + int64_t(t & Bm1) * GROW;
-          kr[u] = load_stream16(reinterpret_cast<const uint4*>(kp + off));
-          vr[u] = load_stream16(reinterpret_cast<const uint4*>(vp + off));
+          const int64_t off = int64_t(pb) * block_bytes + head_off +
+                              int64_t(ut / NI) * B * GROW + int64_t(t & Bm1) * GROW;
+          kr[ut] = load_stream16(reinterpret_cast<const uint4*>(kp + off));
+          vr[ut] = load_stream16(reinterpret_cast<const uint4*>(vp + off));
         }
       };
       // NB tiles in flight: tile j + NB - 1 loads while tile j is computed
@@ -678,7 +710,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
       // load is unconditional (past the chunk it re-reads the chunk's last
       // tile, an L2 hit): with conditional loads the compiler cannot count the
       // loads in flight and waits for all of them.
-      uint4 kb[NB][NI], vb[NB][NI];
+      uint4 kb[NB][NIT], vb[NB][NIT];
       int j = jc;
 #pragma unroll
       for (int b = 0; b < NB - 1; ++b) load_tile(min(j + b, jc_end - 1), kb[b], vb[b]);
@@ -698,7 +730,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     }
   };
 
-  walk_slice<D, 8>(a, w, lane, n_hchunk, HPW, begin_segment, run_tiles, end_segment);
+  walk_slice<D, 8>(a, w, lane, n_hchunk, HPW, KVP, begin_segment, run_tiles, end_segment);
 }
 
 // Combine the partials of each split segment. Wave w looks at the segment
@@ -763,14 +795,31 @@ hipError_t run(const DecodeArgs& a, hipStream_t st) {
   wpg = wpg < 1 ? 1 : (wpg > kMaxWavesPerGroup ? kMaxWavesPerGroup : wpg);
   const int groups = (a.workers + wpg - 1) / wpg;
   const float scale_log2 = a.scale * kLog2e;
+  // FP8 MHA with an even number of heads: units of two adjacent KV heads
+  // (one contiguous run of both heads' rows per tile), combined as 2 heads
+  if constexpr (DTYPE == PA_FP8_E4M3 && HPW == 1) {
+    if (a.num_q_heads == a.num_kv_heads && a.num_kv_heads % 2 == 0) {
+      const size_t lds = size_t(wpg) * 2 * 2 * kTile * 2 * D;  // K and V tiles of 2 heads
+      if (a.block_size >= kTile)
+        decode_mfma_kernel<D, 2, true, DTYPE, 2>
+            <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
+      else
+        decode_mfma_kernel<D, 2, false, DTYPE, 2>
+            <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      decode_combine_kernel<PA_BF16, D, 2><<<groups, kWave * wpg, 0, st>>>(a);
+      return hipGetLastError();
+    }
+  }
   // bf16 groups of >= 4 heads and every FP8 pool run on the matrix cores
   if constexpr (DTYPE == PA_FP8_E4M3 || (DTYPE == PA_BF16 && HPW >= 4)) {
     const size_t lds = size_t(wpg) * 2 * kTile * 2 * D;  // a K and a V tile per wave (bf16)
     if (a.block_size >= kTile)
-      decode_mfma_kernel<D, HPW, true, DTYPE>
+      decode_mfma_kernel<D, HPW, true, DTYPE, 1>
           <<<groups, kWave * wpg, lds, st>>>(a, b_shift, n_hchunk, scale_log2);
     else
-      decode_mfma_kernel<D, HPW, false, DTYPE>
+      decode_mfma_kernel<D, HPW, false, DTYPE, 1>
           <<<groups, kWave * wpg, lds, st>>>(a, b_shift, n_hchunk, scale_log2);
   } else {
     if (a.block_size >= kTile)
