@@ -485,12 +485,14 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
 // KV = PA_BF16, or PA_FP8_E4M3: the pool holds E4M3 codes, which are widened
 // exactly to bf16 on their way into LDS; k_scale then multiplies the scores and
 // v_scale the output, and everything from LDS on is the bf16 kernel.
-// KVP = 2 (MHA, HPW = 2): a unit is two consecutive KV heads with their one
-// query head each. Column c of the MFMA tiles is head kvh + c and is scored
-// against, and weights, that head's own K and V tiles. The two heads' rows of a
-// block are adjacent in the pool, so each tile reads one contiguous run of
-// 2*16 rows per pool instead of two of 16: with FP8 rows (128 B) a 16-row run
-// is only 2 KB, and the memory system serves such short runs much more slowly.
+// KVP = 2 (FP8 MHA, HPW = 2): a unit is two adjacent KV heads with their one
+// query head each. Columns c < HPW/2 belong to KV head kvh, the others to
+// kvh + 1; each column is scored against, and weights, its own head's K and V
+// tiles. The two heads' rows of a block are adjacent in the pool, so each tile
+// reads one contiguous run of 2*16 rows per pool instead of two of 16: the
+// memory system serves short runs (2 KB for 16 FP8 rows of 128 B) much more
+// slowly than long ones. (bf16 groups of 8 paired the same way, 16 columns,
+// ran no faster: their 4 KB runs are long enough.)
 template <int D, int HPW, bool BIG_B, int KV, int KVP>
 __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
@@ -504,7 +506,8 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   constexpr int RPI = 1024 / GROW;  // rows per wave-wide 16-byte load
   constexpr int NI = kTile / RPI;   // loads per lane per tile and KV head, for K and for V
   constexpr int NIT = NI * KVP;     // loads per lane per tile, for K and for V
-  static_assert(KVP == 1 || HPW == KVP, "paired KV heads carry one query head each");
+  static_assert(HPW % KVP == 0, "a unit's columns split evenly over its KV heads");
+  constexpr int CPH = HPW / KVP;    // MFMA columns (query heads) per KV head of the unit
   constexpr int RPL = 256 / ROW;    // rows per 256-byte LDS bank line
   constexpr int TB = kTile * ROW;   // bytes of one K or V tile in LDS
   // tiles in flight per wave: an FP8 tile is half the bytes, so more of them
@@ -605,7 +608,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     }
     // column i16 is scored against the K tile of its own KV head
     f32x4_t sc = scp[0];
-    if constexpr (KVP == 2) sc = i16 == 1 ? scp[1] : scp[0];
+    if constexpr (KVP == 2) sc = i16 >= CPH ? scp[1] : scp[0];
     const int key0 = j * kTile + 4 * g;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -657,7 +660,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     // this lane's column: with paired KV heads, column 1 is in the second set
     f32x4_t oc[DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oc[dt] = KVP == 2 && i16 == 1 ? o[KVP - 1][dt] : o[0][dt];
+    for (int dt = 0; dt < DT; ++dt) oc[dt] = KVP == 2 && i16 >= CPH ? o[KVP - 1][dt] : o[0][dt];
     if (owns_start && owns_end) {
       if (a.lse && g == 0)
         a.lse[int64_t(x.s) * Hq + head_of(x) + i16] = m * c2 + __builtin_amdgcn_logf(l);

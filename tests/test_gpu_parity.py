@@ -184,8 +184,9 @@ def _single_seq(L, Hq, Hkv, D, B, dtype, seed, zero_keys=False):
     # cores): head_dim 64, blocks smaller than a 16-token tile, two head
     # chunks per KV head
     (64, 8, 16, 4), (128, 4, 16, 2), (64, 16, 32, 2),
-    # MHA with an odd head count (FP8 pools pair KV heads only when even)
-    (128, 16, 3, 3)])
+    # MHA with an odd head count (FP8 pools pair KV heads only when even);
+    # groups of 8 over 2 KV heads, blocks of 16 and 8
+    (128, 16, 3, 3), (128, 16, 16, 2), (64, 8, 16, 2)])
 def test_edge_lengths(dtype, L, D, B, Hq, Hkv):
     from oracle.attention import decode_attention
     q, k, v, got = _single_seq(L, Hq, Hkv, D, B, dtype, seed=L * 7 + D)
