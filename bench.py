@@ -197,23 +197,31 @@ def _stats_us(ms):
             "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)}
 
 
-def time_steps(step, steps, warmup):
+EVENT_EVERY = 8  # timed steps per step that records HIP events
+
+
+def time_steps(step, steps, warmup, event_every=EVENT_EVERY):
     """Run warmup steps, then exactly `steps` timed steps bracketed by synchronisation.
-    Each step records 3 events (before, between its two calls, after) on the launch stream."""
+    Every `event_every`-th timed step also records 3 events (before, between its
+    two calls, after) on the launch stream: the per-call durations are the means
+    over those sampled steps. (An event record costs about 3 us of stream time
+    on this device, so recording them on every step would inflate the step
+    time by some 4 %.)"""
     import numpy as np
     import torch
     for i in range(warmup):
         step(i, None)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    sampled = list(range(0, steps, event_every))
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
-        step(i, evs[i])
+        step(i, evs.get(i))
     torch.cuda.synchronize()
     total = time.perf_counter() - t_start
-    first = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    second = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    first = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in sampled])
+    second = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in sampled])
     return total * 1e3 / steps, first, second
 
 
@@ -404,7 +412,7 @@ def mixed_row(ld, steps, warmup, workers):
             fn(p)
             if ev is not None:
                 ev[2].record(stream)
-        return time_steps(step, steps, warmup)[2]
+        return time_steps(step, steps, warmup, event_every=1)[2]  # per-call durations
 
     m_ms = timed(lambda p: pkv.attention_mixed(q, loc, lens, p, tables, nd, C, wl.scale, workers,
                                                out=out, workspace=ws))
@@ -539,7 +547,7 @@ def decode_row(ld, steps, warmup, workers, path="plain"):
 
 
 def prefill_row(ld, steps, warmup):
-    ms_step, w_ms, p_ms = time_steps(prefill_step_fn(ld), steps, warmup)
+    ms_step, w_ms, p_ms = time_steps(prefill_step_fn(ld), steps, warmup, event_every=1)
     wl = ld.wl
     flops = 4.0 * wl.head_dim * wl.num_q_heads * ld.p_keys
     tflops = flops / (float(p_ms.mean()) * 1e-3) / 1e12
