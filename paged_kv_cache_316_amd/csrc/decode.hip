@@ -750,39 +750,70 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kern
   const int4 seg = a.ws_seg[w];
   if (seg.x < 0) return;
   const int wb = seg.z, head0 = seg.w;
-  // one lane group of LPR lanes per query head of the unit
-  for (int hh = lane / LPR; hh < HPW; hh += kWave / LPR) {
-    const int c = lane % LPR;
-    float M = -INFINITY;
-    for (int v = w; v <= wb; ++v) {
-      const int sl = v == w ? 2 * v + 1 : 2 * v;
-      M = fmaxf(M, a.ws_ml[int64_t(sl) * HPW + hh].x);
-    }
-    float den = 0.f, num[VEC];
+  // one lane group of LPR lanes per query head of the unit; with more heads
+  // than lane groups a lane takes several heads, whose loads are issued
+  // together. The partials are merged online (running max M, rescaled sums),
+  // two of them per step so that their loads are in flight together.
+  constexpr int GROUPS = kWave / LPR;
+  constexpr int HPL = (HPW + GROUPS - 1) / GROUPS;  // heads per lane
+  const int c = lane % LPR;
+  float M[HPL], den[HPL], num[HPL][VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) num[e] = 0.f;
-    for (int v = w; v <= wb; ++v) {
-      const int sl = v == w ? 2 * v + 1 : 2 * v;
-      const float2 ml = a.ws_ml[int64_t(sl) * HPW + hh];
-      const float f = __builtin_amdgcn_exp2f(ml.x - M);
-      den = fmaf(ml.y, f, den);
-      const float4* src = reinterpret_cast<const float4*>(a.ws_acc + (int64_t(sl) * HPW + hh) * D + c * VEC);
+  for (int k = 0; k < HPL; ++k) {
+    M[k] = -INFINITY;
+    den[k] = 0.f;
 #pragma unroll
-      for (int e = 0; e < VEC; e += 4) {
-        const float4 x = src[e / 4];
-        num[e] = fmaf(x.x, f, num[e]);
-        num[e + 1] = fmaf(x.y, f, num[e + 1]);
-        num[e + 2] = fmaf(x.z, f, num[e + 2]);
-        num[e + 3] = fmaf(x.w, f, num[e + 3]);
+    for (int e = 0; e < VEC; ++e) num[k][e] = 0.f;
+  }
+  auto slot_of = [&](int v) { return v == w ? 2 * v + 1 : 2 * v; };
+  for (int v = w; v <= wb; v += 2) {
+    const int nv = v + 1 <= wb ? 2 : 1;  // wave-uniform
+    float2 ml[2][HPL];
+    float4 x[2][HPL][VEC / 4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int sl = slot_of(q < nv ? v + q : v);
+#pragma unroll
+      for (int k = 0; k < HPL; ++k) {
+        const int hh = min(lane / LPR + k * GROUPS, HPW - 1);
+        ml[q][k] = a.ws_ml[int64_t(sl) * HPW + hh];
+        const float4* src =
+            reinterpret_cast<const float4*>(a.ws_acc + (int64_t(sl) * HPW + hh) * D + c * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) x[q][k][e / 4] = src[e / 4];
       }
     }
-    const float inv = 1.f / den;
-    if (a.lse && c == 0)
-      a.lse[int64_t(seg.x) * a.num_q_heads + head0 + hh] = M + __builtin_amdgcn_logf(den);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) num[e] *= inv;
+    for (int k = 0; k < HPL; ++k) {
+      const float m2 = nv == 2 ? ml[1][k].x : -INFINITY;
+      const float Mn = fmaxf(M[k], fmaxf(ml[0][k].x, m2));
+      const float fo = M[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[k] - Mn);
+      const float f0 = __builtin_amdgcn_exp2f(ml[0][k].x - Mn);
+      const float f1 = nv == 2 ? __builtin_amdgcn_exp2f(m2 - Mn) : 0.f;
+      den[k] = den[k] * fo + ml[0][k].y * f0 + (nv == 2 ? ml[1][k].y * f1 : 0.f);
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        const float4 x0 = x[0][k][e / 4], x1 = x[1][k][e / 4];
+        num[k][e] = num[k][e] * fo + x0.x * f0 + x1.x * f1;
+        num[k][e + 1] = num[k][e + 1] * fo + x0.y * f0 + x1.y * f1;
+        num[k][e + 2] = num[k][e + 2] * fo + x0.z * f0 + x1.z * f1;
+        num[k][e + 3] = num[k][e + 3] * fo + x0.w * f0 + x1.w * f1;
+      }
+      M[k] = Mn;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < HPL; ++k) {
+    const int hh = lane / LPR + k * GROUPS;
+    if (hh >= HPW) continue;
+    const float inv = 1.f / den[k];
+    if (a.lse && c == 0)
+      a.lse[int64_t(seg.x) * a.num_q_heads + head0 + hh] = M[k] + __builtin_amdgcn_logf(den[k]);
+    float f[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) f[e] = num[k][e] * inv;
     uint4* o = static_cast<uint4*>(a.out) + ((int64_t(seg.x) * a.num_q_heads + head0 + hh) * D) / VEC + c;
-    *o = pack16<DTYPE>(num);
+    *o = pack16<DTYPE>(f);
   }
 }
 
