@@ -344,9 +344,10 @@ PrefixPlan prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   p.n_cblk = int32_t((cols + 16 * p.groups_per_wave - 1) / (16 * p.groups_per_wave));
   p.n_tiles = int32_t((int64_t(num_prefix_blocks) * block_size + kPTile - 1) / kPTile);
   if (p.n_tiles <= 0) return p;
-  // about four waves per compute unit, but no key range under 8 tiles
+  // as many key ranges as one round of resident waves (8 per compute unit)
+  // holds, but no key range under 8 tiles
   const int64_t per_split = int64_t(num_kv_heads) * p.n_cblk;
-  const int64_t want = (int64_t(4) * (num_cus > 0 ? num_cus : 256) + per_split - 1) / per_split;
+  const int64_t want = int64_t(8) * (num_cus > 0 ? num_cus : 256) / per_split;
   const int64_t cap = p.n_tiles / 8 > 1 ? p.n_tiles / 8 : 1;
   const int64_t n = want < 1 ? 1 : (want > cap ? cap : want);
   p.tiles_per_split = int32_t((p.n_tiles + n - 1) / n);
