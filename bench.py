@@ -524,7 +524,7 @@ def stream_read_ceiling(gib: int = 4):
     del buf
     torch.cuda.empty_cache()
     return {"gbps": round(best, 1), "grid": best_grid, "bytes": gib << 30,
-            "kernel": "pa_probe_stream_read (16-byte non-temporal loads, 4 in flight per lane)"}
+            "kernel": "pa_probe_stream_read (16-byte non-temporal loads, 8 KB contiguous runs per wave, 8 in flight per lane)"}
 
 
 def decode_row(ld, steps, warmup, workers, path="plain"):

@@ -147,7 +147,8 @@ pa_status pa_swap_blocks(const pa_pool* device_pool, const pa_pool* host_pool,
 /*
  * pa_probe_stream_read — measurement aid, not part of the attention path:
  * reads `bytes` of device memory once, with 16-byte non-temporal loads from
- * `grid` workgroups of 256 threads (grid <= 0: 16 per compute unit). Timing
+ * `grid` workgroups of 256 threads (grid <= 0: 16 per compute unit), each
+ * wavefront reading contiguous 8 KB runs (8 loads in flight per lane). Timing
  * it gives this device's streaming-read rate, the ceiling that the decode
  * kernels' HBM rate is compared against.
  *   buf  : device, 16-byte aligned; bytes a multiple of 16 (0: no-op)
