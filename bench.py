@@ -198,10 +198,19 @@ def _stats_us(ms):
 
 
 EVENT_EVERY = 8  # timed steps per step that records HIP events
+# Extra rows run a few tens of steps right after seconds of host-side set-up
+# with the GPU idle; measured that way the shortest of them (the FP8 decode,
+# ~10 ms of work in all) read 8 % slow against the same call after a longer
+# run of steps. Their warmup therefore also lasts at least this long. The
+# main row keeps exactly --warmup steps.
+EXTRA_ROW_WARM_S = 0.25
+_warm_s = 0.0
 
 
 def time_steps(step, steps, warmup, event_every=EVENT_EVERY):
-    """Run warmup steps, then exactly `steps` timed steps bracketed by synchronisation.
+    """Run warmup steps (at least `warmup`, and for the extra rows at least
+    _warm_s seconds of them), then exactly `steps` timed steps bracketed by
+    synchronisation.
     Every `event_every`-th timed step also records 3 events (before, between its
     two calls, after) on the launch stream: the per-call durations are the means
     over those sampled steps. (An event record costs about 3 us of stream time
@@ -212,6 +221,13 @@ def time_steps(step, steps, warmup, event_every=EVENT_EVERY):
     for i in range(warmup):
         step(i, None)
     torch.cuda.synchronize()
+    if _warm_s > 0:
+        t0, i = time.perf_counter(), warmup
+        while time.perf_counter() - t0 < _warm_s:
+            for _ in range(8):
+                step(i, None)
+                i += 1
+            torch.cuda.synchronize()
     sampled = list(range(0, steps, event_every))
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
@@ -667,6 +683,8 @@ def main():
             torch.cuda.empty_cache()
             ld = Loaded(name, replicas)
 
+        global _warm_s
+        _warm_s = EXTRA_ROW_WARM_S
         short = max(20, args.steps // 4)
         if want("swap_llama13b"):
             switch("llama13b", 1)
