@@ -389,20 +389,37 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void prefill_kernel(
     lsum += ps;
     // O^T += V^T P^T; operand j of half g in k-step kk = (mt, h) is key
     // 16 kk + 8 (j / 4) + 4 g + j % 4, matching the S^T accumulator order
+    // The V^T operands are read kVAhead products ahead of their use, and the
+    // order (reads first, then one product per pair of reads) is pinned, so
+    // each product waits only for reads issued several products earlier.
     const unsigned char* vt_lds = smem + (2 + par) * PS::TILE;
+    constexpr int NPV = 4 * PS::DTILES;  // products of this tile: (kk, dt), dt fastest
+    constexpr int kVAhead = 3;
+    auto vread = [&](int i) {
+      const int kk = i / PS::DTILES, dt = i % PS::DTILES;
+      const uint32_t rows = uint32_t(kk * 16 * PS::ROW);
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)(vt_lds + ((v_lo ^ (64u * dt)) + rows)));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)(vt_lds + ((v_hi ^ (64u * dt)) + rows)));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      return make_uint4(l2.x, l2.y, h2.x, h2.y);
+    };
+    uint4 vop[NPV];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int i = 0; i < kVAhead; ++i) vop[i] = vread(i);
 #pragma unroll
-      for (int dt = 0; dt < PS::DTILES; ++dt) {
-        const uint32_t rows = uint32_t(kk * 16 * PS::ROW);
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)(vt_lds + ((v_lo ^ (64u * dt)) + rows)));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)(vt_lds + ((v_hi ^ (64u * dt)) + rows)));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        o[dt] = mfma32(make_uint4(l2.x, l2.y, h2.x, h2.y), pop[kk], o[dt]);
-      }
+    for (int i = 0; i < NPV; ++i) {
+      if (i + kVAhead < NPV) vop[i + kVAhead] = vread(i + kVAhead);
+      o[i % PS::DTILES] = mfma32(vop[i], pop[i / PS::DTILES], o[i % PS::DTILES]);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < NPV - kVAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 0);
   };
 
   // prologue: K(0), V(0), K(1) in flight, then the scores of tile 0
