@@ -13,6 +13,10 @@ or a scale. Readings used here:
   single-precision division), clamped to [-448, 448] and rounded to the
   nearest E4M3 value, ties to even mantissa. A stored code c stands for
   decode(c) * scale.
+* Values the format cannot hold (the pages say nothing; reading of this
+  library): a quotient beyond +-448, +-infinity included, saturates to the
+  largest finite code of its sign (0x7E / 0xFE); a NaN input, whatever its
+  sign or payload, is stored as the NaN code 0x7F.
 
 Everything is written from the format definition: the table of the 128
 non-negative codes comes from sign/exponent/mantissa, and encoding picks the
@@ -58,10 +62,16 @@ def e4m3_encode(y) -> np.ndarray:
     return np.where(np.signbit(y), mag | np.uint8(0x80), mag).astype(np.uint8)
 
 
+NAN_CODE = 0x7F
+
+
 def quantize(x, scale: float) -> np.ndarray:
     """Codes of the values x under one pool scale (see the module docstring)."""
-    y = np.asarray(x, dtype=np.float32) / np.float32(scale)
-    return e4m3_encode(np.clip(y, -E4M3_MAX, E4M3_MAX))
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = np.asarray(x, dtype=np.float32) / np.float32(scale)
+    nan = np.isnan(y)
+    codes = e4m3_encode(np.clip(np.where(nan, np.float32(0), y), -E4M3_MAX, E4M3_MAX))
+    return np.where(nan, np.uint8(NAN_CODE), codes).astype(np.uint8)
 
 
 def dequantize(codes, scale: float) -> np.ndarray:

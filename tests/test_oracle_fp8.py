@@ -98,6 +98,26 @@ def test_quantize_scale_and_clamp():
     assert int(fp8.quantize(np.float32(0.7), float(s2))) == int(fp8.e4m3_encode(y))
 
 
+def test_quantize_non_finite_and_overflow():
+    """Reading for values the format cannot hold: NaN of either sign or any
+    payload -> the NaN code 0x7F; +-inf, and finite values whose fp32 quotient
+    overflows, saturate to +-448 (0x7E / 0xFE)."""
+    bits = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFBFFFFF], dtype=np.uint32)
+    nans = bits.view(np.float32)
+    assert np.all(fp8.quantize(nans, 0.5) == 0x7F)
+    assert np.all(fp8.quantize(nans, 2.0 ** -6) == 0x7F)
+    inf = np.array([np.inf, -np.inf], dtype=np.float32)
+    assert list(fp8.quantize(inf, 0.0123)) == [0x7E, 0xFE]
+    big = np.array([3.0e38, -3.0e38], dtype=np.float32)  # 3e38 / 1e-3 overflows fp32
+    assert list(fp8.quantize(big, 1e-3)) == [0x7E, 0xFE]
+    # a NaN among finite values leaves the others alone
+    mixed = np.array([1.0, np.nan, -1.0], dtype=np.float32)
+    assert list(fp8.quantize(mixed, 2.0 ** -6)) == [0x68, 0x7F, 0xE8]
+    # the NaN code decodes to NaN, the saturated codes to +-448
+    assert np.isnan(fp8.e4m3_decode(np.uint8(0x7F)))
+    assert list(fp8.e4m3_decode(np.array([0x7E, 0xFE], dtype=np.uint8))) == [448.0, -448.0]
+
+
 # ----------------------------------------------------- planted mistakes ----
 def _enc_truncate(y):
     y = np.asarray(y, dtype=np.float32)
