@@ -24,11 +24,17 @@
  *    ("LLM inference engine internals", section 2.3, append_slot).
  *  - Grouped heads: query head h reads KV head h / (num_q_heads / num_kv_heads).
  *  - Errors: entry points return a pa_status and never abort. Every argument
- *    that can be checked on the host is checked before any launch; on error no
- *    work is queued. Contents of device arrays (block ids, slots, lengths) are
- *    preconditions: they must index inside the pool and the tables.
+ *    that can be checked on the host is checked before any launch; when such a
+ *    check fails no work is queued. A call that launches several kernels and
+ *    gets PA_ERR_HIP from a later launch may leave its earlier launches queued.
+ *    Contents of device arrays (block ids, slots, lengths, copy pairs) are
+ *    preconditions: they must index inside the pool and the tables. The
+ *    pa_check_* functions below verify them on host copies of those arrays
+ *    (a debug aid; the device calls do not read them back).
  *    pa_last_error() gives a message for the most recent failure on the calling
  *    thread.
+ *  - Softmax scale: every attention call takes `scale` (typically
+ *    1/sqrt(head_dim)); it must be finite and > 0, else PA_ERR_INVALID.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -96,7 +102,9 @@ int32_t pa_version(void);
  * pool each value x is stored as the E4M3 code nearest to
  * min(max(x / scale, -448), 448), x / scale an IEEE single-precision
  * division, ties to the even mantissa (a deterministic function of x and the
- * pool's k_scale / v_scale). Slots must be distinct and < num_blocks * B;
+ * pool's k_scale / v_scale). Quotients beyond +-448, +-infinity included,
+ * saturate to the code of +-448 (0x7E / 0xFE); a NaN value of either sign is
+ * stored as the NaN code 0x7F. Slots must be distinct and < num_blocks * B;
  * nothing else in the pool is touched. num_tokens == 0 is a no-op.
  */
 pa_status pa_cache_write(const pa_pool* pool, const void* k_new, const void* v_new,
@@ -183,7 +191,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   seq_lens     : device, int32 [num_seqs], each in [0, max_blocks_per_seq * B];
  *                  a sequence of length 0 gets an all-zero output
  *   num_q_heads  : multiple of pool->num_kv_heads
- *   scale        : softmax scale (typically 1/sqrt(head_dim))
+ *   scale        : softmax scale, finite and > 0 (typically 1/sqrt(head_dim))
  *   num_workers  : 0 = default; any positive count gives the same result up to
  *                  fp32 rounding order
  *   workspace    : device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
@@ -303,6 +311,46 @@ pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_lo
                              int32_t num_decode, int32_t num_prefill, int32_t num_q_heads,
                              int32_t max_q_len, float scale, int32_t num_workers, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------- host checks of preconditions --- */
+
+/*
+ * The device calls take block tables, lengths, slots, copy pairs and chunk
+ * offsets in device memory and do not read them back on the host, so their
+ * contents are preconditions (a table entry outside the pool makes a kernel
+ * read outside it). These functions check host copies of those arrays before
+ * a launch: a debug aid for callers and bindings. Each returns PA_OK, or
+ * PA_ERR_INVALID with pa_last_error() naming the first violation. All array
+ * arguments are HOST memory, read during the call; pools are used only for
+ * num_blocks and block_size (their data pointers are not touched).
+ */
+
+/* Tables and lengths of pa_decode (and of the decode rows of the other calls):
+ * 0 <= seq_lens[s] <= max_blocks_per_seq * B, and the first
+ * ceil(seq_lens[s] / B) entries of row s lie in [0, num_blocks)
+ * ("Why PagedAttention multiplies LLM serving throughput", section "Block
+ * Table: the GPU page table"). */
+pa_status pa_check_batch(const pa_pool* pool, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs);
+/* Slots of pa_cache_write: each negative (skipped) or < num_blocks * B, and no
+ * slot named twice ("LLM inference engine internals", section 2.3). */
+pa_status pa_check_slots(const pa_pool* pool, const int64_t* slot_mapping, int32_t num_tokens);
+/* Pairs of pa_copy_blocks: ids in [0, num_blocks), no block both a source and a
+ * destination, no destination twice ("vLLM PagedAttention explained", 4.1). */
+pa_status pa_check_copies(const pa_pool* pool, const int32_t* src_dst, int32_t num_pairs);
+/* Row offsets of pa_prefill_chunk / pa_attention_mixed: q_start_loc[0] = 0;
+ * the first num_decode sequences have one row each; every other sequence has
+ * 0 <= q_len <= max_q_len rows and q_len <= seq_lens[s] (its rows are in the
+ * pool); q_start_loc[num_seqs] <= total_rows (the rows of q and out);
+ * seq_lens >= 0 ("vLLM PagedAttention explained", section 7.2). */
+pa_status pa_check_chunks(const int32_t* q_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_decode, int32_t max_q_len, int64_t total_rows);
+/* pa_check_batch, plus the precondition of pa_decode_shared_prefix: every row
+ * begins with row 0's first num_prefix_blocks entries and every sequence is at
+ * least num_prefix_blocks * B tokens long. */
+pa_status pa_check_shared_prefix(const pa_pool* pool, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t num_prefix_blocks);
 
 /* ------------------------------------------------------------------ host --- */
 

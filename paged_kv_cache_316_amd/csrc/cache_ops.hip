@@ -33,13 +33,17 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
 }
 
 // Four values -> four E4M3 codes (first value in the low byte): x / scale (an
-// IEEE division), clamped to the largest finite code, rounded to nearest even
-// by v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950).
+// IEEE division), clamped to the largest finite magnitude (a quotient of
+// +-inf included), rounded to nearest even by v_cvt_pk_fp8_f32 (OCP E4M3 on
+// gfx950). A NaN input is stored as the NaN code 0x7F whatever its sign or
+// payload: it is converted as 0 and its byte replaced afterwards.
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float s) {
-  auto q = [s](float x) { return fminf(fmaxf(x / s, -448.f), 448.f); };
+  auto q = [s](float x) { return x != x ? 0.f : fminf(fmaxf(x / s, -448.f), 448.f); };
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(q(a), q(b), 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(q(c), q(d), w, true);
-  return uint32_t(w);
+  const uint32_t nan = (a != a ? 0xffu : 0u) | (b != b ? 0xff00u : 0u) |
+                       (c != c ? 0xff0000u : 0u) | (d != d ? 0xff000000u : 0u);
+  return (uint32_t(w) & ~nan) | (0x7f7f7f7fu & nan);
 }
 
 // 16 bf16 values (two 16-byte chunks) -> 16 codes.
