@@ -6,7 +6,10 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+# PAGEDKV_LIB names another build of the same library (the sanitizer build of
+# the host code uses it); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_OOM = 0, -1, -2, -3
 PA_ERR_STATE, PA_ERR_WORKSPACE, PA_ERR_HIP = -4, -5, -6
@@ -54,6 +57,12 @@ SIGNATURES = {
     "pa_swap_blocks": (c_int32, [_P(PaPool), _P(PaPool), c_void_p, c_int32, c_int32, c_void_p]),
     "pa_prefill_chunk": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, _P(PaPool), c_void_p,
                                    c_int32, c_int32, c_int32, c_int32, c_float, c_void_p]),
+    "pa_check_batch": (c_int32, [_P(PaPool), c_void_p, c_int32, c_void_p, c_int32]),
+    "pa_check_slots": (c_int32, [_P(PaPool), c_void_p, c_int32]),
+    "pa_check_copies": (c_int32, [_P(PaPool), c_void_p, c_int32]),
+    "pa_check_chunks": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int64]),
+    "pa_check_shared_prefix": (c_int32, [_P(PaPool), c_void_p, c_int32, c_void_p, c_int32,
+                                         c_int32]),
     "pa_alloc_create": (c_int32, [c_int32, c_int32, c_void_p, _P(c_void_p)]),
     "pa_alloc_destroy": (None, [c_void_p]),
     "pa_alloc_allocate": (c_int32, [c_void_p, c_int64, c_void_p, c_int32, _P(c_int32), c_void_p]),

@@ -1,5 +1,5 @@
-// C ABI entry points: host-side argument checks, workspace sizing, dispatch
-// to the HIP launchers, and status / error-message plumbing.
+// C ABI entry points of the device calls: host-side argument checks,
+// workspace sizing and dispatch to the HIP launchers.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -14,8 +14,6 @@
 namespace pa {
 
 namespace {
-thread_local char g_msg[512] = "";
-
 constexpr int32_t kWavesPerCU = 8;  // default decode workers per compute unit
 
 int32_t device_cus() {
@@ -134,6 +132,15 @@ pa_status check_pool(const pa_pool* p, const char* who) {
   return PA_OK;
 }
 
+// Softmax scale: finite and > 0. A negative scale would turn the running max
+// into the smallest logit and the weights could overflow; zero or non-finite
+// scales have no meaningful attention.
+pa_status check_scale(float scale, const char* who) {
+  if (!(scale > 0.f && scale <= 3.402823466e38f))
+    return fail(PA_ERR_INVALID, "%s: scale=%g must be finite and > 0", who, double(scale));
+  return PA_OK;
+}
+
 pa_status hip_status(hipError_t e, const char* who) {
   if (e == hipSuccess) return PA_OK;
   return fail(PA_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
@@ -173,38 +180,11 @@ DecodeArgs decode_args(void* out, const void* q, const pa_pool* pool, const int3
 
 }  // namespace
 
-pa_status fail(pa_status s, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
-  va_end(ap);
-  return s;
-}
-
-void clear_error() { g_msg[0] = '\0'; }
-
 }  // namespace pa
 
 using pa::fail;
 
 extern "C" {
-
-const char* pa_status_string(pa_status s) {
-  switch (s) {
-    case PA_OK: return "ok";
-    case PA_ERR_INVALID: return "invalid argument";
-    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
-    case PA_ERR_OOM: return "out of free blocks";
-    case PA_ERR_STATE: return "invalid allocator state (unknown or duplicate sequence)";
-    case PA_ERR_WORKSPACE: return "workspace too small";
-    case PA_ERR_HIP: return "HIP runtime error";
-  }
-  return "unknown status";
-}
-
-const char* pa_last_error(void) { return pa::g_msg; }
-
-int32_t pa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
 
 pa_status pa_cache_write(const pa_pool* pool, const void* k_new, const void* v_new,
                          const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
@@ -348,7 +328,7 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t
   if (num_q_heads % pool->num_kv_heads)
     return fail(PA_ERR_INVALID, "pa_decode: num_q_heads=%d not a multiple of num_kv_heads=%d",
                 num_q_heads, pool->num_kv_heads);
-  if (!(scale == scale)) return fail(PA_ERR_INVALID, "pa_decode: scale is NaN");
+  if (pa_status s = pa::check_scale(scale, "pa_decode")) return s;
   if (num_workers < 0 || num_workers > (1 << 24))
     return fail(PA_ERR_INVALID, "pa_decode: num_workers=%d out of range", num_workers);
   if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
@@ -401,7 +381,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const pa_pool* pool,
   if (num_q_heads % pool->num_kv_heads)
     return fail(PA_ERR_INVALID, "%s: num_q_heads=%d not a multiple of num_kv_heads=%d", who,
                 num_q_heads, pool->num_kv_heads);
-  if (!(scale == scale)) return fail(PA_ERR_INVALID, "%s: scale is NaN", who);
+  if (pa_status s = pa::check_scale(scale, who)) return s;
   if (num_workers < 0 || num_workers > (1 << 24))
     return fail(PA_ERR_INVALID, "%s: num_workers=%d out of range", who, num_workers);
   if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
@@ -480,7 +460,7 @@ pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_lo
   if (num_q_heads % pool->num_kv_heads)
     return fail(PA_ERR_INVALID, "%s: num_q_heads=%d not a multiple of num_kv_heads=%d", who,
                 num_q_heads, pool->num_kv_heads);
-  if (!(scale == scale)) return fail(PA_ERR_INVALID, "%s: scale is NaN", who);
+  if (pa_status s = pa::check_scale(scale, who)) return s;
   if (num_workers < 0 || num_workers > (1 << 24))
     return fail(PA_ERR_INVALID, "%s: num_workers=%d out of range", who, num_workers);
   if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
@@ -543,24 +523,25 @@ pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_lo
     a.block_size = pool->block_size;
     a.max_q_len = max_q_len;
     a.scale = scale;
-    const hipStream_t pst = side ? side->stream : st;
-    if (pa_status s = pa::hip_status(pa::launch_prefill(a, pst), who)) return s;
-    if (side) return pa::hip_status(hipEventRecord(side->join, pst), who);
-    return PA_OK;
+    return pa::hip_status(pa::launch_prefill(a, side ? side->stream : st), who);
   };
+  pa_status result = PA_OK;
   if (pa::kMixedDecodeFirst) {
-    if (num_decode > 0)
-      if (pa_status s = run_decode()) return s;
-    if (chunks)
-      if (pa_status s = run_chunks()) return s;
+    if (num_decode > 0) result = run_decode();
+    if (chunks && result == PA_OK) result = run_chunks();
   } else {
-    if (chunks)
-      if (pa_status s = run_chunks()) return s;
-    if (num_decode > 0)
-      if (pa_status s = run_decode()) return s;
+    if (chunks) result = run_chunks();
+    if (num_decode > 0 && result == PA_OK) result = run_decode();
   }
-  if (side) return pa::hip_status(hipStreamWaitEvent(st, side->join, 0), who);
-  return PA_OK;
+  if (side) {
+    // Join the side stream back into the caller's stream whatever happened
+    // above, so that no work of this call is left unordered with later work
+    // on `stream`. A launch error is reported in preference to a join error.
+    hipError_t e = hipEventRecord(side->join, side->stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, side->join, 0);
+    if (result == PA_OK) result = pa::hip_status(e, who);
+  }
+  return result;
 }
 
 pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,
@@ -578,7 +559,7 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: NULL pointer argument");
   if (num_q_heads % pool->num_kv_heads)
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: num_q_heads not a multiple of num_kv_heads");
-  if (!(scale == scale)) return fail(PA_ERR_INVALID, "pa_prefill_chunk: scale is NaN");
+  if (pa_status s = pa::check_scale(scale, "pa_prefill_chunk")) return s;
   if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
        reinterpret_cast<uintptr_t>(pool->k_pool) | reinterpret_cast<uintptr_t>(pool->v_pool)) & 15)
     return fail(PA_ERR_INVALID, "pa_prefill_chunk: out/q/pools must be 16-byte aligned");

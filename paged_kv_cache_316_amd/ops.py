@@ -7,8 +7,10 @@ attention path runs in the library's HIP kernels.
 from __future__ import annotations
 
 import ctypes
+import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 from ._lib import PA_BF16, PA_F32, PA_FP8_E4M3, PaPool, PagedKVError, check, lib
@@ -22,6 +24,63 @@ def _stream() -> ctypes.c_void_p:
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+# Input checks: with PAGEDKV_CHECK=1 in the environment (or set_input_checks(True))
+# every call first copies its index arrays (tables, lengths, slots, copy pairs,
+# chunk offsets) to the host and has the library's pa_check_* functions verify
+# them, raising on the first violation. A debug aid: it synchronizes the stream.
+_CHECK_INPUTS = os.environ.get("PAGEDKV_CHECK", "") == "1"
+
+
+def set_input_checks(on: bool) -> None:
+    global _CHECK_INPUTS
+    _CHECK_INPUTS = bool(on)
+
+
+def _host(a, dtype) -> np.ndarray:
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
+def check_batch(pool: "KVPool", block_tables, seq_lens) -> None:
+    """Tables and lengths index inside the pool (host check; raises PagedKVError)."""
+    t, n = _host(block_tables, np.int32), _host(seq_lens, np.int32)
+    if t.ndim != 2 or n.shape != (t.shape[0],):
+        raise ValueError("block_tables must be [S, maxB] and seq_lens [S]")
+    check(lib().pa_check_batch(ctypes.byref(pool.c), t.ctypes.data, t.shape[1], n.ctypes.data,
+                               n.shape[0]))
+
+
+def check_slots(pool: "KVPool", slot_mapping) -> None:
+    """Slots inside the pool and distinct (host check)."""
+    s = _host(slot_mapping, np.int64).reshape(-1)
+    check(lib().pa_check_slots(ctypes.byref(pool.c), s.ctypes.data, s.shape[0]))
+
+
+def check_copies(pool: "KVPool", src_dst) -> None:
+    """Copy pairs inside the pool, no block both a source and a destination (host check)."""
+    p = _host(src_dst, np.int32).reshape(-1, 2)
+    check(lib().pa_check_copies(ctypes.byref(pool.c), p.ctypes.data, p.shape[0]))
+
+
+def check_chunks(q_start_loc, seq_lens, num_decode: int, max_q_len: int, total_rows: int) -> None:
+    """Chunk row offsets consistent with lengths, max_q_len and the rows of q (host check)."""
+    loc, n = _host(q_start_loc, np.int32), _host(seq_lens, np.int32)
+    if loc.shape != (n.shape[0] + 1,):
+        raise ValueError("q_start_loc must have one entry more than seq_lens")
+    check(lib().pa_check_chunks(loc.ctypes.data, n.ctypes.data, n.shape[0], int(num_decode),
+                                int(max_q_len), int(total_rows)))
+
+
+def check_shared_prefix(pool: "KVPool", block_tables, seq_lens, num_prefix_blocks: int) -> None:
+    """check_batch plus: every row starts with row 0's first num_prefix_blocks blocks."""
+    t, n = _host(block_tables, np.int32), _host(seq_lens, np.int32)
+    if t.ndim != 2 or n.shape != (t.shape[0],):
+        raise ValueError("block_tables must be [S, maxB] and seq_lens [S]")
+    check(lib().pa_check_shared_prefix(ctypes.byref(pool.c), t.ctypes.data, t.shape[1],
+                                       n.ctypes.data, n.shape[0], int(num_prefix_blocks)))
 
 
 def _need(t: torch.Tensor, name: str, dtype=None, device=True) -> None:
@@ -92,6 +151,8 @@ def cache_write(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
         _need(t, n, pool.io_dtype)
         if tuple(t.shape) != (T, pool.num_kv_heads, pool.head_dim):
             raise ValueError(f"{n} must be [{T}, {pool.num_kv_heads}, {pool.head_dim}]")
+    if _CHECK_INPUTS:
+        check_slots(pool, slot_mapping)
     check(lib().pa_cache_write(ctypes.byref(pool.c), k_new.data_ptr(), v_new.data_ptr(),
                                slot_mapping.data_ptr(), T, _stream()))
 
@@ -102,6 +163,8 @@ def copy_blocks(pool: KVPool, src_dst: torch.Tensor) -> None:
     n = src_dst.shape[0] if src_dst.numel() else 0
     if src_dst.numel() and tuple(src_dst.shape) != (n, 2):
         raise ValueError("src_dst must be [n, 2]")
+    if _CHECK_INPUTS and n:
+        check_copies(pool, src_dst)
     check(lib().pa_copy_blocks(ctypes.byref(pool.c), _ptr(src_dst), n, _stream()))
 
 
@@ -173,6 +236,8 @@ def decode(q: torch.Tensor, pool: KVPool, block_tables: torch.Tensor, seq_lens: 
     if D != pool.head_dim or block_tables.dim() != 2 or block_tables.shape[0] != S \
             or seq_lens.shape != (S,):
         raise ValueError("shape mismatch between q, block_tables and seq_lens")
+    if _CHECK_INPUTS:
+        check_batch(pool, block_tables, seq_lens)
     if plan is None:
         plan = DecodePlan(pool, S, Hq, workers)
     elif (plan.num_seqs, plan.num_q_heads, plan.workers, plan.pool) != (S, Hq, workers, pool):
@@ -214,6 +279,8 @@ def decode_shared_prefix(q: torch.Tensor, pool: KVPool, block_tables: torch.Tens
         n = decode_shared_prefix_workspace_bytes(S, Hq, pool.num_kv_heads, D, pool.block_size,
                                                  num_prefix_blocks, workers)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    if _CHECK_INPUTS:
+        check_shared_prefix(pool, block_tables, seq_lens, num_prefix_blocks)
     check(lib().pa_decode_shared_prefix(out.data_ptr(), q.data_ptr(), ctypes.byref(pool.c),
                                         block_tables.data_ptr(), block_tables.shape[1],
                                         seq_lens.data_ptr(), S, Hq, float(scale),
@@ -245,6 +312,9 @@ def attention_mixed(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.
         n = decode_workspace_bytes(max(num_decode, 1), q.shape[1], pool.num_kv_heads,
                                    pool.head_dim, workers)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    if _CHECK_INPUTS:
+        check_batch(pool, block_tables, seq_lens)
+        check_chunks(q_start_loc, seq_lens, num_decode, max_q_len, q.shape[0])
     check(lib().pa_attention_mixed(out.data_ptr(), q.data_ptr(), q_start_loc.data_ptr(),
                                    seq_lens.data_ptr(), ctypes.byref(pool.c),
                                    block_tables.data_ptr(), block_tables.shape[1], int(num_decode),
@@ -267,6 +337,9 @@ def prefill_chunk(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.Te
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", pool.dtype)
+    if _CHECK_INPUTS:
+        check_batch(pool, block_tables, seq_lens)
+        check_chunks(q_start_loc, seq_lens, 0, max_q_len, q.shape[0])
     check(lib().pa_prefill_chunk(out.data_ptr(), q.data_ptr(), q_start_loc.data_ptr(),
                                  seq_lens.data_ptr(), ctypes.byref(pool.c),
                                  block_tables.data_ptr(), block_tables.shape[1], S, q.shape[1],
@@ -274,7 +347,9 @@ def prefill_chunk(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.Te
     return out
 
 
-__all__ = ["KVPool", "DecodePlan", "attention_mixed", "cache_write", "copy_blocks", "decode",
+__all__ = ["KVPool", "DecodePlan", "attention_mixed", "cache_write", "check_batch", "check_chunks",
+           "check_copies", "check_shared_prefix", "check_slots", "copy_blocks", "decode",
+           "set_input_checks",
            "decode_workspace_bytes", "decode_shared_prefix", "decode_shared_prefix_workspace_bytes",
            "prefill_chunk", "swap_blocks", "swap_in", "swap_out", "PA_SWAP_IN", "PA_SWAP_OUT",
            "PagedKVError"]

@@ -220,3 +220,23 @@ def test_swap_argument_checks():
     assert call(d=d8, h=h8) == -1 and b"scale" in L.pa_last_error()
     # past the host checks the pointers are looked up: fake addresses are refused
     assert call() == -1 and b"pool memory" in L.pa_last_error()
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("-inf"), float("nan")])
+def test_every_attention_call_rejects_bad_scales(scale):
+    """The softmax scale must be finite and > 0 in every attention entry point."""
+    L = lib()
+    p = _pool(num_kv_heads=8)
+    f = ctypes.c_float(scale)
+    need = L.pa_decode_workspace_bytes(2, 8, 8, 128, 0)
+    assert L.pa_decode(16, 16, ctypes.byref(p), 16, 4, 16, 2, 8, f, 0, 16, need, None) == -1
+    assert b"scale" in L.pa_last_error()
+    nsp = L.pa_decode_shared_prefix_workspace_bytes(2, 8, 8, 128, 16, 1, 0)
+    assert L.pa_decode_shared_prefix(16, 16, ctypes.byref(p), 16, 4, 16, 2, 8, f, 1, 0, 16, nsp,
+                                     None) == -1
+    assert b"scale" in L.pa_last_error()
+    assert L.pa_prefill_chunk(16, 16, 16, 16, ctypes.byref(p), 16, 4, 2, 8, 64, f, None) == -1
+    assert b"scale" in L.pa_last_error()
+    assert L.pa_attention_mixed(16, 16, 16, 16, ctypes.byref(p), 16, 4, 1, 1, 8, 64, f, 0, 16,
+                                1 << 24, None) == -1
+    assert b"scale" in L.pa_last_error()

@@ -1,0 +1,137 @@
+"""Host checks of the device-array preconditions (pa_check_*), on the CPU:
+valid batches from the allocator pass, and each kind of bad table, length,
+slot, copy pair or chunk offset is rejected with a message naming it."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_316_amd as pkv
+import workloads
+from paged_kv_cache_316_amd._lib import PaPool, PagedKVError, lib
+from paged_kv_cache_316_amd.runner import run_script
+
+NB, B = 12, 4
+
+
+class _Pool:
+    """Geometry-only stand-in for a KVPool (the checks never touch pool memory)."""
+
+    def __init__(self, num_blocks=NB, block_size=B):
+        self.c = PaPool(16, 32, num_blocks, 2, block_size, 64, 1, 1.0, 1.0)
+
+
+def _raises(fn, *args, match):
+    with pytest.raises(PagedKVError, match=match):
+        fn(*args)
+
+
+def test_valid_batches_from_every_workload_pass():
+    for name in workloads.config_names():
+        wl = workloads.make(name, "small")
+        alloc = pkv.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
+        events = run_script(alloc, wl.ops)
+        pool = _Pool(wl.num_blocks, wl.block_size)
+        tables, lens = alloc.batch_tables(wl.decode_seqs)
+        pkv.check_batch(pool, tables, lens)
+        for ev in events:
+            if ev[0] == "write":
+                pkv.check_slots(pool, ev[1])
+            elif ev[0] == "copy" and len(ev[1]):
+                pkv.check_copies(pool, ev[1])
+
+
+def test_batch_rejects_bad_tables_and_lengths():
+    pool = _Pool()
+    tables = np.array([[3, 7, 0], [1, 2, 0]], dtype=np.int32)
+    lens = np.array([6, 8], dtype=np.int32)  # 2 blocks each of 4 tokens; entry 2 unused
+    pkv.check_batch(pool, tables, lens)
+    bad = tables.copy(); bad[1, 1] = NB
+    _raises(pkv.check_batch, pool, bad, lens, match=r"block_tables\[1\]\[1\]=12 outside")
+    bad = tables.copy(); bad[0, 0] = -1
+    _raises(pkv.check_batch, pool, bad, lens, match=r"block_tables\[0\]\[0\]=-1")
+    # entries past a sequence's blocks are never read: anything goes there
+    junk = tables.copy(); junk[:, 2] = 999
+    pkv.check_batch(pool, junk, lens)
+    _raises(pkv.check_batch, pool, tables, np.array([6, 13], np.int32),
+            match=r"seq_lens\[1\]=13 outside \[0, max_blocks_per_seq \* B = 12\]")
+    _raises(pkv.check_batch, pool, tables, np.array([-1, 8], np.int32), match=r"seq_lens\[0\]=-1")
+    # a longer length reads one more entry, which must then be valid
+    _raises(pkv.check_batch, pool, junk, np.array([9, 8], np.int32), match=r"\[0\]\[2\]=999")
+
+
+def test_slots_reject_out_of_pool_and_duplicates():
+    pool = _Pool()
+    pkv.check_slots(pool, np.array([0, 5, -1, 47, -7], np.int64))
+    _raises(pkv.check_slots, pool, np.array([0, 48], np.int64), match=r"slot_mapping\[1\]=48 >= num_blocks")
+    _raises(pkv.check_slots, pool, np.array([5, 9, 5], np.int64), match=r"slot 5 named by tokens 0 and 2")
+
+
+def test_copies_reject_bad_pairs():
+    pool = _Pool()
+    pkv.check_copies(pool, np.array([[1, 2], [1, 3], [4, 5]], np.int32))  # one source, two copies
+    _raises(pkv.check_copies, pool, np.array([[1, 12]], np.int32), match="outside the pool")
+    _raises(pkv.check_copies, pool, np.array([[-2, 3]], np.int32), match="outside the pool")
+    _raises(pkv.check_copies, pool, np.array([[1, 2], [3, 2]], np.int32), match="destination of two")
+    _raises(pkv.check_copies, pool, np.array([[1, 2], [2, 3]], np.int32), match="both a source")
+    _raises(pkv.check_copies, pool, np.array([[1, 2], [3, 1]], np.int32), match="both a source")
+    _raises(pkv.check_copies, pool, np.array([[4, 4]], np.int32), match="both a source")
+
+
+def test_chunks_reject_bad_offsets():
+    lens = np.array([10, 7, 600, 512], np.int32)
+    loc = np.array([0, 1, 2, 514, 1026], np.int32)  # two decode rows, chunks of 512
+    pkv.check_chunks(loc, lens, 2, 512, 1026)
+    _raises(pkv.check_chunks, np.array([1, 2, 3, 515, 1027], np.int32), lens, 2, 512, 1027,
+            match=r"q_start_loc\[0\]=1")
+    _raises(pkv.check_chunks, np.array([0, 2, 3, 515, 1027], np.int32), lens, 2, 512, 1027,
+            match="decode sequence 0 has 2 rows")
+    _raises(pkv.check_chunks, loc, lens, 2, 511, 1026, match="512 rows > max_q_len=511")
+    _raises(pkv.check_chunks, loc, np.array([10, 7, 600, 500], np.int32), 2, 512, 1026,
+            match="seq_lens=500")
+    _raises(pkv.check_chunks, loc, lens, 2, 512, 1000, match="beyond the 1000 rows")
+    _raises(pkv.check_chunks, np.array([0, 1, 2, 514, 300], np.int32), lens, 2, 512, 1026,
+            match="decreases at sequence 3")
+
+
+def test_shared_prefix_precondition():
+    pool = _Pool()
+    tables = np.array([[3, 7, 1], [3, 7, 2], [3, 7, 5]], np.int32)
+    lens = np.array([9, 12, 8], np.int32)
+    pkv.check_shared_prefix(pool, tables, lens, 2)
+    bad = tables.copy(); bad[2, 1] = 6
+    _raises(pkv.check_shared_prefix, pool, bad, lens, 2, match=r"block_tables\[2\]\[1\]=6 differs")
+    _raises(pkv.check_shared_prefix, pool, tables, np.array([9, 12, 7], np.int32), 2,
+            match=r"seq_lens\[2\]=7 shorter than the 8 shared")
+
+
+def test_null_and_negative_arguments():
+    L = lib()
+    p = _Pool().c
+    assert L.pa_check_batch(ctypes.byref(p), None, 4, None, 2) == -1
+    assert L.pa_check_batch(ctypes.byref(p), None, 4, None, 0) == 0
+    assert L.pa_check_slots(None, None, 1) == -1
+    assert L.pa_check_copies(ctypes.byref(p), None, -1) == -1
+    assert L.pa_check_chunks(None, None, 3, 4, 16, 10) == -1  # num_decode > num_seqs
+    bad_b = _Pool(block_size=6).c
+    assert L.pa_check_slots(ctypes.byref(bad_b), None, 0) == -1
+    assert b"power of two" in L.pa_last_error()
+
+
+def test_checks_run_before_launch_when_enabled(monkeypatch):
+    """With input checks on, a bad table is refused by the binding before the
+    library is asked to launch anything (no device needed)."""
+    import torch
+    pool = pkv.KVPool.__new__(pkv.KVPool)
+    pool.c = _Pool().c
+    pool.head_dim, pool.num_kv_heads, pool.dtype = 64, 2, torch.bfloat16
+    calls = []
+    monkeypatch.setattr(pkv.ops, "_CHECK_INPUTS", True)
+    monkeypatch.setattr(pkv.ops, "_need", lambda *a, **k: None)
+    monkeypatch.setattr(pkv.ops, "DecodePlan", lambda *a, **k: calls.append("plan"))
+    q = torch.zeros(1, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(PagedKVError, match="outside the pool"):
+        pkv.ops.decode(q, pool, torch.tensor([[99]], dtype=torch.int32),
+                       torch.tensor([3], dtype=torch.int32), 0.1, plan=None, out=q)
+    assert calls == []  # refused before any workspace was set up
