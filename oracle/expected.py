@@ -25,13 +25,27 @@ NAN_BITS = {"f32": 0x7FC00001, "bf16": 0x7FC1, "fp8_e4m3": 0x7F}
 _MIRROR_DTYPE = {"f32": np.float32, "bf16": np.uint16, "fp8_e4m3": np.uint8}
 
 
+_ALL_BF16 = (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32)  # every bf16 value
+
+
+def _code_table(scale: float) -> np.ndarray:
+    """fp8.quantize of every bf16 bit pattern: quantize acts on each value
+    alone, so a bf16 array's codes are this table indexed by its bits."""
+    return fp8.quantize(_ALL_BF16, scale)
+
+
+def _quantize_bf16(wl, rows, scale):
+    if rows.dtype == np.uint16:  # bf16 bits (all FP8 workloads draw bf16 rows)
+        return _code_table(scale)[rows]
+    return fp8.quantize(wl.values(rows), scale)
+
+
 def stored_rows(wl, rows_k, rows_v):
     """What the pool holds for these K/V rows: the rows themselves, or their
     FP8 codes under the pool's scales."""
     if wl.pool_dtype != "fp8_e4m3":
         return rows_k, rows_v
-    return (fp8.quantize(wl.values(rows_k), wl.k_scale),
-            fp8.quantize(wl.values(rows_v), wl.v_scale))
+    return _quantize_bf16(wl, rows_k, wl.k_scale), _quantize_bf16(wl, rows_v, wl.v_scale)
 
 
 def logical_kv(wl, seq):
@@ -41,7 +55,8 @@ def logical_kv(wl, seq):
         k, v = wl.logical_kv(seq)
         return k.astype(np.float64), v.astype(np.float64)
     ck, cv = stored_rows(wl, wl.rows_k[r], wl.rows_v[r])
-    return fp8.dequantize(ck, wl.k_scale), fp8.dequantize(cv, wl.v_scale)
+    return (fp8.dequantize(np.arange(256), wl.k_scale)[ck],
+            fp8.dequantize(np.arange(256), wl.v_scale)[cv])
 
 
 def pool_after(wl, stop_before: Optional[str] = None):

@@ -4,6 +4,8 @@ results with the oracle."""
 
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 import torch
 
@@ -91,3 +93,24 @@ def assert_close(wl, got: np.ndarray, want: np.ndarray, what: str = "") -> dict:
         bad = err > bar
         assert not bad.any(), f"{what}: {int(bad.sum())} elements out of tolerance, {stats}"
     return stats
+
+
+# Full-size workloads take seconds to draw and their fp64 oracle results
+# seconds more; several test files compare against the same ones, so each is
+# drawn and computed once per test session.
+@functools.lru_cache(maxsize=None)
+def full_workload(name: str):
+    import workloads
+    return workloads.make(name, "full")
+
+
+@functools.lru_cache(maxsize=None)
+def full_decode_out(name: str) -> np.ndarray:
+    from oracle.expected import decode_out
+    return decode_out(full_workload(name))
+
+
+@functools.lru_cache(maxsize=None)
+def full_prefill_out(name: str) -> np.ndarray:
+    from oracle.expected import prefill_out
+    return prefill_out(full_workload(name))

@@ -14,9 +14,10 @@ import torch
 
 import paged_kv_cache_316_amd as pkv
 import workloads
-from oracle.expected import decode_out, pool_after, stored_rows
+from oracle.expected import decode_out, pool_after
 
-from gpu_util import Loaded, assert_close, out_f64, pool_bits, to_device
+from gpu_util import (Loaded, assert_close, full_decode_out, full_workload, out_f64, pool_bits,
+                      to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -186,7 +187,9 @@ def _single_seq(L, Hq, Hkv, D, B, dtype, seed, zero_keys=False):
     (64, 8, 16, 4), (128, 4, 16, 2), (64, 16, 32, 2),
     # MHA with an odd head count (FP8 pools pair KV heads only when even);
     # groups of 8 over 2 KV heads, blocks of 16 and 8
-    (128, 16, 3, 3), (128, 16, 16, 2), (64, 8, 16, 2)])
+    (128, 16, 3, 3), (128, 16, 16, 2), (64, 8, 16, 2),
+    # blocks of 64 tokens (several tiles per block), MHA and groups of 8
+    (128, 64, 4, 4), (128, 64, 16, 2)])
 def test_edge_lengths(dtype, L, D, B, Hq, Hkv):
     from oracle.attention import decode_attention
     q, k, v, got = _single_seq(L, Hq, Hkv, D, B, dtype, seed=L * 7 + D)
@@ -246,32 +249,21 @@ FULL = ["tiny", "llama13b", "cow", "cow504", "beam", "prefix", "llama70b", "llam
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
-    """Full-size workloads in the default launch configuration: the pool bits
-    are checked on sampled blocks, and the decode output on sampled sequences
-    (shortest, longest and seeded picks) against the oracle."""
-    wl = workloads.make(name, "full")
+def test_full_size_every_row(name):
+    """Full-size workloads in the default launch configuration (the one the
+    bench times): every output row of every sequence against the oracle, and
+    both pools byte for byte against the oracle's mirror (every cache write
+    and copy of the op script right, nothing else touched)."""
+    wl = full_workload(name)
     _note(f"full-size parity: {name}, S={len(wl.decode_seqs)}")
     g = Loaded(wl)
     out = g.decode()
-    lens = wl.seq_lens
-    rng = np.random.default_rng(77)
-    idx = sorted(set([int(np.argmin(lens)), int(np.argmax(lens))] +
-                     [int(x) for x in rng.choice(len(lens), size=min(6, len(lens)), replace=False)]))
-    got = out_f64(out[torch.tensor(idx, device="cuda")])
-    want = decode_out(wl, idx)
-    stats = assert_close(wl, got, want, name)
-    _note(f"  sampled {idx}: {stats}")
-    # every sequence's table reads back its logical K rows (sampled blocks, bitwise)
-    tables = g.tables.cpu().numpy()
-    kb = pool_bits(g.pool.k)
-    for i in idx:
-        seq = wl.decode_seqs[i]
-        L = int(lens[i])
-        t = np.arange(L)
-        rows = kb[tables[i, t // wl.block_size], :, t % wl.block_size, :]
-        stored_k, _ = stored_rows(wl, wl.rows_k[wl.hist[seq]], wl.rows_v[wl.hist[seq]][:0])
-        assert np.array_equal(rows, stored_k.view(rows.dtype))
+    stats = assert_close(wl, out_f64(out), full_decode_out(name), name)
+    _note(f"  all {len(wl.decode_seqs)} rows: {stats}")
+    mirror, _, _ = pool_after(wl)
+    kb, vb = pool_bits(g.pool.k), pool_bits(g.pool.v)
+    assert np.array_equal(kb, mirror.k.view(kb.dtype)), f"{name}: K pool differs from the mirror"
+    assert np.array_equal(vb, mirror.v.view(vb.dtype)), f"{name}: V pool differs from the mirror"
 
 
 def test_stream_read_probe_runs():

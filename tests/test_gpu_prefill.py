@@ -14,7 +14,7 @@ import paged_kv_cache_316_amd as pkv
 from oracle.attention import prefill_attention
 from oracle.expected import prefill_out
 
-from gpu_util import Loaded, assert_close, out_f64, to_device
+from gpu_util import Loaded, assert_close, full_prefill_out, full_workload, out_f64, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -74,7 +74,7 @@ def test_head_groupings(Hq, Hkv):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("B", [4, 8, 16, 32])
+@pytest.mark.parametrize("B", [4, 8, 16, 32, 64, 128])
 def test_block_sizes_and_head_dims(D, B):
     got, want = _run_random([200, 65, 513], [64, 1, 150], 8, 2, D, B, seed=D + B)
     assert_close(_BF16, got, want, f"D={D} B={B}")
@@ -114,19 +114,16 @@ def test_workload_small():
 
 
 @pytest.mark.slow
-def test_workload_full_sampled():
-    """8 x 512-row chunks, 64/8 heads, in the launch configuration the bench times;
-    sampled rows (first, last, seeded) of every chunk against the oracle."""
-    wl = workloads.make("llama70b", "full")
+def test_workload_full_every_row():
+    """8 x 512-row chunks, 64/8 heads, in the launch configuration the bench
+    times: every row of every chunk against the oracle."""
+    wl = full_workload("llama70b")
     print(f"full prefill parity: {len(wl.prefill_seqs)} chunks", flush=True)
     g = Loaded(wl)
     q, loc, lens, tables = _prefill_inputs(g, wl)
     out = out_f64(pkv.prefill_chunk(q, loc, lens, g.pool, tables, wl.prefill_len, wl.scale))
-    rng = np.random.default_rng(9)
-    rows = sorted(set([0, 31, 32, wl.prefill_len - 1] +
-                      [int(x) for x in rng.choice(wl.prefill_len, size=4, replace=False)]))
+    want = full_prefill_out("llama70b")
     C = wl.prefill_len
     for j in range(len(wl.prefill_seqs)):
-        want = prefill_out(wl, [j], rows)
-        got = out[[j * C + r for r in rows]]
-        assert_close(wl, got, want, f"chunk {j}")
+        stats = assert_close(wl, out[j * C:(j + 1) * C], want[j * C:(j + 1) * C], f"chunk {j}")
+        print(f"  chunk {j} (ends at {int(wl.prefill_start[j]) + C}): {stats}", flush=True)

@@ -14,7 +14,7 @@ import workloads
 from oracle.attention import decode_attention
 from oracle.expected import decode_out
 
-from gpu_util import Loaded, assert_close, out_f64
+from gpu_util import Loaded, assert_close, full_decode_out, full_workload, out_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -79,22 +79,17 @@ def test_no_shared_blocks_is_plain_decode():
 
 
 @pytest.mark.slow
-def test_prefix_workload_full_sampled():
-    """Full size in the default launch configuration: sampled rows against the
-    oracle, and every row within the bar of the plain decode's output."""
-    wl = workloads.make("prefix", "full")
+def test_prefix_workload_full_every_row():
+    """Full size in the default launch configuration: every row against the
+    oracle, and against the plain decode's output."""
+    wl = full_workload("prefix")
     g = Loaded(wl)
     P = _shared_blocks(g, wl)
     _note(f"shared-prefix decode: prefix full, S={len(wl.decode_seqs)} P={P}")
     out = pkv.decode_shared_prefix(g.q, g.pool, g.tables, g.lens, P, wl.scale)
     torch.cuda.synchronize()
-    lens = wl.seq_lens
-    rng = np.random.default_rng(78)
-    idx = sorted(set([int(np.argmin(lens)), int(np.argmax(lens))] +
-                     [int(x) for x in rng.choice(len(lens), size=6, replace=False)]))
-    got = out_f64(out[torch.tensor(idx, device="cuda")])
-    stats = assert_close(wl, got, decode_out(wl, idx), "prefix full")
-    _note(f"  sampled {idx}: {stats}")
+    stats = assert_close(wl, out_f64(out), full_decode_out("prefix"), "prefix full")
+    _note(f"  all rows: {stats}")
     assert_close(wl, out_f64(out), out_f64(g.decode()), "prefix full vs plain decode")
 
 
