@@ -210,6 +210,28 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_noalloc — pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, kernels and results as pa_decode with
+ * the same num_workers, but no workspace argument: the scratch lives in a
+ * static device array of the library, pa_decode_noalloc_scratch_bytes()
+ * (32 MiB) per device, held by every device the library runs on until the
+ * process ends. The caller still passes inputs and outputs. The call
+ * allocates nothing; its first call on a device looks up that device's copy
+ * of the array. A call whose workspace (pa_decode_workspace_bytes) exceeds
+ * the array returns PA_ERR_WORKSPACE with nothing queued; the default worker
+ * count needs at most 16.3 MiB on 256 compute units. All calls on one device
+ * share its array: calls that overlap on one device (other streams, other
+ * host threads) race and must be serialized by the caller.
+ */
+pa_status pa_decode_noalloc(void* out, const void* q, const pa_pool* pool,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                            float scale, int32_t num_workers, void* stream);
+/* Bytes of the static scratch array behind pa_decode_noalloc. */
+size_t pa_decode_noalloc_scratch_bytes(void);
+
+/*
  * Workspace needed by pa_decode_shared_prefix, in bytes (0 for invalid sizes).
  * block_size and num_prefix_blocks size the partials of the shared part.
  */

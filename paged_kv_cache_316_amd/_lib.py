@@ -47,6 +47,9 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode": (c_int32, [c_void_p, c_void_p, _P(PaPool), c_void_p, c_int32, c_void_p, c_int32,
                             c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
+    "pa_decode_noalloc": (c_int32, [c_void_p, c_void_p, _P(PaPool), c_void_p, c_int32, c_void_p,
+                                    c_int32, c_int32, c_float, c_int32, c_void_p]),
+    "pa_decode_noalloc_scratch_bytes": (c_size_t, []),
     "pa_decode_shared_prefix_workspace_bytes": (c_size_t, [c_int32] * 7),
     "pa_decode_shared_prefix": (c_int32, [c_void_p, c_void_p, _P(PaPool), c_void_p, c_int32,
                                           c_void_p, c_int32, c_int32, c_float, c_int32, c_int32,

@@ -7,6 +7,7 @@
 #include <cstring>
 #include <vector>
 
+#include "api_internal.h"
 #include "device.h"
 #include "pagedkv.h"
 #include "status.h"
@@ -180,6 +181,42 @@ DecodeArgs decode_args(void* out, const void* q, const pa_pool* pool, const int3
 
 }  // namespace
 
+pa_status decode_check(const DecodeCall& c, const char* who, size_t* need) {
+  *need = 0;
+  const pa_pool* pool = c.pool;
+  if (pa_status s = check_pool(pool, who)) return s;
+  if (c.num_seqs < 0 || c.max_blocks_per_seq <= 0 || c.num_q_heads <= 0)
+    return fail(PA_ERR_INVALID, "%s: num_seqs=%d max_blocks_per_seq=%d num_q_heads=%d", who,
+                c.num_seqs, c.max_blocks_per_seq, c.num_q_heads);
+  if (c.num_seqs == 0) return PA_OK;
+  if (!c.out || !c.q || !c.block_tables || !c.seq_lens)
+    return fail(PA_ERR_INVALID, "%s: out/q/block_tables/seq_lens is NULL", who);
+  if (c.num_q_heads % pool->num_kv_heads)
+    return fail(PA_ERR_INVALID, "%s: num_q_heads=%d not a multiple of num_kv_heads=%d", who,
+                c.num_q_heads, pool->num_kv_heads);
+  if (pa_status s = check_scale(c.scale, who)) return s;
+  if (c.num_workers < 0 || c.num_workers > (1 << 24))
+    return fail(PA_ERR_INVALID, "%s: num_workers=%d out of range", who, c.num_workers);
+  if ((reinterpret_cast<uintptr_t>(c.out) | reinterpret_cast<uintptr_t>(c.q) |
+       reinterpret_cast<uintptr_t>(pool->k_pool) | reinterpret_cast<uintptr_t>(pool->v_pool)) & 15)
+    return fail(PA_ERR_INVALID, "%s: out/q/pools must be 16-byte aligned", who);
+  const int32_t G = c.num_q_heads / pool->num_kv_heads;
+  if (!decode_supported(pool->dtype, pool->head_dim, G))
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype=%d head_dim=%d group=%d not built", who,
+                pool->dtype, pool->head_dim, G);
+  *need = decode_layout(c.num_seqs, c.num_q_heads, pool->num_kv_heads, pool->head_dim,
+                        c.num_workers).total();
+  return PA_OK;
+}
+
+pa_status decode_launch(const DecodeCall& c, void* workspace, void* stream, const char* who) {
+  const DecodeLayout lay = decode_layout(c.num_seqs, c.num_q_heads, c.pool->num_kv_heads,
+                                         c.pool->head_dim, c.num_workers);
+  const DecodeArgs a = decode_args(c.out, c.q, c.pool, c.block_tables, c.max_blocks_per_seq,
+                                   c.seq_lens, c.num_seqs, c.num_q_heads, c.scale, lay, workspace);
+  return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)), who);
+}
+
 }  // namespace pa
 
 using pa::fail;
@@ -318,36 +355,18 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t
                     int32_t num_q_heads, float scale, int32_t num_workers, void* workspace,
                     size_t workspace_bytes, void* stream) {
   pa::clear_error();
-  if (pa_status s = pa::check_pool(pool, "pa_decode")) return s;
-  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0)
-    return fail(PA_ERR_INVALID, "pa_decode: num_seqs=%d max_blocks_per_seq=%d num_q_heads=%d",
-                num_seqs, max_blocks_per_seq, num_q_heads);
+  const char* who = "pa_decode";
+  const pa::DecodeCall c{out, q, pool, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                         num_q_heads, scale, num_workers};
+  size_t need = 0;
+  if (pa_status s = pa::decode_check(c, who, &need)) return s;
   if (num_seqs == 0) return PA_OK;
-  if (!out || !q || !block_tables || !seq_lens)
-    return fail(PA_ERR_INVALID, "pa_decode: out/q/block_tables/seq_lens is NULL");
-  if (num_q_heads % pool->num_kv_heads)
-    return fail(PA_ERR_INVALID, "pa_decode: num_q_heads=%d not a multiple of num_kv_heads=%d",
-                num_q_heads, pool->num_kv_heads);
-  if (pa_status s = pa::check_scale(scale, "pa_decode")) return s;
-  if (num_workers < 0 || num_workers > (1 << 24))
-    return fail(PA_ERR_INVALID, "pa_decode: num_workers=%d out of range", num_workers);
-  if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
-       reinterpret_cast<uintptr_t>(pool->k_pool) | reinterpret_cast<uintptr_t>(pool->v_pool)) & 15)
-    return fail(PA_ERR_INVALID, "pa_decode: out/q/pools must be 16-byte aligned");
-  const int32_t G = num_q_heads / pool->num_kv_heads;
-  if (!pa::decode_supported(pool->dtype, pool->head_dim, G))
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: dtype=%d head_dim=%d group=%d not built",
-                pool->dtype, pool->head_dim, G);
-  const pa::DecodeLayout lay =
-      pa::decode_layout(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim, num_workers);
-  if (!workspace || workspace_bytes < lay.total())
+  if (!workspace || workspace_bytes < need)
     return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes, %zu needed",
-                workspace ? workspace_bytes : size_t(0), lay.total());
+                workspace ? workspace_bytes : size_t(0), need);
   if (reinterpret_cast<uintptr_t>(workspace) & 15)
     return fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
-  const pa::DecodeArgs a = pa::decode_args(out, q, pool, block_tables, max_blocks_per_seq,
-                                           seq_lens, num_seqs, num_q_heads, scale, lay, workspace);
-  return pa::hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)), "pa_decode");
+  return pa::decode_launch(c, workspace, stream, who);
 }
 
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

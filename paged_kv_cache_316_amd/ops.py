@@ -252,6 +252,32 @@ def decode(q: torch.Tensor, pool: KVPool, block_tables: torch.Tensor, seq_lens: 
     return out
 
 
+def decode_noalloc(q: torch.Tensor, pool: KVPool, block_tables: torch.Tensor,
+                   seq_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                   workers: int = 0) -> torch.Tensor:
+    """pa_decode_noalloc: decode with the library's static scratch array instead of a
+    workspace; `out` [S, Hq, D] is the caller's (nothing is allocated here)."""
+    _need(q, "q", pool.io_dtype)
+    _need(block_tables, "block_tables", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(out, "out", pool.io_dtype)
+    S, Hq, D = q.shape
+    if D != pool.head_dim or block_tables.dim() != 2 or block_tables.shape[0] != S \
+            or seq_lens.shape != (S,) or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, out, block_tables and seq_lens")
+    if _CHECK_INPUTS:
+        check_batch(pool, block_tables, seq_lens)
+    check(lib().pa_decode_noalloc(out.data_ptr(), q.data_ptr(), ctypes.byref(pool.c),
+                                  block_tables.data_ptr(), block_tables.shape[1],
+                                  seq_lens.data_ptr(), S, Hq, float(scale), int(workers),
+                                  _stream()))
+    return out
+
+
+def decode_noalloc_scratch_bytes() -> int:
+    return int(lib().pa_decode_noalloc_scratch_bytes())
+
+
 def decode_shared_prefix_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
                                          head_dim: int, block_size: int, num_prefix_blocks: int,
                                          workers: int = 0) -> int:
@@ -349,7 +375,7 @@ def prefill_chunk(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.Te
 
 __all__ = ["KVPool", "DecodePlan", "attention_mixed", "cache_write", "check_batch", "check_chunks",
            "check_copies", "check_shared_prefix", "check_slots", "copy_blocks", "decode",
-           "set_input_checks",
+           "decode_noalloc", "decode_noalloc_scratch_bytes", "set_input_checks",
            "decode_workspace_bytes", "decode_shared_prefix", "decode_shared_prefix_workspace_bytes",
            "prefill_chunk", "swap_blocks", "swap_in", "swap_out", "PA_SWAP_IN", "PA_SWAP_OUT",
            "PagedKVError"]

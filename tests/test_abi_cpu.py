@@ -240,3 +240,23 @@ def test_every_attention_call_rejects_bad_scales(scale):
     assert L.pa_attention_mixed(16, 16, 16, 16, ctypes.byref(p), 16, 4, 1, 1, 8, 64, f, 0, 16,
                                 1 << 24, None) == -1
     assert b"scale" in L.pa_last_error()
+
+
+def test_noalloc_decode_argument_checks():
+    """pa_decode_noalloc checks its arguments like pa_decode and refuses a call
+    whose workspace would not fit its static scratch array, before any launch."""
+    L = lib()
+    p = _pool(num_kv_heads=8)
+    cap = L.pa_decode_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    f = ctypes.c_float(0.1)
+    call = lambda out=16, Hq=8, workers=0, scale=f, S=2: L.pa_decode_noalloc(
+        out, 16, ctypes.byref(p), 16, 4, 16, S, Hq, scale, workers, None)
+    assert call(S=0, out=None) == 0                       # nothing to do
+    assert call(Hq=12) == -1 and b"multiple" in L.pa_last_error()
+    assert call(out=None) == -1
+    assert call(scale=ctypes.c_float(-1.0)) == -1
+    assert call(workers=-2) == -1
+    # G = 1 MHA: 2 * W * 2 * (128 * 4 + 8) + 16 W bytes; 1 << 14 workers need 34.3 MB
+    assert L.pa_decode_workspace_bytes(2, 8, 8, 128, 1 << 14) > cap
+    assert call(workers=1 << 14) == -5 and b"scratch" in L.pa_last_error()
