@@ -57,7 +57,8 @@ def log(msg):
 
 
 KERNEL_SOURCES = {
-    "decode": ("decode.hip", "cache_ops.hip", "device.h"),
+    "decode": ("decode.hip", "device.h"),
+    "cache_ops": ("cache_ops.hip", "device.h"),
     "prefill": ("prefill.hip", "device.h"),
     "prefix_shared": ("prefix.hip", "decode.hip", "device.h"),
 }
@@ -196,13 +197,13 @@ class Loaded:
 
 def _stats_us(ms):
     import numpy as np
-    return {"mean": round(float(ms.mean()) * 1e3, 2),
+    return {"samples": int(len(ms)), "mean": round(float(ms.mean()) * 1e3, 2),
             "p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
             "p50": round(float(np.percentile(ms, 50)) * 1e3, 2),
             "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)}
 
 
-EVENT_EVERY = 8  # timed steps per step that records HIP events
+EVENT_SAMPLES = 60  # event-recorded calls per row, in a pass of their own
 # Extra rows run a few tens of steps right after seconds of host-side set-up
 # with the GPU idle; measured that way the shortest of them (the FP8 decode,
 # ~10 ms of work in all) read 8 % slow against the same call after a longer
@@ -212,15 +213,14 @@ EXTRA_ROW_WARM_S = 0.25
 _warm_s = 0.0
 
 
-def time_steps(step, steps, warmup, event_every=EVENT_EVERY):
+def time_steps(step, steps, warmup, event_samples=EVENT_SAMPLES):
     """Run warmup steps (at least `warmup`, and for the extra rows at least
     _warm_s seconds of them), then exactly `steps` timed steps bracketed by
-    synchronisation.
-    Every `event_every`-th timed step also records 3 events (before, between its
-    two calls, after) on the launch stream: the per-call durations are the means
-    over those sampled steps. (An event record costs about 3 us of stream time
-    on this device, so recording them on every step would inflate the step
-    time by some 4 %.)"""
+    synchronisation, with no events among them. Then, in a separate pass,
+    `event_samples` more steps that each record 3 events on the launch stream
+    (before, between the step's two calls, after): the per-call durations are
+    taken from those. (An event record costs about 3 us of stream time on this
+    device, so the timed steps carry none.)"""
     import numpy as np
     import torch
     for i in range(warmup):
@@ -233,16 +233,18 @@ def time_steps(step, steps, warmup, event_every=EVENT_EVERY):
                 step(i, None)
                 i += 1
             torch.cuda.synchronize()
-    sampled = list(range(0, steps, event_every))
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
-        step(i, evs.get(i))
+        step(i, None)
     torch.cuda.synchronize()
     total = time.perf_counter() - t_start
-    first = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in sampled])
-    second = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in sampled])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(event_samples)]
+    for k in range(event_samples):
+        step(steps + k, evs[k])
+    torch.cuda.synchronize()
+    first = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    second = np.array([e[1].elapsed_time(e[2]) for e in evs])
     return total * 1e3 / steps, first, second
 
 
@@ -433,7 +435,7 @@ def mixed_row(ld, steps, warmup, workers):
             fn(p)
             if ev is not None:
                 ev[2].record(stream)
-        return time_steps(step, steps, warmup, event_every=1)[2]  # per-call durations
+        return time_steps(step, steps, warmup)[2]  # per-call durations
 
     m_ms = timed(lambda p: pkv.attention_mixed(q, loc, lens, p, tables, nd, C, wl.scale, workers,
                                                out=out, workspace=ws))
@@ -548,6 +550,148 @@ def stream_read_ceiling(gib: int = 4):
             "kernel": "pa_probe_stream_read (16-byte non-temporal loads, 8 KB contiguous runs per wave, 8 in flight per lane)"}
 
 
+class Relaid:
+    """The decode batch of a loaded workload laid out again: the same sequences
+    and K/V values in a new pool of another block size and/or placement,
+    optionally only the first kv_heads KV heads (and their query heads). Set
+    up through the library: its block allocator gives the slots (distinct
+    token ids per sequence, so no block is shared by the prefix hash) and
+    pa_cache_write stores the rows."""
+
+    def __init__(self, ld, block_size, placement="random", kv_heads=None, replicas=2, seed=7):
+        import math
+        import numpy as np
+        import torch
+        import paged_kv_cache_316_amd as pkv
+        wl = ld.wl
+        self.wl, self.block_size, self.placement = wl, block_size, placement
+        B = block_size
+        lens = ld.lens.astype(np.int64)
+        S = len(lens)
+        Hkv = kv_heads or wl.num_kv_heads
+        G = wl.num_q_heads // wl.num_kv_heads
+        self.num_kv_heads, self.num_q_heads = Hkv, Hkv * G
+        need = int(sum(-(-int(L) // B) for L in lens))
+        if placement == "contiguous":  # FIFO from 0, 1, 2, ...: each sequence's blocks in order
+            num_blocks, order = need, np.arange(need, dtype=np.int32)
+        else:
+            num_blocks = int(math.ceil(1.1 * need))
+            order = np.random.default_rng(seed).permutation(num_blocks).astype(np.int32)
+        alloc = pkv.BlockAllocator(num_blocks, B, order)
+        slots, rows = [], []
+        for i, seq in enumerate(wl.decode_seqs):
+            L = int(lens[i])
+            _, sl = alloc.allocate(i, (np.arange(L) + (i << 16)).astype(np.int32))
+            slots.append(sl)
+            rows.append(np.asarray(wl.hist[seq][:L]))
+        slots, rows = np.concatenate(slots), np.concatenate(rows)
+        pool_dt = {"f32": torch.float32, "bf16": torch.bfloat16,
+                   "fp8_e4m3": torch.float8_e4m3fn}[wl.pool_dtype]
+        pool = pkv.KVPool.empty(num_blocks, Hkv, B, wl.head_dim, pool_dt,
+                                k_scale=wl.k_scale, v_scale=wl.v_scale)
+        for a in range(0, len(slots), 1 << 15):
+            r = rows[a:a + (1 << 15)]
+            k = np.ascontiguousarray(wl.rows_k[r][:, :Hkv])
+            v = np.ascontiguousarray(wl.rows_v[r][:, :Hkv])
+            dev = (lambda x: torch.from_numpy(x).cuda()) if wl.dtype == "f32" else \
+                  (lambda x: torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16))
+            pkv.cache_write(pool, dev(k), dev(v), torch.from_numpy(slots[a:a + (1 << 15)]).cuda())
+        self.pools = [pool] + [pkv.KVPool(pool.k.clone(), pool.v.clone(), wl.k_scale, wl.v_scale)
+                               for _ in range(replicas - 1)]
+        tables, lens32 = alloc.batch_tables(list(range(S)))
+        self.lens = lens32
+        self.tables_d = torch.from_numpy(tables).cuda()
+        self.lens_d = torch.from_numpy(lens32).cuda()
+        self.q = ld.q[:, :self.num_q_heads].contiguous()
+        self.per_tok = 2 * Hkv * wl.head_dim * wl.elt_bytes
+        self.kv_bytes = float(lens.sum()) * self.per_tok
+        self.waste_bytes = float(sum(-(-int(L) // B) * B - int(L) for L in lens)) * self.per_tok
+        self.pool_bytes = float(num_blocks) * B * self.per_tok
+        torch.cuda.synchronize()
+
+    def decode_time(self, steps, warmup, workers):
+        import torch
+        import paged_kv_cache_316_amd as pkv
+        S = len(self.lens)
+        plans = [pkv.DecodePlan(p, S, self.num_q_heads, workers) for p in self.pools]
+        stream = torch.cuda.current_stream()
+
+        def step(i, ev):
+            j = i % len(self.pools)
+            if ev is not None:
+                ev[0].record(stream)
+                ev[1].record(stream)
+            pkv.decode(self.q, self.pools[j], self.tables_d, self.lens_d, self.wl.scale, workers,
+                       plan=plans[j])
+            if ev is not None:
+                ev[2].record(stream)
+        ms_step, _, d_ms = time_steps(step, steps, warmup)
+        return ms_step, d_ms, plans[0].out
+
+
+def layout_rows(ld, steps, warmup, workers):
+    """The pages' two kernel claims on the LLaMA-13B-shaped batch: paged access
+    costs little against contiguous storage ("LLM inference engine internals",
+    section 2.4, closing paragraph), and small blocks read less efficiently
+    while large ones waste the unused part of each sequence's last block
+    ("vLLM PagedAttention explained", section 8.1). The same sequences and
+    values are laid out with 8-, 16-, 32- and 64-token blocks at random
+    placement, and with 16-token blocks in order (each sequence's blocks
+    consecutive in the pool)."""
+    import gc
+    import torch
+    rows, base_out, times = {}, None, {}
+    for B, placement in ((16, "random"), (16, "contiguous"), (8, "random"), (32, "random"),
+                         (64, "random")):
+        r = Relaid(ld, B, placement)
+        ms_step, d_ms, out = r.decode_time(steps, warmup, workers)
+        t = float(d_ms.mean()) * 1e-3
+        times[(B, placement)] = t
+        out = out.clone()
+        if base_out is None:
+            base_out = out
+        gbps = r.kv_bytes / t / 1e9
+        name = ("decode_llama13b_contiguous" if placement == "contiguous"
+                else f"decode_llama13b_B{B}")
+        rows[name] = {
+            "block_size": B, "placement": placement, "decode_us": _stats_us(d_ms),
+            "kv_bytes": int(r.kv_bytes), "decode_kv_gbps": round(gbps, 2),
+            "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+            "last_block_waste_bytes": int(r.waste_bytes),
+            "last_block_waste_pct_of_pool_use": round(100 * r.waste_bytes /
+                                                      (r.kv_bytes + r.waste_bytes), 3),
+            "pool_bytes": int(r.pool_bytes),
+            # the kernels' arithmetic depends only on logical positions (16-token
+            # tiles), so every layout gives the same bits
+            "output_bitwise_equal_to_B16_random": bool(torch.equal(out.view(torch.int16),
+                                                                   base_out.view(torch.int16)))}
+        del r
+        gc.collect()
+        torch.cuda.empty_cache()
+    t_rand, t_cont = times[(16, "random")], times[(16, "contiguous")]
+    rows["decode_llama13b_contiguous"]["paged_random_vs_contiguous_overhead_pct"] = \
+        round(100 * (t_rand / t_cont - 1), 2)
+    return rows
+
+
+def tp_shard_row(ld, steps, warmup, workers):
+    """One GPU's share of the Llama-2-70B-shaped layer under 4-way tensor
+    parallelism as the pages describe it ("vLLM PagedAttention explained",
+    section 6: every GPU holds the same block tables and its own heads' KV):
+    16 query and 2 KV heads, the same sequences and tables."""
+    r = Relaid(ld, ld.wl.block_size, "random", kv_heads=ld.wl.num_kv_heads // 4)
+    ms_step, d_ms, _ = r.decode_time(steps, warmup, workers)
+    t = float(d_ms.mean()) * 1e-3
+    gbps = r.kv_bytes / t / 1e9
+    return {"workload": "Llama-2-70B-shaped layer, one of 4 tensor-parallel shards: 256 seqs, "
+                        "16 q / 2 KV heads x 128, bf16, block 16, lengths log-uniform [128,8192]",
+            "num_q_heads": r.num_q_heads, "num_kv_heads": r.num_kv_heads,
+            "decode_us": _stats_us(d_ms), "kv_bytes": int(r.kv_bytes),
+            "decode_kv_gbps": round(gbps, 2), "tokens_per_s": round(len(r.lens) / t, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}}
+
+
 def decode_row(ld, steps, warmup, workers, path="plain"):
     step = (decode_step_fn(ld, workers) if path == "plain"
             else shared_prefix_step_fn(ld, workers, shared_prefix_blocks(ld)))
@@ -568,7 +712,7 @@ def decode_row(ld, steps, warmup, workers, path="plain"):
 
 
 def prefill_row(ld, steps, warmup):
-    ms_step, w_ms, p_ms = time_steps(prefill_step_fn(ld), steps, warmup, event_every=1)
+    ms_step, w_ms, p_ms = time_steps(prefill_step_fn(ld), steps, warmup)
     wl = ld.wl
     flops = 4.0 * wl.head_dim * wl.num_q_heads * ld.p_keys
     tflops = flops / (float(p_ms.mean()) * 1e-3) / 1e12
@@ -596,7 +740,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-rows", action="store_true",
                     help="skip the Llama-2-70B-shaped GQA decode, chunked-prefill, mixed-step, "
-                         "FP8-KV decode, block-swap, shared-block and shared-prefix decode rows")
+                         "FP8-KV decode, block-swap, block-layout, tensor-parallel-shard, "
+                         "shared-block and shared-prefix decode rows")
     ap.add_argument("--rows", default="",
                     help="comma-separated extra rows to run (default: all), e.g. "
                          "prefill_llama70b,swap_llama13b")
@@ -666,6 +811,7 @@ def main():
         "stream_read_ceiling": ceiling,
         "pct_of_stream_ceiling": round(100 * row["decode_kv_gbps"] / ceiling["gbps"], 2),
         "prefill_source_hash": kernel_source_hash("prefill"),
+        "cache_ops_source_hash": kernel_source_hash("cache_ops"),
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
@@ -718,6 +864,14 @@ def main():
             f["tokens_per_s_model_equiv"] = round(f["tokens_per_s"] / MODEL_LAYERS["llama13b_fp8"], 1)
             f["pct_of_stream_ceiling"] = round(100 * f["decode_kv_gbps"] / ceiling["gbps"], 2)
             f["workload"] = WORKLOAD_TEXT["llama13b_fp8"]
+        if any(want(n) for n in ("decode_llama13b_contiguous", "decode_llama13b_B8",
+                                 "decode_llama13b_B16", "decode_llama13b_B32",
+                                 "decode_llama13b_B64", "layouts")):
+            switch("llama13b", 1)
+            rows.update(layout_rows(ld, short, args.warmup, args.workers))
+        if want("decode_llama70b_tp4_shard"):
+            switch("llama70b", 1)
+            rows["decode_llama70b_tp4_shard"] = tp_shard_row(ld, short, args.warmup, args.workers)
         for name in ("cow", "cow504", "beam"):  # shared blocks, plain decode
             if want(f"decode_{name}"):
                 switch(name)
