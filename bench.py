@@ -305,22 +305,69 @@ def unique_kv_bytes(ld):
     return float(sum(filled.values())) * per_tok
 
 
+GROUP_SIZE = {"cow": 3, "cow504": 3, "beam": 4}  # samples per prompt, beam width
+
+
 def shared_block_row(ld, steps, warmup, workers):
-    """Plain decode of a batch with shared blocks: logical and unique bytes."""
+    """A batch of forked sequences (parallel samples, beams): plain pa_decode,
+    which reads every shared block once per sequence, beside pa_decode_grouped,
+    which reads a group's common blocks once for the group. Unique bytes: each
+    distinct physical block's filled tokens once."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_316_amd as pkv
+    wl = ld.wl
     row = decode_row(ld, steps, warmup, workers)
     uniq = unique_kv_bytes(ld)
     t = row["decode_us"]["mean"] * 1e-6
-    return {"workload": WORKLOAD_TEXT[ld.name], "num_seqs": len(ld.wl.decode_seqs),
-            "ms_per_step": row["ms_per_step"], "tokens_per_s": row["tokens_per_s"],
-            "decode_us": row["decode_us"], "logical_kv_bytes": int(ld.kv_bytes),
-            "unique_kv_bytes": int(uniq), "shared_read_share": round(1 - uniq / ld.kv_bytes, 4),
-            "logical_kv_gbps": round(ld.kv_bytes / t / 1e9, 2),
-            "unique_kv_gbps": round(uniq / t / 1e9, 2),
-            "roofline": {"bound": "hbm", "achieved": round(uniq / t / 1e9, 2),
+    # grouped: the shared prefix of each group from the host tables
+    M = GROUP_SIZE[ld.name]
+    S = len(wl.decode_seqs)
+    pl = pkv.group_prefix_lens(ld.tables_d.cpu().numpy(), ld.lens, M, wl.block_size)
+    pl_d = torch.from_numpy(pl).cuda()
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elt_bytes
+    grouped_bytes = float(pl[::M].astype(np.int64).sum() +
+                          (ld.lens.astype(np.int64) - pl).sum()) * per_tok
+    out = torch.empty_like(ld.q)
+    ws = torch.empty(pkv.decode_grouped_workspace_bytes(S, wl.num_q_heads, wl.num_kv_heads,
+                                                        wl.head_dim, workers),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev):
+        p = ld.pools[i % len(ld.pools)]
+        if ev is not None:
+            ev[0].record(stream)
+        ld.decode_write.run(p)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.decode_grouped(ld.q, p, ld.tables_d, ld.lens_d, pl_d, M, wl.scale, workers, out=out,
+                           workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+    ms_step, _, g_ms = time_steps(step, steps, warmup)
+    tg = float(g_ms.mean()) * 1e-3
+    return {"workload": WORKLOAD_TEXT[ld.name], "num_seqs": S, "group_size": M,
+            "logical_kv_bytes": int(ld.kv_bytes), "unique_kv_bytes": int(uniq),
+            "grouped_kv_bytes": int(grouped_bytes),
+            "shared_read_share": round(1 - uniq / ld.kv_bytes, 4),
+            "plain_decode": {"ms_per_step": row["ms_per_step"], "decode_us": row["decode_us"],
+                             "logical_kv_gbps": round(ld.kv_bytes / t / 1e9, 2),
+                             "unique_kv_gbps": round(uniq / t / 1e9, 2)},
+            "grouped_decode": {"ms_per_step": round(ms_step, 5),
+                               "tokens_per_s": round(S / (ms_step * 1e-3), 1),
+                               "decode_us": _stats_us(g_ms),
+                               "grouped_kv_gbps": round(grouped_bytes / tg / 1e9, 2),
+                               "unique_kv_gbps": round(uniq / tg / 1e9, 2),
+                               "logical_kv_gbps": round(ld.kv_bytes / tg / 1e9, 2)},
+            "speedup_grouped_vs_plain": round(t / tg, 3),
+            "roofline": {"bound": "hbm", "achieved": round(uniq / tg / 1e9, 2),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(uniq / t / 1e9 / HBM_PEAK_GBPS, 4),
-                         "note": "achieved on unique physical bytes (re-reads of shared "
-                                 "blocks hit the caches)"}}
+                         "frac": round(uniq / tg / 1e9 / HBM_PEAK_GBPS, 4),
+                         "kernel": "pa_decode_grouped (grouped MFMA decode + LSE combine)",
+                         "note": "achieved on the batch's unique physical bytes; the grouped "
+                                 "call itself must read grouped_kv_bytes (a group's common "
+                                 "blocks once, each member's later blocks once)"}}
 
 
 def shared_prefix_blocks(ld):

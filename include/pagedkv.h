@@ -277,6 +277,53 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const pa_pool* pool,
                                   float scale, int32_t num_prefix_blocks, int32_t num_workers,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace needed by pa_decode_grouped, in bytes (0 for invalid sizes). */
+size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t num_workers);
+
+/*
+ * pa_decode_grouped — pa_decode for a batch of groups of sequences that share
+ * the blocks of a common start: the parallel samples of one prompt, or the
+ * beams of one beam search ("vLLM PagedAttention explained", sections 4.1 and
+ * 4.2: forked sequences share their blocks through reference counts until
+ * they diverge). The result is the same attention as pa_decode gives (every
+ * sequence attends over its own seq_lens[s] tokens), but a group's shared
+ * blocks are read once per KV head for the whole group instead of once per
+ * member: the members' query heads are the columns of one unit on the matrix
+ * cores, which scores the shared blocks for all of them and then each
+ * member's own later blocks for that member's columns only.
+ * Arguments are those of pa_decode, plus:
+ *   prefix_lens  : device, int32 [num_seqs]: the first prefix_lens[s] tokens
+ *                  of sequence s are the same physical blocks for every
+ *                  member of its group. Precondition: a multiple of B, equal
+ *                  within each group, <= seq_lens[s], and block_tables rows of
+ *                  a group equal in their first prefix_lens / B entries
+ *                  (pa_group_prefix_lens computes it from host tables,
+ *                  pa_check_grouped checks it). Shared blocks are read through
+ *                  the group's first row; a batch that breaks the
+ *                  precondition gets wrong results. 0 everywhere is valid
+ *                  (nothing read once).
+ *   group_size   : sequences 0..group_size-1 form group 0, and so on;
+ *                  num_seqs must be a multiple of it. Groups whose query heads
+ *                  (group_size * num_q_heads / num_kv_heads) exceed 16 are
+ *                  handled as sub-groups of the largest divisor that fits (the
+ *                  shared blocks are then read once per sub-group);
+ *                  PA_ERR_UNSUPPORTED when even one sequence's query heads
+ *                  per KV head exceed 16.
+ *   workspace    : device, >= pa_decode_grouped_workspace_bytes(...) bytes,
+ *                  16-byte aligned, scratch; calls sharing one must not overlap.
+ * bf16 and PA_FP8_E4M3 pools, head_dim 64 or 128 (PA_ERR_UNSUPPORTED
+ * otherwise); output in bf16, fp32 accumulation. Two kernels: the grouped
+ * decode, then the log-sum-exp combine of units split between wavefronts.
+ */
+pa_status pa_decode_grouped(void* out, const void* q, const pa_pool* pool,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, const int32_t* prefix_lens,
+                            int32_t num_seqs, int32_t group_size, int32_t num_q_heads,
+                            float scale, int32_t num_workers, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /*
  * pa_prefill_chunk — causal attention of a chunk of prompt rows per sequence
  * over that sequence's paged K/V ("vLLM PagedAttention explained", section
@@ -373,6 +420,21 @@ pa_status pa_check_chunks(const int32_t* q_start_loc, const int32_t* seq_lens, i
 pa_status pa_check_shared_prefix(const pa_pool* pool, const int32_t* block_tables,
                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
                                  int32_t num_seqs, int32_t num_prefix_blocks);
+
+/* Shared prefix of each group of group_size consecutive rows (host arrays):
+ * the leading table entries identical in every member's row, counting only
+ * blocks full in every member (j < min over members of seq_lens / B), times B;
+ * written to prefix_lens[s] for every member (host int32 [num_seqs]). What a
+ * pa_alloc_fork family of sequences shares ("vLLM PagedAttention explained",
+ * sections 4.1-4.2). */
+pa_status pa_group_prefix_lens(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t group_size,
+                               int32_t block_size, int32_t* prefix_lens);
+/* pa_check_batch plus the precondition of pa_decode_grouped on host copies of
+ * its arrays (see there). */
+pa_status pa_check_grouped(const pa_pool* pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                           const int32_t* prefix_lens, int32_t num_seqs, int32_t group_size);
 
 /* ------------------------------------------------------------------ host --- */
 

@@ -12,14 +12,17 @@ from .allocator import BlockAllocator
 from .ops import (DecodePlan, KVPool, attention_mixed, cache_write, check_batch, check_chunks,
                   check_copies, check_shared_prefix, check_slots, copy_blocks, decode,
                   decode_noalloc, decode_noalloc_scratch_bytes, decode_shared_prefix,
-                  set_input_checks,
+                  decode_grouped, decode_grouped_workspace_bytes, check_grouped,
+                  group_prefix_lens, set_input_checks,
                   decode_shared_prefix_workspace_bytes, decode_workspace_bytes, prefill_chunk,
                   probe_stream_read, swap_blocks, swap_in, swap_out, PA_SWAP_IN, PA_SWAP_OUT)
 
 __all__ = ["AllocatorStateError", "OutOfBlocks", "PagedKVError", "LIB_PATH", "SIGNATURES", "lib",
            "BlockAllocator", "DecodePlan", "KVPool", "attention_mixed", "cache_write", "check_batch",
            "check_chunks", "check_copies", "check_shared_prefix", "check_slots", "copy_blocks",
-           "decode", "decode_noalloc", "decode_noalloc_scratch_bytes", "set_input_checks",
+           "decode", "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_grouped",
+           "decode_grouped_workspace_bytes", "check_grouped", "group_prefix_lens",
+           "set_input_checks",
            "decode_shared_prefix", "decode_shared_prefix_workspace_bytes",
            "decode_workspace_bytes", "prefill_chunk", "probe_stream_read", "swap_blocks", "swap_in",
            "swap_out", "PA_SWAP_IN", "PA_SWAP_OUT"]

@@ -50,6 +50,14 @@ SIGNATURES = {
     "pa_decode_noalloc": (c_int32, [c_void_p, c_void_p, _P(PaPool), c_void_p, c_int32, c_void_p,
                                     c_int32, c_int32, c_float, c_int32, c_void_p]),
     "pa_decode_noalloc_scratch_bytes": (c_size_t, []),
+    "pa_decode_grouped_workspace_bytes": (c_size_t, [c_int32] * 5),
+    "pa_decode_grouped": (c_int32, [c_void_p, c_void_p, _P(PaPool), c_void_p, c_int32, c_void_p,
+                                    c_void_p, c_int32, c_int32, c_int32, c_float, c_int32,
+                                    c_void_p, c_size_t, c_void_p]),
+    "pa_group_prefix_lens": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32,
+                                       c_void_p]),
+    "pa_check_grouped": (c_int32, [_P(PaPool), c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                                   c_int32]),
     "pa_decode_shared_prefix_workspace_bytes": (c_size_t, [c_int32] * 7),
     "pa_decode_shared_prefix": (c_int32, [c_void_p, c_void_p, _P(PaPool), c_void_p, c_int32,
                                           c_void_p, c_int32, c_int32, c_float, c_int32, c_int32,

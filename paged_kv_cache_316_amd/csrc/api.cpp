@@ -59,6 +59,26 @@ DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
 
 size_t align16(size_t n) { return (n + 15) & ~size_t(15); }
 
+// Grouped decode: the same partial slots with 16 columns per unit.
+DecodeLayout grouped_layout(int32_t head_dim, int32_t workers) {
+  DecodeLayout d{};
+  d.workers = workers > 0 ? workers : default_workers();
+  d.heads_per_unit = kGroupedCols;
+  const size_t slots = size_t(2) * d.workers * d.heads_per_unit;
+  d.acc_bytes = slots * head_dim * 4;
+  d.ml_bytes = slots * 8;
+  d.seg_bytes = size_t(d.workers) * 16;
+  return d;
+}
+
+// Members per unit of the grouped decode: the largest divisor of group_size
+// whose members' query heads fit the 16 columns of one unit (0 if none).
+int32_t grouped_members(int32_t group_size, int32_t G) {
+  for (int32_t m = group_size; m >= 1; --m)
+    if (group_size % m == 0 && m * G <= kGroupedCols) return m;
+  return 0;
+}
+
 // Shared-prefix decode workspace: the decode's, then the tail log-sum-exp and
 // the prefix partials.
 struct PrefixLayout {
@@ -176,6 +196,9 @@ DecodeArgs decode_args(void* out, const void* q, const pa_pool* pool, const int3
   a.v_scale = fp8 ? pool->v_scale : 1.f;
   a.lse = nullptr;
   a.len_offset = 0;
+  a.prefix_lens = nullptr;
+  a.group_size = 1;
+  a.num_groups = num_seqs;
   return a;
 }
 
@@ -367,6 +390,53 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t
   if (reinterpret_cast<uintptr_t>(workspace) & 15)
     return fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
   return pa::decode_launch(c, workspace, stream, who);
+}
+
+size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t num_workers) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_workers < 0 || num_q_heads % num_kv_heads)
+    return 0;
+  return pa::grouped_layout(head_dim, num_workers).total();
+}
+
+pa_status pa_decode_grouped(void* out, const void* q, const pa_pool* pool,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, const int32_t* prefix_lens,
+                            int32_t num_seqs, int32_t group_size, int32_t num_q_heads,
+                            float scale, int32_t num_workers, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  const char* who = "pa_decode_grouped";
+  const pa::DecodeCall c{out, q, pool, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                         num_q_heads, scale, num_workers};
+  size_t plain_need = 0;
+  if (pa_status s = pa::decode_check(c, who, &plain_need)) return s;
+  if (group_size < 1 || (num_seqs > 0 && num_seqs % group_size))
+    return fail(PA_ERR_INVALID, "%s: num_seqs=%d is not a multiple of group_size=%d", who,
+                num_seqs, group_size);
+  if (num_seqs == 0) return PA_OK;
+  if (!prefix_lens) return fail(PA_ERR_INVALID, "%s: prefix_lens is NULL", who);
+  if (pool->dtype != PA_BF16 && pool->dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype=%d not built (bf16 or fp8 pools)", who, pool->dtype);
+  const int32_t G = num_q_heads / pool->num_kv_heads;
+  const int32_t members = pa::grouped_members(group_size, G);
+  if (members == 0)
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head exceed the %d columns of a "
+                "unit", who, G, pa::kGroupedCols);
+  const pa::DecodeLayout lay = pa::grouped_layout(pool->head_dim, num_workers);
+  if (!workspace || workspace_bytes < lay.total())
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who,
+                workspace ? workspace_bytes : size_t(0), lay.total());
+  if (reinterpret_cast<uintptr_t>(workspace) & 15)
+    return fail(PA_ERR_INVALID, "%s: workspace must be 16-byte aligned", who);
+  pa::DecodeArgs a = pa::decode_args(out, q, pool, block_tables, max_blocks_per_seq, seq_lens,
+                                     num_seqs, num_q_heads, scale, lay, workspace);
+  a.prefix_lens = prefix_lens;
+  a.group_size = members;
+  a.num_groups = num_seqs / members;
+  return pa::hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)), who);
 }
 
 size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

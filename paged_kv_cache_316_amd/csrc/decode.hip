@@ -154,26 +154,40 @@ __device__ __forceinline__ int len_of(const DecodeArgs& a, int s) {
   return max(a.seq_lens[s] - a.len_offset, 0);
 }
 
-template <int D, int VEC, class Begin, class Run, class End>
+// Tiles of group g in the grouped decode: its shared prefix once, then the
+// tokens after the prefix of each member.
+__device__ __forceinline__ int group_tiles(const DecodeArgs& a, int g) {
+  const int s0 = g * a.group_size;
+  const int P = a.prefix_lens[s0];
+  int n = tiles_of(P);
+  for (int m = 0; m < a.group_size; ++m) n += tiles_of(a.seq_lens[s0 + m] - P);
+  return n;
+}
+
+// GROUPED: the walk's items are groups of sequences (their length in tiles),
+// else sequences (their length in tokens).
+template <int D, int VEC, bool GROUPED, class Begin, class Run, class End>
 __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane, int n_hchunk,
                                            int hpw, int kvp, Begin begin, Run run, End end) {
-  const int S = a.num_seqs;
+  const int S = GROUPED ? a.num_groups : a.num_seqs;
   const int Hq = a.num_q_heads;
   const int G = Hq / a.num_kv_heads;
   const int units = (a.num_kv_heads / kvp) * n_hchunk;
+  auto item_len = [&](int s) -> int { return GROUPED ? group_tiles(a, s) : len_of(a, s); };
+  auto item_tiles = [&](int v) -> int { return GROUPED ? v : tiles_of(v); };
 
   int64_t total = 0;
   for (int base = 0; base < S; base += kWave) {
     const int s = base + lane;
-    total += wave_sum_i32(s < S ? tiles_of(len_of(a, s)) : 0);
+    total += wave_sum_i32(s < S ? item_tiles(item_len(s)) : 0);
   }
   total = uniform64(total * units);
   const int64_t W = total < a.workers ? total : a.workers;  // every active wave gets >= 1 tile
 
   // empty sequences: zeros, written by wave (s mod Wz)
   const int Wz = W > 0 ? int(W) : a.workers;
-  for (int s = w; s < S; s += Wz) {
-    if (len_of(a, s) > 0) continue;
+  for (int s = w; s < a.num_seqs; s += Wz) {
+    if ((GROUPED ? a.seq_lens[s] : len_of(a, s)) > 0) continue;
     uint4* o = static_cast<uint4*>(a.out) + (int64_t(s) * Hq * D) / VEC;
     for (int i = lane; i < Hq * D / VEC; i += kWave) o[i] = make_uint4(0, 0, 0, 0);
     if (a.lse)
@@ -185,24 +199,24 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
   }
   const int64_t g_begin = total * w / W, g_end = total * (w + 1) / W;
 
-  // lengths of 64 consecutive sequences, one per lane, read with v_readlane so
-  // that moving to the next sequence issues no memory load in the common case
+  // lengths of 64 consecutive items, one per lane, read with v_readlane so
+  // that moving to the next item issues no memory load in the common case
   int lwin_base = S, lwin = 0;
   auto seq_len = [&](int s) -> int {
     if (s - lwin_base >= kWave || s < lwin_base) {
       lwin_base = s;
-      lwin = s + lane < S ? len_of(a, s + lane) : 0;
+      lwin = s + lane < S ? item_len(s + lane) : 0;
     }
     return __builtin_amdgcn_readlane(lwin, s - lwin_base);
   };
 
-  // locate g_begin: the sequence whose tiles (times units) contain it
+  // locate g_begin: the item whose tiles (times units) contain it
   Cursor cur{};
   {
-    int64_t before = 0;  // tiles x units before this chunk of sequences
+    int64_t before = 0;  // tiles x units before this chunk of items
     for (int base = 0; base < S; base += kWave) {
       const int s = base + lane;
-      const int t = s < S ? tiles_of(len_of(a, s)) : 0;
+      const int t = s < S ? item_tiles(item_len(s)) : 0;
       const int64_t incl = before + int64_t(wave_incl_scan_i32(t, lane)) * units;
       const int64_t excl = incl - int64_t(t) * units;
       const unsigned long long hit = __ballot(s < S && t > 0 && excl <= g_begin && g_begin < incl);
@@ -254,7 +268,7 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
       do {
         ++cur.s;
         cur.L = seq_len(cur.s);
-        cur.n = tiles_of(cur.L);
+        cur.n = item_tiles(cur.L);
       } while (cur.n == 0);
     }
   }
@@ -456,7 +470,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
     }
   };
 
-  walk_slice<D, VEC>(a, w, lane, n_hchunk, HPW, 1, begin_segment, run_tiles, end_segment);
+  walk_slice<D, VEC, false>(a, w, lane, n_hchunk, HPW, 1, begin_segment, run_tiles, end_segment);
 }
 
 // GQA decode on the matrix cores (bf16, HPW >= 4 query heads per KV head).
@@ -493,9 +507,19 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
 // memory system serves short runs (2 KB for 16 FP8 rows of 128 B) much more
 // slowly than long ones. (bf16 groups of 8 paired the same way, 16 columns,
 // ran no faster: their 4 KB runs are long enough.)
-template <int D, int HPW, bool BIG_B, int KV, int KVP>
+// GROUPED (HPW = 16, KVP = 1): a unit is one KV head of a group of sequences
+// whose first prefix_lens[s] tokens are the same blocks ("vLLM PagedAttention
+// explained", sections 4.1-4.2: parallel samples and beams share the blocks of
+// their common start). Column c < group_size * G is query head kvh*G + c%G of
+// member c/G. A segment's tiles are the shared prefix (every column scores it)
+// and then each member's tokens after the prefix, which only that member's
+// columns score (the others get -inf); so each shared K/V tile is read once
+// for the whole group, and each column's softmax runs over exactly its own
+// sequence's tokens.
+template <int D, int HPW, bool BIG_B, int KV, int KVP, bool GROUPED>
 __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
+  static_assert(!GROUPED || (KVP == 1 && HPW == kGroupedCols), "grouped units: 16 columns");
   constexpr bool FP8 = KV == PA_FP8_E4M3;
   constexpr int ROW = 2 * D;        // bytes per bf16 K/V row in LDS
   constexpr int GROW = FP8 ? D : ROW;  // bytes per row in the pool
@@ -555,15 +579,21 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   float m, lpart;
   const float c2 = FP8 ? scale_log2 * a.k_scale : scale_log2;
   const float vsc = FP8 ? a.v_scale : 1.f;
+  const int ncols = GROUPED ? a.group_size * G : HPW;  // columns in use
   auto head_of = [&](const Cursor& x) { return x.kvh * G + x.hc * HPW; };
+  // (sequence, query head) row of q / out of column c (c < ncols)
+  auto row_of = [&](const Cursor& x, int c) -> int64_t {
+    if constexpr (GROUPED) return int64_t(x.s * a.group_size + c / G) * Hq + x.kvh * G + c % G;
+    else return int64_t(x.s) * Hq + head_of(x) + c;
+  };
   auto begin_segment = [&](const Cursor& x) {
     // columns past the unit's heads multiply zeros (their load is clamped to a real head)
     const unsigned char* qp = static_cast<const unsigned char*>(a.q) +
-                              (int64_t(x.s) * Hq + head_of(x) + min(i16, HPW - 1)) * ROW + 16 * g;
+                              row_of(x, min(i16, ncols - 1)) * ROW + 16 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint4 qv = *reinterpret_cast<const uint4*>(qp + 64 * ks);
-      qop[ks] = i16 < HPW ? qv : make_uint4(0, 0, 0, 0);
+      qop[ks] = i16 < ncols ? qv : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int p = 0; p < KVP; ++p)
@@ -573,7 +603,8 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     lpart = 0.f;
   };
 
-  auto compute = [&](int j, int L, const uint4* kr, const uint4* vr) {
+  // colok: this lane's column scores the tile (false: its scores are -inf)
+  auto compute = [&](int j, int L, const uint4* kr, const uint4* vr, bool colok) {
     // tiles -> LDS (the previous tile's reads were issued earlier by this
     // wave, and LDS serves one wave's accesses in order)
 #pragma unroll
@@ -612,7 +643,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     const int key0 = j * kTile + 4 * g;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (key0 + i >= L) sc[i] = -INFINITY;
+      if (key0 + i >= L || !colok) sc[i] = -INFINITY;
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     {  // max over lanes l, l^16, l^32, l^48 (the 4 lanes of head l%16), on the VALU
       const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
@@ -656,17 +687,18 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   auto end_segment = [&](const Cursor& x, bool owns_start, bool owns_end) {
     float l = lpart + __shfl_xor(lpart, 16);
     l += __shfl_xor(l, 32);
-    if (i16 >= HPW) return;
+    if (i16 >= ncols) return;
     // this lane's column: with paired KV heads, column 1 is in the second set
     f32x4_t oc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oc[dt] = KVP == 2 && i16 >= CPH ? o[KVP - 1][dt] : o[0][dt];
     if (owns_start && owns_end) {
-      if (a.lse && g == 0)
-        a.lse[int64_t(x.s) * Hq + head_of(x) + i16] = m * c2 + __builtin_amdgcn_logf(l);
+      // a grouped member without tokens scored nothing: the walk wrote its zeros
+      if (GROUPED && !(l > 0.f)) return;
+      if (a.lse && g == 0) a.lse[row_of(x, i16)] = m * c2 + __builtin_amdgcn_logf(l);
       const float inv = vsc / l;
       uint2* orow = reinterpret_cast<uint2*>(static_cast<unsigned char*>(a.out) +
-                                             (int64_t(x.s) * Hq + head_of(x) + i16) * ROW);
+                                             row_of(x, i16) * ROW);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
         orow[(16 * dt + 4 * g) / 4] = make_uint2(pack_bf16(oc[dt][0] * inv, oc[dt][1] * inv),
@@ -682,15 +714,14 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     if (g == 0) a.ws_ml[int64_t(slot) * HPW + i16] = make_float2(m * c2, l);
   };
 
-  // Tiles [j0, j1) of one segment, in chunks whose blocks fit a 64-entry
-  // window of the block table; branch-free, with NB tiles in flight. Keys
-  // past the end are clamped to the last token (a valid, written slot) and
-  // masked out in compute.
-  auto run_tiles = [&](const Cursor& x, int j0, int j1) {
-    const int32_t* row = a.block_tables + int64_t(x.s) * a.max_blocks_per_seq;
-    const int nblk = (x.L + Bm1) >> b_shift;
-    const int Lm1 = x.L - 1;
-    const int64_t head_off = int64_t(x.kvh) * B * GROW + lch * 16;
+  // Tiles [j0, j1) of a run of L tokens whose blocks are row[0], row[1], ...,
+  // in chunks whose blocks fit a 64-entry window of the block table;
+  // branch-free, with NB tiles in flight. Keys past the end are clamped to the
+  // last token (a valid, written slot) and masked out in compute.
+  auto run_part = [&](const int32_t* row, int L, int j0, int j1, int kvh, bool colok) {
+    const int nblk = (L + Bm1) >> b_shift;
+    const int Lm1 = L - 1;
+    const int64_t head_off = int64_t(kvh) * B * GROW + lch * 16;
     for (int jc = j0; jc < j1;) {
       const int jb0 = (jc * kTile) >> b_shift;
       const int win = jb0 + lane < nblk ? row[jb0 + lane] : 0;
@@ -723,24 +754,51 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
           const int jl = min(j + b + NB - 1, jc_end - 1);
           load_tile(jl, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
           __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this tile's math
-          compute(j + b, x.L, kb[b], vb[b]);
+          compute(j + b, L, kb[b], vb[b], colok);
         }
       }
 #pragma unroll
       for (int b = 0; b < NB - 1; ++b)  // the last tiles, already loaded
-        if (j + b < jc_end) compute(j + b, x.L, kb[b], vb[b]);
+        if (j + b < jc_end) compute(j + b, L, kb[b], vb[b], colok);
       jc = jc_end;
     }
   };
 
-  walk_slice<D, 8>(a, w, lane, n_hchunk, HPW, KVP, begin_segment, run_tiles, end_segment);
+  // Tiles [j0, j1) of one segment. Plain: the sequence's tokens. Grouped: the
+  // group's shared prefix (read through the first member's table row), then
+  // the tokens after it of member 0, 1, ... (through that member's row, from
+  // the entry of the prefix's end on), each scored by that member's columns.
+  auto run_tiles = [&](const Cursor& x, int j0, int j1) {
+    if constexpr (!GROUPED) {
+      run_part(a.block_tables + int64_t(x.s) * a.max_blocks_per_seq, x.L, j0, j1, x.kvh, true);
+    } else {
+      const int s0 = x.s * a.group_size;
+      const int P = a.prefix_lens[s0];
+      int first = 0;  // the part's first tile in the segment
+      for (int mb = -1; mb < a.group_size && first < j1; ++mb) {
+        const int s = mb < 0 ? s0 : s0 + mb;
+        const int Lp = mb < 0 ? P : max(a.seq_lens[s] - P, 0);
+        const int np = tiles_of(Lp);
+        const int lo = max(j0, first), hi = min(j1, first + np);
+        if (lo < hi) {
+          const int32_t* row = a.block_tables + int64_t(s) * a.max_blocks_per_seq +
+                               (mb < 0 ? 0 : (P >> b_shift));
+          run_part(row, Lp, lo - first, hi - first, x.kvh, mb < 0 || i16 / G == mb);
+        }
+        first += np;
+      }
+    }
+  };
+
+  walk_slice<D, 8, GROUPED>(a, w, lane, n_hchunk, HPW, KVP, begin_segment, run_tiles,
+                            end_segment);
 }
 
 // Combine the partials of each split segment. Wave w looks at the segment
 // that wave w of the decode kernel started and left open (if any); its
 // partials are in slot 2w+1 (wave w) and slots 2v for the waves v in
 // (w, last] that continued it.
-template <int DTYPE, int D, int HPW>
+template <int DTYPE, int D, int HPW, bool GROUPED>
 __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kernel(DecodeArgs a) {
   using RS = RowShape<DTYPE, D>;
   constexpr int VEC = RS::VEC, LPR = RS::LPR;
@@ -787,9 +845,13 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kern
     for (int k = 0; k < HPL; ++k) {
       const float m2 = nv == 2 ? ml[1][k].x : -INFINITY;
       const float Mn = fmaxf(M[k], fmaxf(ml[0][k].x, m2));
-      const float fo = M[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[k] - Mn);
-      const float f0 = __builtin_amdgcn_exp2f(ml[0][k].x - Mn);
-      const float f1 = nv == 2 ? __builtin_amdgcn_exp2f(m2 - Mn) : 0.f;
+      // A partial that scored nothing has m = -inf (in the grouped decode, a
+      // wave that only saw other members' tokens): weight 0. While every
+      // partial so far is such, the base is 0 so no -inf - -inf arises.
+      const float Ms = Mn == -INFINITY ? 0.f : Mn;
+      const float fo = M[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[k] - Ms);
+      const float f0 = __builtin_amdgcn_exp2f(ml[0][k].x - Ms);
+      const float f1 = nv == 2 ? __builtin_amdgcn_exp2f(m2 - Ms) : 0.f;
       den[k] = den[k] * fo + ml[0][k].y * f0 + (nv == 2 ? ml[1][k].y * f1 : 0.f);
 #pragma unroll
       for (int e = 0; e < VEC; e += 4) {
@@ -802,17 +864,23 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kern
       M[k] = Mn;
     }
   }
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int ncols = GROUPED ? a.group_size * G : HPW;
 #pragma unroll
   for (int k = 0; k < HPL; ++k) {
     const int hh = lane / LPR + k * GROUPS;
-    if (hh >= HPW) continue;
+    if (hh >= ncols) continue;
+    // grouped: a member without tokens has no partials (the walk wrote its zeros)
+    if (GROUPED && !(den[k] > 0.f)) continue;
     const float inv = 1.f / den[k];
-    if (a.lse && c == 0)
-      a.lse[int64_t(seg.x) * a.num_q_heads + head0 + hh] = M[k] + __builtin_amdgcn_logf(den[k]);
+    const int64_t row = GROUPED ? int64_t(seg.x * a.group_size + hh / G) * a.num_q_heads +
+                                      head0 + hh % G
+                                : int64_t(seg.x) * a.num_q_heads + head0 + hh;
+    if (a.lse && c == 0) a.lse[row] = M[k] + __builtin_amdgcn_logf(den[k]);
     float f[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) f[e] = num[k][e] * inv;
-    uint4* o = static_cast<uint4*>(a.out) + ((int64_t(seg.x) * a.num_q_heads + head0 + hh) * D) / VEC + c;
+    uint4* o = static_cast<uint4*>(a.out) + (row * D) / VEC + c;
     *o = pack16<DTYPE>(f);
   }
 }
@@ -835,14 +903,14 @@ hipError_t run(const DecodeArgs& a, hipStream_t st) {
     if (a.num_q_heads == a.num_kv_heads && a.num_kv_heads % 2 == 0) {
       const size_t lds = size_t(wpg) * 2 * 2 * kTile * 2 * D;  // K and V tiles of 2 heads
       if (a.block_size >= kTile)
-        decode_mfma_kernel<D, 2, true, DTYPE, 2>
+        decode_mfma_kernel<D, 2, true, DTYPE, 2, false>
             <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
       else
-        decode_mfma_kernel<D, 2, false, DTYPE, 2>
+        decode_mfma_kernel<D, 2, false, DTYPE, 2, false>
             <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      decode_combine_kernel<PA_BF16, D, 2><<<groups, kWave * wpg, 0, st>>>(a);
+      decode_combine_kernel<PA_BF16, D, 2, false><<<groups, kWave * wpg, 0, st>>>(a);
       return hipGetLastError();
     }
   }
@@ -850,10 +918,10 @@ hipError_t run(const DecodeArgs& a, hipStream_t st) {
   if constexpr (DTYPE == PA_FP8_E4M3 || (DTYPE == PA_BF16 && HPW >= 4)) {
     const size_t lds = size_t(wpg) * 2 * kTile * 2 * D;  // a K and a V tile per wave (bf16)
     if (a.block_size >= kTile)
-      decode_mfma_kernel<D, HPW, true, DTYPE, 1>
+      decode_mfma_kernel<D, HPW, true, DTYPE, 1, false>
           <<<groups, kWave * wpg, lds, st>>>(a, b_shift, n_hchunk, scale_log2);
     else
-      decode_mfma_kernel<D, HPW, false, DTYPE, 1>
+      decode_mfma_kernel<D, HPW, false, DTYPE, 1, false>
           <<<groups, kWave * wpg, lds, st>>>(a, b_shift, n_hchunk, scale_log2);
   } else {
     if (a.block_size >= kTile)
@@ -866,7 +934,30 @@ hipError_t run(const DecodeArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int OUT = DTYPE == PA_F32 ? PA_F32 : PA_BF16;  // FP8 pools give bf16 output
-  decode_combine_kernel<OUT, D, HPW><<<groups, kWave * wpg, 0, st>>>(a);
+  decode_combine_kernel<OUT, D, HPW, false><<<groups, kWave * wpg, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// Grouped decode: one unit per (group, KV head) of 16 columns, on the matrix
+// cores (bf16 and FP8 pools).
+template <int DTYPE, int D>
+hipError_t run_grouped(const DecodeArgs& a, hipStream_t st) {
+  int b_shift = 0;
+  while ((1 << b_shift) < a.block_size) ++b_shift;
+  const int cus = a.num_cus > 0 ? a.num_cus : 1;
+  int wpg = (a.workers + cus - 1) / cus;
+  wpg = wpg < 1 ? 1 : (wpg > kMaxWavesPerGroup ? kMaxWavesPerGroup : wpg);
+  const int groups = (a.workers + wpg - 1) / wpg;
+  const float scale_log2 = a.scale * kLog2e;
+  const size_t lds = size_t(wpg) * 2 * kTile * 2 * D;  // a K and a V tile per wave (bf16)
+  constexpr int H = kGroupedCols;
+  if (a.block_size >= kTile)
+    decode_mfma_kernel<D, H, true, DTYPE, 1, true><<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
+  else
+    decode_mfma_kernel<D, H, false, DTYPE, 1, true><<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_combine_kernel<PA_BF16, D, H, true><<<groups, kWave * wpg, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -894,6 +985,18 @@ bool decode_supported(int dtype, int head_dim, int group) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  if (a.prefix_lens) {
+    if (a.group_size < 1 || a.group_size * (a.num_q_heads / a.num_kv_heads) > kGroupedCols)
+      return hipErrorInvalidValue;
+    if (a.dtype == PA_BF16) {
+      if (a.head_dim == 128) return run_grouped<PA_BF16, 128>(a, st);
+      if (a.head_dim == 64) return run_grouped<PA_BF16, 64>(a, st);
+    } else if (a.dtype == PA_FP8_E4M3) {
+      if (a.head_dim == 128) return run_grouped<PA_FP8_E4M3, 128>(a, st);
+      if (a.head_dim == 64) return run_grouped<PA_FP8_E4M3, 64>(a, st);
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.dtype == PA_BF16) {
     if (a.head_dim == 128) return run_d<PA_BF16, 128>(a, st);
     if (a.head_dim == 64) return run_d<PA_BF16, 64>(a, st);

@@ -108,6 +108,14 @@ struct DecodeArgs {
                // in log2-scaled score units (-inf for an empty sequence)
   int32_t len_offset;  // attend to tokens len_offset .. seq_lens[s]-1; block_tables then
                        // points at the row entry of block len_offset / block_size
+  // Grouped decode (set prefix_lens): the sequences form num_groups consecutive
+  // groups of group_size; the first prefix_lens[s] tokens of every member of a
+  // group (a multiple of block_size, equal within the group) are the same
+  // physical blocks. Each (group, KV head) is one unit of group_size * G <= 16
+  // columns: the shared blocks are read once for all of them, then each
+  // member's own tokens for its columns only.
+  const int32_t* prefix_lens;
+  int32_t group_size, num_groups;
 };
 
 hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void* v_new,
@@ -127,6 +135,8 @@ hipError_t launch_copy_blocks(const pa_pool& pool, const int32_t* src_dst, int32
                               hipStream_t stream);
 // Returns hipErrorInvalidValue for shapes without a compiled kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Columns (query heads of all members) of one unit of the grouped decode.
+constexpr int kGroupedCols = 16;
 bool decode_supported(int dtype, int head_dim, int group);
 // Query heads handled together with their KV head by one wave (divides the group size).
 int decode_heads_per_unit(int group);

@@ -1,6 +1,7 @@
 // Host-side checks of the preconditions that the device calls cannot check
 // themselves: the contents of block tables, lengths, slots, copy pairs and
-// chunk offsets, which live in device memory during a call. A caller (or a
+// chunk offsets, which live in device memory during a call. Also the host
+// helper that finds the blocks a group of sequences shares. A caller (or a
 // debug mode of a binding) copies those arrays to the host and passes them
 // here before launching; every function reports the first violation it finds
 // through pa_last_error() and returns PA_ERR_INVALID. Plain host C++.
@@ -10,6 +11,7 @@
 // block * B + offset; "Why PagedAttention multiplies LLM serving throughput",
 // section "Block Table: the GPU page table": logical block j of a sequence is
 // its table entry j).
+#include <algorithm>
 #include <cstdint>
 #include <vector>
 
@@ -161,6 +163,68 @@ pa_status pa_check_shared_prefix(const pa_pool* pool, const int32_t* block_table
       if (row[j] != block_tables[j])
         return fail(PA_ERR_INVALID, "%s: block_tables[%d][%d]=%d differs from row 0 (%d)", who, s,
                     j, row[j], block_tables[j]);
+  }
+  return PA_OK;
+}
+
+pa_status pa_group_prefix_lens(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t group_size,
+                               int32_t block_size, int32_t* prefix_lens) {
+  pa::clear_error();
+  const char* who = "pa_group_prefix_lens";
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || group_size < 1 || block_size <= 0 ||
+      num_seqs % group_size)
+    return fail(PA_ERR_INVALID, "%s: num_seqs=%d max_blocks_per_seq=%d group_size=%d "
+                "block_size=%d", who, num_seqs, max_blocks_per_seq, group_size, block_size);
+  if (num_seqs == 0) return PA_OK;
+  if (!block_tables || !seq_lens || !prefix_lens) return fail(PA_ERR_INVALID, "%s: NULL array", who);
+  for (int32_t s0 = 0; s0 < num_seqs; s0 += group_size) {
+    // blocks full in every member
+    int64_t full = max_blocks_per_seq;
+    for (int32_t m = 0; m < group_size; ++m) {
+      const int32_t L = seq_lens[s0 + m];
+      if (L < 0) return fail(PA_ERR_INVALID, "%s: seq_lens[%d]=%d < 0", who, s0 + m, L);
+      full = std::min<int64_t>(full, L / block_size);
+    }
+    const int32_t* r0 = block_tables + int64_t(s0) * max_blocks_per_seq;
+    int64_t j = 0;
+    for (; j < full; ++j) {
+      bool same = true;
+      for (int32_t m = 1; m < group_size && same; ++m)
+        same = block_tables[int64_t(s0 + m) * max_blocks_per_seq + j] == r0[j];
+      if (!same) break;
+    }
+    for (int32_t m = 0; m < group_size; ++m) prefix_lens[s0 + m] = int32_t(j * block_size);
+  }
+  return PA_OK;
+}
+
+pa_status pa_check_grouped(const pa_pool* pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                           const int32_t* prefix_lens, int32_t num_seqs, int32_t group_size) {
+  if (pa_status s = pa_check_batch(pool, block_tables, max_blocks_per_seq, seq_lens, num_seqs))
+    return s;
+  const char* who = "pa_check_grouped";
+  if (group_size < 1 || num_seqs % group_size)
+    return fail(PA_ERR_INVALID, "%s: num_seqs=%d is not a multiple of group_size=%d", who,
+                num_seqs, group_size);
+  if (num_seqs > 0 && !prefix_lens) return fail(PA_ERR_INVALID, "%s: prefix_lens is NULL", who);
+  const int32_t B = pool->block_size;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t s0 = s - s % group_size;
+    const int32_t P = prefix_lens[s];
+    if (P < 0 || P % B || P > seq_lens[s])
+      return fail(PA_ERR_INVALID, "%s: prefix_lens[%d]=%d is not a multiple of B=%d in [0, "
+                  "seq_lens=%d]", who, s, P, B, seq_lens[s]);
+    if (P != prefix_lens[s0])
+      return fail(PA_ERR_INVALID, "%s: prefix_lens[%d]=%d differs from its group's first "
+                  "member (%d)", who, s, P, prefix_lens[s0]);
+    const int32_t* row = block_tables + int64_t(s) * max_blocks_per_seq;
+    const int32_t* r0 = block_tables + int64_t(s0) * max_blocks_per_seq;
+    for (int32_t j = 0; j < P / B; ++j)
+      if (row[j] != r0[j])
+        return fail(PA_ERR_INVALID, "%s: block_tables[%d][%d]=%d differs from its group's "
+                    "first member (%d) inside the shared prefix", who, s, j, row[j], r0[j]);
   }
   return PA_OK;
 }

@@ -83,6 +83,28 @@ def check_shared_prefix(pool: "KVPool", block_tables, seq_lens, num_prefix_block
                                        n.ctypes.data, n.shape[0], int(num_prefix_blocks)))
 
 
+def check_grouped(pool: "KVPool", block_tables, seq_lens, prefix_lens, group_size: int) -> None:
+    """check_batch plus the shared-prefix precondition of decode_grouped (host check)."""
+    t, n = _host(block_tables, np.int32), _host(seq_lens, np.int32)
+    p = _host(prefix_lens, np.int32)
+    if t.ndim != 2 or n.shape != (t.shape[0],) or p.shape != n.shape:
+        raise ValueError("block_tables must be [S, maxB], seq_lens and prefix_lens [S]")
+    check(lib().pa_check_grouped(ctypes.byref(pool.c), t.ctypes.data, t.shape[1], n.ctypes.data,
+                                 p.ctypes.data, n.shape[0], int(group_size)))
+
+
+def group_prefix_lens(block_tables, seq_lens, group_size: int, block_size: int) -> np.ndarray:
+    """Tokens each group of group_size consecutive rows shares (host computation on
+    host copies of the tables): int32 [S], equal within a group."""
+    t, n = _host(block_tables, np.int32), _host(seq_lens, np.int32)
+    if t.ndim != 2 or n.shape != (t.shape[0],):
+        raise ValueError("block_tables must be [S, maxB] and seq_lens [S]")
+    out = np.zeros(n.shape[0], dtype=np.int32)
+    check(lib().pa_group_prefix_lens(t.ctypes.data, t.shape[1], n.ctypes.data, n.shape[0],
+                                     int(group_size), int(block_size), out.ctypes.data))
+    return out
+
+
 def _need(t: torch.Tensor, name: str, dtype=None, device=True) -> None:
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -278,6 +300,42 @@ def decode_noalloc_scratch_bytes() -> int:
     return int(lib().pa_decode_noalloc_scratch_bytes())
 
 
+def decode_grouped_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                   head_dim: int, workers: int = 0) -> int:
+    return int(lib().pa_decode_grouped_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                       head_dim, workers))
+
+
+def decode_grouped(q: torch.Tensor, pool: KVPool, block_tables: torch.Tensor,
+                   seq_lens: torch.Tensor, prefix_lens: torch.Tensor, group_size: int,
+                   scale: float, workers: int = 0, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode for groups of ``group_size`` consecutive sequences whose first
+    ``prefix_lens[s]`` tokens are the same blocks; those are read once per group."""
+    _need(q, "q", pool.io_dtype)
+    _need(block_tables, "block_tables", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(prefix_lens, "prefix_lens", torch.int32)
+    S, Hq, D = q.shape
+    if D != pool.head_dim or block_tables.dim() != 2 or block_tables.shape[0] != S \
+            or seq_lens.shape != (S,) or prefix_lens.shape != (S,):
+        raise ValueError("shape mismatch between q, block_tables, seq_lens and prefix_lens")
+    if _CHECK_INPUTS:
+        check_grouped(pool, block_tables, seq_lens, prefix_lens, group_size)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", pool.io_dtype)
+    if workspace is None:
+        n = decode_grouped_workspace_bytes(S, Hq, pool.num_kv_heads, D, workers)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    check(lib().pa_decode_grouped(out.data_ptr(), q.data_ptr(), ctypes.byref(pool.c),
+                                  block_tables.data_ptr(), block_tables.shape[1],
+                                  seq_lens.data_ptr(), prefix_lens.data_ptr(), S, int(group_size),
+                                  Hq, float(scale), int(workers), workspace.data_ptr(),
+                                  workspace.numel(), _stream()))
+    return out
+
+
 def decode_shared_prefix_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
                                          head_dim: int, block_size: int, num_prefix_blocks: int,
                                          workers: int = 0) -> int:
@@ -375,7 +433,9 @@ def prefill_chunk(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.Te
 
 __all__ = ["KVPool", "DecodePlan", "attention_mixed", "cache_write", "check_batch", "check_chunks",
            "check_copies", "check_shared_prefix", "check_slots", "copy_blocks", "decode",
-           "decode_noalloc", "decode_noalloc_scratch_bytes", "set_input_checks",
+           "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_grouped",
+           "decode_grouped_workspace_bytes", "check_grouped", "group_prefix_lens",
+           "set_input_checks",
            "decode_workspace_bytes", "decode_shared_prefix", "decode_shared_prefix_workspace_bytes",
            "prefill_chunk", "swap_blocks", "swap_in", "swap_out", "PA_SWAP_IN", "PA_SWAP_OUT",
            "PagedKVError"]

@@ -260,3 +260,24 @@ def test_noalloc_decode_argument_checks():
     # G = 1 MHA: 2 * W * 2 * (128 * 4 + 8) + 16 W bytes; 1 << 14 workers need 34.3 MB
     assert L.pa_decode_workspace_bytes(2, 8, 8, 128, 1 << 14) > cap
     assert call(workers=1 << 14) == -5 and b"scratch" in L.pa_last_error()
+
+
+def test_grouped_decode_argument_checks():
+    L = lib()
+    p = _pool(num_kv_heads=8)
+    need = L.pa_decode_grouped_workspace_bytes(6, 8, 8, 128, 10)
+    # 16 columns per partial slot: 2 * 10 * 16 * (128 * 4 + 8) + 10 * 16
+    assert need == 2 * 10 * 16 * (128 * 4 + 8) + 10 * 16
+    f = ctypes.c_float(0.1)
+    call = lambda S=6, M=3, Hq=8, pool=p, pl=16, ws=16, wsb=need, workers=10, scale=f: \
+        L.pa_decode_grouped(16, 16, ctypes.byref(pool), 16, 4, 16, pl, S, M, Hq, scale, workers,
+                            ws, wsb, None)
+    assert call(S=0) == 0                                     # nothing to do
+    assert call(M=4) == -1 and b"multiple of group_size" in L.pa_last_error()
+    assert call(M=0) == -1
+    assert call(pl=None) == -1 and b"prefix_lens" in L.pa_last_error()
+    assert call(pool=_pool(num_kv_heads=8, dtype=0)) == -2   # fp32 pools: not built
+    assert call(Hq=8 * 17, pool=_pool(num_kv_heads=8)) == -2 and b"columns" in L.pa_last_error()
+    assert call(ws=None) == -5 and call(wsb=need - 1) == -5
+    assert call(scale=ctypes.c_float(0.0)) == -1
+    assert L.pa_decode_grouped_workspace_bytes(6, 6, 4, 128, 0) == 0  # 6 not a multiple of 4

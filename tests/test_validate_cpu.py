@@ -135,3 +135,41 @@ def test_checks_run_before_launch_when_enabled(monkeypatch):
         pkv.ops.decode(q, pool, torch.tensor([[99]], dtype=torch.int32),
                        torch.tensor([3], dtype=torch.int32), 0.1, plan=None, out=q)
     assert calls == []  # refused before any workspace was set up
+
+
+def test_group_prefix_lens_and_grouped_precondition():
+    pool = _Pool()  # 12 blocks of 4
+    # two groups of 2: group 0 shares blocks 3, 7 then diverges; group 1 shares
+    # block 1 only while full in both members (member 1 has 5 tokens: 1 full block)
+    tables = np.array([[3, 7, 2], [3, 7, 5], [1, 9, 4], [1, 9, 0]], np.int32)
+    lens = np.array([10, 12, 11, 5], np.int32)
+    pl = pkv.group_prefix_lens(tables, lens, 2, B)
+    assert pl.tolist() == [8, 8, 4, 4]
+    pkv.check_grouped(pool, tables, lens, pl, 2)
+    # groups of one share with themselves: every full block
+    assert pkv.group_prefix_lens(tables, lens, 1, B).tolist() == [8, 12, 8, 4]
+    # groups of four: only block 0 would need to match across all, and it does not
+    assert pkv.group_prefix_lens(tables, lens, 4, B).tolist() == [0, 0, 0, 0]
+    _raises(pkv.check_grouped, pool, tables, lens, np.array([8, 8, 8, 8], np.int32), 2,
+            match=r"prefix_lens\[3\]=8 is not a multiple of B=4 in \[0, seq_lens=5\]")
+    _raises(pkv.check_grouped, pool, tables, lens, np.array([8, 4, 4, 4], np.int32), 2,
+            match=r"prefix_lens\[1\]=4 differs from its group's first member")
+    _raises(pkv.check_grouped, pool, tables, lens, np.array([8, 8, 6, 6], np.int32), 2,
+            match="not a multiple of B")
+    bad = tables.copy(); bad[1, 1] = 8
+    _raises(pkv.check_grouped, pool, bad, lens, pl, 2, match=r"block_tables\[1\]\[1\]=8 differs")
+    _raises(pkv.check_grouped, pool, tables, lens, pl, 3, match="multiple of group_size")
+    with pytest.raises(PagedKVError):
+        pkv.group_prefix_lens(tables, lens, 3, B)
+
+
+def test_group_prefix_lens_on_sharing_workloads():
+    """The forked families of the sharing workloads share their prompt's full blocks."""
+    for name, M, prompt in (("cow", 3, 48), ("cow504", 3, 40), ("beam", 4, 40)):
+        wl = workloads.make(name, "small")
+        alloc = pkv.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
+        run_script(alloc, wl.ops)
+        tables, lens = alloc.batch_tables(wl.decode_seqs)
+        pl = pkv.group_prefix_lens(tables, lens, M, wl.block_size)
+        pkv.check_grouped(_Pool(wl.num_blocks, wl.block_size), tables, lens, pl, M)
+        assert (pl >= (prompt // wl.block_size) * wl.block_size).all(), (name, pl)
