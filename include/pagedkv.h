@@ -220,7 +220,7 @@ pa_status pa_decode(void* out, const void* q, const pa_pool* pool,
  * allocates nothing; its first call on a device looks up that device's copy
  * of the array. A call whose workspace (pa_decode_workspace_bytes) exceeds
  * the array returns PA_ERR_WORKSPACE with nothing queued; the default worker
- * count needs at most 16.3 MiB on 256 compute units. All calls on one device
+ * count needs at most 16.6 MiB on 256 compute units. All calls on one device
  * share its array: calls that overlap on one device (other streams, other
  * host threads) race and must be serialized by the caller.
  */

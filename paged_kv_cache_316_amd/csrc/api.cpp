@@ -51,7 +51,7 @@ DecodeLayout decode_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
   d.units = num_q_heads / d.heads_per_unit;
   const size_t slots = size_t(2) * d.workers * d.heads_per_unit;
   d.acc_bytes = slots * head_dim * 4;
-  d.ml_bytes = slots * 8;
+  d.ml_bytes = size_t(2) * d.workers * kMLStride * 8;
   d.seg_bytes = size_t(d.workers) * 16;
   (void)num_seqs;
   return d;
@@ -66,7 +66,7 @@ DecodeLayout grouped_layout(int32_t head_dim, int32_t workers) {
   d.heads_per_unit = kGroupedCols;
   const size_t slots = size_t(2) * d.workers * d.heads_per_unit;
   d.acc_bytes = slots * head_dim * 4;
-  d.ml_bytes = slots * 8;
+  d.ml_bytes = size_t(2) * d.workers * kMLStride * 8;
   d.seg_bytes = size_t(d.workers) * 16;
   return d;
 }

@@ -144,11 +144,20 @@ struct Cursor {
 };
 
 // This wave's slice of the work list, walked segment by segment: for each
-// segment (sequence, unit) it calls begin(cursor), run(cursor, j0, j1) for
-// the slice's tiles [j0, j1) of it, and end(cursor, owns_start, owns_end),
-// then records the segment the slice starts and leaves open (if any) for the
-// combine kernel. Also writes zeros for empty sequences. VEC: elements of the
-// output dtype per 16 bytes; hpw: query heads per unit.
+// segment (sequence, unit) it calls prefetch(cursor), which issues the
+// segment's query loads and the load of the block-table window of its first
+// tile and returns that window, then begin(cursor), run(cursor, j0, j1, window)
+// for the slice's tiles [j0, j1) of it, and end(cursor, owns_start, owns_end),
+// which stores the result; finally it records the segment the slice starts and
+// leaves open (if any) for the combine kernel. Also writes zeros for empty
+// sequences. VEC: elements of the output dtype per 16 bytes; hpw: query heads
+// per unit.
+// Order at a segment boundary: the next segment's prefetch comes before the
+// current segment's end. Stores and loads share one counter of outstanding
+// vector memory operations, which completes in issue order; loads issued
+// after a segment's stores could only be waited for together with those
+// stores, whose completion is slow while the chip streams K/V. Issued before
+// them, the next segment's first loads are awaited while the stores drain.
 // tokens of sequence s this call attends to: those after the first len_offset
 __device__ __forceinline__ int len_of(const DecodeArgs& a, int s) {
   return max(a.seq_lens[s] - a.len_offset, 0);
@@ -166,9 +175,10 @@ __device__ __forceinline__ int group_tiles(const DecodeArgs& a, int g) {
 
 // GROUPED: the walk's items are groups of sequences (their length in tiles),
 // else sequences (their length in tokens).
-template <int D, int VEC, bool GROUPED, class Begin, class Run, class End>
+template <int D, int VEC, bool GROUPED, class Prefetch, class Begin, class Run, class End>
 __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane, int n_hchunk,
-                                           int hpw, int kvp, Begin begin, Run run, End end) {
+                                           int hpw, int kvp, Prefetch prefetch, Begin begin,
+                                           Run run, End end) {
   const int S = GROUPED ? a.num_groups : a.num_seqs;
   const int Hq = a.num_q_heads;
   const int G = Hq / a.num_kv_heads;
@@ -242,35 +252,42 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
   // walk the segments of this slice
   int64_t g = g_begin;
   int4 split = make_int4(-1, 0, 0, 0);  // the segment this slice starts and leaves unfinished
+  int win = prefetch(cur);
+  begin(cur);
   while (true) {
     const int j1 = int(min(int64_t(cur.n), int64_t(cur.j) + (g_end - g)));
     const bool owns_start = cur.j == 0, owns_end = j1 == cur.n;
-    begin(cur);
-    run(cur, cur.j, j1);
-    end(cur, owns_start, owns_end);
+    run(cur, cur.j, j1, win);
     if (owns_start && !owns_end) {  // only the last segment of a slice can be left open
       const int64_t last = cur.seg0 + cur.n - 1;
       split = make_int4(cur.s, cur.u, int(((last + 1) * W - 1) / total),
                         cur.kvh * G + cur.hc * hpw);
     }
     g += j1 - cur.j;
-    if (g >= g_end) break;
-    // next segment: next unit of this sequence, or the next non-empty sequence
-    cur.j = 0;
-    cur.seg0 += cur.n;
-    ++cur.u;
-    if (++cur.hc == n_hchunk) {
-      cur.hc = 0;
-      cur.kvh += kvp;
+    const bool more = g < g_end;
+    const Cursor done = cur;
+    if (more) {
+      // next segment: next unit of this sequence, or the next non-empty sequence
+      cur.j = 0;
+      cur.seg0 += cur.n;
+      ++cur.u;
+      if (++cur.hc == n_hchunk) {
+        cur.hc = 0;
+        cur.kvh += kvp;
+      }
+      if (cur.u == units) {
+        cur.u = cur.kvh = cur.hc = 0;
+        do {
+          ++cur.s;
+          cur.L = seq_len(cur.s);
+          cur.n = item_tiles(cur.L);
+        } while (cur.n == 0);
+      }
+      win = prefetch(cur);  // its loads go out before the stores of `done`
     }
-    if (cur.u == units) {
-      cur.u = cur.kvh = cur.hc = 0;
-      do {
-        ++cur.s;
-        cur.L = seq_len(cur.s);
-        cur.n = item_tiles(cur.L);
-      } while (cur.n == 0);
-    }
+    end(done, owns_start, owns_end);
+    if (!more) break;
+    begin(cur);
   }
   if (lane == 0) a.ws_seg[w] = split;
 }
@@ -298,14 +315,24 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
 
   // ---- per-segment state ------------------------------------------------------
   float qf[HPW][QF];
-  uint4 qb[HPW];
+  uint4 qb[HPW], qnext[HPW];
   float m[HPW], l[HPW], acc[HPW][VEC];
   auto head_of = [&](const Cursor& x) { return x.kvh * G + x.hc * HPW; };
-  auto begin_segment = [&](const Cursor& x) {
+  // the segment's query loads and the block-table window of its tile x.j
+  auto prefetch = [&](const Cursor& x) -> int {
     const uint4* qp = static_cast<const uint4*>(a.q) + ((int64_t(x.s) * Hq + head_of(x)) * D) / VEC + c;
 #pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) qnext[hh] = qp[hh * (D / VEC)];
+    const int32_t* row = a.block_tables + int64_t(x.s) * a.max_blocks_per_seq;
+    const int nblk = (x.L + Bm1) >> b_shift;
+    const int jb0 = (x.j * kTile) >> b_shift;
+    return jb0 + lane < nblk ? row[jb0 + lane] : 0;
+  };
+  auto begin_segment = [&](const Cursor& x) {
+    (void)x;
+#pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      qb[hh] = qp[hh * (D / VEC)];
+      qb[hh] = qnext[hh];
       if constexpr (DTYPE == PA_F32) {
         qf[hh][0] = __uint_as_float(qb[hh].x) * scale_log2;
         qf[hh][1] = __uint_as_float(qb[hh].y) * scale_log2;
@@ -408,7 +435,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
 #pragma unroll
         for (int e = 0; e < VEC; e += 4)
           dst[e / 4] = make_float4(acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]);
-        if (c == 0) a.ws_ml[int64_t(slot) * HPW + hh] = make_float2(m[hh], l[hh]);
+        if (c == 0) a.ws_ml[int64_t(slot) * kMLStride + hh] = make_float2(m[hh], l[hh]);
       }
     }
   };
@@ -419,13 +446,14 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
   // tile j+1 is loading while tile j is computed. Rows past the end of the
   // sequence are clamped to its last token (a valid, written slot) and masked
   // out in compute, so no load sits under divergent control flow.
-  auto run_tiles = [&](const Cursor& x, int j0, int j1) {
+  // win0: the window of tile j0's chunk (prefetched)
+  auto run_tiles = [&](const Cursor& x, int j0, int j1, int win0) {
     const int32_t* row = a.block_tables + int64_t(x.s) * a.max_blocks_per_seq;
     const int nblk = (x.L + Bm1) >> b_shift;
     const int Lm1 = x.L - 1;
     for (int jc = j0; jc < j1;) {
       const int jb0 = (jc * kTile) >> b_shift;
-      const int win = jb0 + lane < nblk ? row[jb0 + lane] : 0;
+      const int win = jc == j0 ? win0 : (jb0 + lane < nblk ? row[jb0 + lane] : 0);
       const int jc_end = min(j1, ((jb0 + kWave) << b_shift) / kTile);
       auto load_tile = [&](int j, uint4* kr, uint4* vr) {
         if constexpr (BIG_B) {
@@ -470,7 +498,8 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
     }
   };
 
-  walk_slice<D, VEC, false>(a, w, lane, n_hchunk, HPW, 1, begin_segment, run_tiles, end_segment);
+  walk_slice<D, VEC, false>(a, w, lane, n_hchunk, HPW, 1, prefetch, begin_segment, run_tiles,
+                            end_segment);
 }
 
 // GQA decode on the matrix cores (bf16, HPW >= 4 query heads per KV head).
@@ -574,7 +603,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   const unsigned char* vp = static_cast<const unsigned char*>(a.v_pool);
   const int64_t block_bytes = int64_t(Hkv) * B * GROW;
 
-  uint4 qop[KS];
+  uint4 qop[KS], qnext[KS];
   f32x4_t o[KVP][DT];
   float m, lpart;
   const float c2 = FP8 ? scale_log2 * a.k_scale : scale_log2;
@@ -586,15 +615,49 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     if constexpr (GROUPED) return int64_t(x.s * a.group_size + c / G) * Hq + x.kvh * G + c % G;
     else return int64_t(x.s) * Hq + head_of(x) + c;
   };
-  auto begin_segment = [&](const Cursor& x) {
+  // Where tile j of a segment lies: the table row of its part (the sequence's
+  // row; grouped: the shared prefix through the first member's row, or a
+  // member's tokens after it through that member's row from the prefix's end
+  // on), the part's length and the tile's index inside the part.
+  struct Part {
+    const int32_t* row;
+    int L, j;
+  };
+  auto part_of = [&](const Cursor& x, int j) -> Part {
+    if constexpr (!GROUPED) {
+      return Part{a.block_tables + int64_t(x.s) * a.max_blocks_per_seq, x.L, j};
+    } else {
+      const int s0 = x.s * a.group_size;
+      const int P = a.prefix_lens[s0];
+      const int np = tiles_of(P);
+      if (j < np) return Part{a.block_tables + int64_t(s0) * a.max_blocks_per_seq, P, j};
+      j -= np;
+      int mb = 0;
+      int Lm = max(a.seq_lens[s0] - P, 0);
+      while (j >= tiles_of(Lm) && mb + 1 < a.group_size) {
+        j -= tiles_of(Lm);
+        ++mb;
+        Lm = max(a.seq_lens[s0 + mb] - P, 0);
+      }
+      return Part{a.block_tables + int64_t(s0 + mb) * a.max_blocks_per_seq + (P >> b_shift), Lm, j};
+    }
+  };
+  // the segment's query loads and the block-table window of its tile x.j
+  auto prefetch = [&](const Cursor& x) -> int {
     // columns past the unit's heads multiply zeros (their load is clamped to a real head)
     const unsigned char* qp = static_cast<const unsigned char*>(a.q) +
                               row_of(x, min(i16, ncols - 1)) * ROW + 16 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 qv = *reinterpret_cast<const uint4*>(qp + 64 * ks);
-      qop[ks] = i16 < ncols ? qv : make_uint4(0, 0, 0, 0);
-    }
+    for (int ks = 0; ks < KS; ++ks) qnext[ks] = *reinterpret_cast<const uint4*>(qp + 64 * ks);
+    const Part pt = part_of(x, x.j);
+    const int nblk = (pt.L + Bm1) >> b_shift;
+    const int jb0 = (pt.j * kTile) >> b_shift;
+    return jb0 + lane < nblk ? pt.row[jb0 + lane] : 0;
+  };
+  auto begin_segment = [&](const Cursor& x) {
+    (void)x;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qop[ks] = i16 < ncols ? qnext[ks] : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int p = 0; p < KVP; ++p)
 #pragma unroll
@@ -684,47 +747,109 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
       }
   };
 
+  // Results leave through the wave's own LDS tiles, idle at a segment's end
+  // (LDS serves one wave's accesses in order, so this wave's reads of its
+  // last tile come first): end_segment assembles each column's row there,
+  // and flush() later writes the rows with 16 contiguous bytes per lane, each
+  // store instruction covering whole rows (256 bytes of bf16 output, 512 of
+  // fp32 partials for head_dim 128). flush() runs once the next segment's
+  // first K/V loads are issued (or when the wave is done). Stores and loads
+  // complete in issue order for this wave's counter of outstanding memory
+  // operations, so a store issued before a load delays every use of that
+  // load until the store is acknowledged, and stores that miss the L2 are
+  // acknowledged slowly while the chip streams K/V. Issued at a segment's end,
+  // the results of units of 8 query heads cost the Llama-2-70B-shaped batch
+  // 9 % of its rate.
+  int pend = 0;            // 0: nothing; 1: output rows; 2: partial rows (wave-uniform)
+  Cursor pend_x{};         // the segment the pending rows belong to
+  uint64_t pend_rows = 0;  // output: bit c set when column c's row is written
+  int pend_slot = 0;       // partials: the slot
+  float2 pend_ml = make_float2(0.f, 0.f);
   auto end_segment = [&](const Cursor& x, bool owns_start, bool owns_end) {
     float l = lpart + __shfl_xor(lpart, 16);
     l += __shfl_xor(l, 32);
-    if (i16 >= ncols) return;
+    const bool col = i16 < ncols;
     // this lane's column: with paired KV heads, column 1 is in the second set
     f32x4_t oc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oc[dt] = KVP == 2 && i16 >= CPH ? o[KVP - 1][dt] : o[0][dt];
+    unsigned char* stage = kt_lds;  // KVP * 2 * TB bytes: 16 rows of fp32 partials fit
+    pend_x = x;
     if (owns_start && owns_end) {
       // a grouped member without tokens scored nothing: the walk wrote its zeros
-      if (GROUPED && !(l > 0.f)) return;
-      if (a.lse && g == 0) a.lse[row_of(x, i16)] = m * c2 + __builtin_amdgcn_logf(l);
+      const bool keep = col && (!GROUPED || l > 0.f);
+      if (a.lse && g == 0 && keep) a.lse[row_of(x, i16)] = m * c2 + __builtin_amdgcn_logf(l);
       const float inv = vsc / l;
-      uint2* orow = reinterpret_cast<uint2*>(static_cast<unsigned char*>(a.out) +
-                                             row_of(x, i16) * ROW);
+      if (keep) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        orow[(16 * dt + 4 * g) / 4] = make_uint2(pack_bf16(oc[dt][0] * inv, oc[dt][1] * inv),
-                                                 pack_bf16(oc[dt][2] * inv, oc[dt][3] * inv));
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<uint2*>(stage + i16 * ROW + (16 * dt + 4 * g) * 2) =
+              make_uint2(pack_bf16(oc[dt][0] * inv, oc[dt][1] * inv),
+                         pack_bf16(oc[dt][2] * inv, oc[dt][3] * inv));
+      }
+      pend_rows = __ballot(g == 0 && keep);
+      pend = 1;
       return;
     }
-    const int slot = 2 * w + (owns_start ? 1 : 0);
-    float4* dst = reinterpret_cast<float4*>(a.ws_acc + (int64_t(slot) * HPW + i16) * D);
+    // a split segment's partial sums go to the combine as bf16 (the (max,
+    // denominator) record stays fp32): half the bytes, and the writes back to
+    // memory of these partials cost the read stream far more than their size
+    if (col) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      dst[(16 * dt + 4 * g) / 4] =
-          make_float4(oc[dt][0] * vsc, oc[dt][1] * vsc, oc[dt][2] * vsc, oc[dt][3] * vsc);
-    if (g == 0) a.ws_ml[int64_t(slot) * HPW + i16] = make_float2(m * c2, l);
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<uint2*>(stage + i16 * ROW + (16 * dt + 4 * g) * 2) =
+            make_uint2(pack_bf16(oc[dt][0] * vsc, oc[dt][1] * vsc),
+                       pack_bf16(oc[dt][2] * vsc, oc[dt][3] * vsc));
+    }
+    pend_slot = 2 * w + (owns_start ? 1 : 0);
+    pend_ml = make_float2(m * c2, l);
+    pend = 2;
+  };
+  auto flush = [&]() {
+    const unsigned char* stage = kt_lds;
+    if (pend == 1) {
+      constexpr int LPRW = ROW / 16;     // lanes per bf16 row
+      constexpr int RPW = kWave / LPRW;  // rows per store instruction
+#pragma unroll 1
+      for (int it = 0; it < (HPW + RPW - 1) / RPW; ++it) {
+        const int cc = it * RPW + lane / LPRW;
+        if (cc < ncols && ((pend_rows >> cc) & 1)) {
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + cc * ROW + (lane % LPRW) * 16);
+          *reinterpret_cast<uint4*>(static_cast<unsigned char*>(a.out) + row_of(pend_x, cc) * ROW +
+                                    (lane % LPRW) * 16) = v;
+        }
+      }
+    } else if (pend == 2) {
+      constexpr int LPRW = ROW / 16;     // lanes per bf16 row
+      constexpr int RPW = kWave / LPRW;  // rows per store instruction
+      unsigned char* part = reinterpret_cast<unsigned char*>(a.ws_acc);  // bf16 rows
+#pragma unroll 1
+      for (int it = 0; it < (HPW + RPW - 1) / RPW; ++it) {
+        const int cc = it * RPW + lane / LPRW;
+        if (cc < ncols) {
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + cc * ROW + (lane % LPRW) * 16);
+          *reinterpret_cast<uint4*>(part + (int64_t(pend_slot) * HPW + cc) * ROW +
+                                    (lane % LPRW) * 16) = v;
+        }
+      }
+      if (g == 0 && i16 < ncols) a.ws_ml[int64_t(pend_slot) * kMLStride + i16] = pend_ml;
+    }
+    pend = 0;
   };
 
   // Tiles [j0, j1) of a run of L tokens whose blocks are row[0], row[1], ...,
   // in chunks whose blocks fit a 64-entry window of the block table;
   // branch-free, with NB tiles in flight. Keys past the end are clamped to the
   // last token (a valid, written slot) and masked out in compute.
-  auto run_part = [&](const int32_t* row, int L, int j0, int j1, int kvh, bool colok) {
+  // win0 (when have_win0): the window of tile j0's chunk, already loaded
+  auto run_part = [&](const int32_t* row, int L, int j0, int j1, int kvh, bool colok, int win0,
+                      bool have_win0) {
     const int nblk = (L + Bm1) >> b_shift;
     const int Lm1 = L - 1;
     const int64_t head_off = int64_t(kvh) * B * GROW + lch * 16;
     for (int jc = j0; jc < j1;) {
       const int jb0 = (jc * kTile) >> b_shift;
-      const int win = jb0 + lane < nblk ? row[jb0 + lane] : 0;
+      const int win = have_win0 && jc == j0 ? win0 : (jb0 + lane < nblk ? row[jb0 + lane] : 0);
       const int jc_end = min(j1, ((jb0 + kWave) << b_shift) / kTile);
       auto load_tile = [&](int j, uint4* kr, uint4* vr) {
         int pb = 0;
@@ -748,6 +873,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
       int j = jc;
 #pragma unroll
       for (int b = 0; b < NB - 1; ++b) load_tile(min(j + b, jc_end - 1), kb[b], vb[b]);
+      flush();  // the previous segment's results, now behind these loads
       for (; j + NB <= jc_end; j += NB) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -768,9 +894,10 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   // group's shared prefix (read through the first member's table row), then
   // the tokens after it of member 0, 1, ... (through that member's row, from
   // the entry of the prefix's end on), each scored by that member's columns.
-  auto run_tiles = [&](const Cursor& x, int j0, int j1) {
+  auto run_tiles = [&](const Cursor& x, int j0, int j1, int win0) {
     if constexpr (!GROUPED) {
-      run_part(a.block_tables + int64_t(x.s) * a.max_blocks_per_seq, x.L, j0, j1, x.kvh, true);
+      run_part(a.block_tables + int64_t(x.s) * a.max_blocks_per_seq, x.L, j0, j1, x.kvh, true,
+               win0, true);
     } else {
       const int s0 = x.s * a.group_size;
       const int P = a.prefix_lens[s0];
@@ -783,22 +910,27 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
         if (lo < hi) {
           const int32_t* row = a.block_tables + int64_t(s) * a.max_blocks_per_seq +
                                (mb < 0 ? 0 : (P >> b_shift));
-          run_part(row, Lp, lo - first, hi - first, x.kvh, mb < 0 || i16 / G == mb);
+          // the part holding tile j0 starts from the prefetched window
+          run_part(row, Lp, lo - first, hi - first, x.kvh, mb < 0 || i16 / G == mb, win0,
+                   lo == j0);
         }
         first += np;
       }
     }
   };
 
-  walk_slice<D, 8, GROUPED>(a, w, lane, n_hchunk, HPW, KVP, begin_segment, run_tiles,
+  walk_slice<D, 8, GROUPED>(a, w, lane, n_hchunk, HPW, KVP, prefetch, begin_segment, run_tiles,
                             end_segment);
+  flush();  // the slice's last segment
 }
 
 // Combine the partials of each split segment. Wave w looks at the segment
 // that wave w of the decode kernel started and left open (if any); its
 // partials are in slot 2w+1 (wave w) and slots 2v for the waves v in
 // (w, last] that continued it.
-template <int DTYPE, int D, int HPW, bool GROUPED>
+// PART_BF16: the partial sums are bf16 rows (written by the matrix-core
+// kernel), else fp32 rows.
+template <int DTYPE, int D, int HPW, bool GROUPED, bool PART_BF16>
 __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kernel(DecodeArgs a) {
   using RS = RowShape<DTYPE, D>;
   constexpr int VEC = RS::VEC, LPR = RS::LPR;
@@ -834,11 +966,19 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kern
 #pragma unroll
       for (int k = 0; k < HPL; ++k) {
         const int hh = min(lane / LPR + k * GROUPS, HPW - 1);
-        ml[q][k] = a.ws_ml[int64_t(sl) * HPW + hh];
-        const float4* src =
-            reinterpret_cast<const float4*>(a.ws_acc + (int64_t(sl) * HPW + hh) * D + c * VEC);
+        ml[q][k] = a.ws_ml[int64_t(sl) * kMLStride + hh];
+        if constexpr (PART_BF16) {
+          static_assert(VEC == 8, "bf16 partials: one 16-byte load per lane");
+          const uint4 b = *reinterpret_cast<const uint4*>(
+              reinterpret_cast<const uint16_t*>(a.ws_acc) + (int64_t(sl) * HPW + hh) * D + c * VEC);
+          x[q][k][0] = make_float4(bf16_lo(b.x), bf16_hi(b.x), bf16_lo(b.y), bf16_hi(b.y));
+          x[q][k][1] = make_float4(bf16_lo(b.z), bf16_hi(b.z), bf16_lo(b.w), bf16_hi(b.w));
+        } else {
+          const float4* src =
+              reinterpret_cast<const float4*>(a.ws_acc + (int64_t(sl) * HPW + hh) * D + c * VEC);
 #pragma unroll
-        for (int e = 0; e < VEC; e += 4) x[q][k][e / 4] = src[e / 4];
+          for (int e = 0; e < VEC; e += 4) x[q][k][e / 4] = src[e / 4];
+        }
       }
     }
 #pragma unroll
@@ -910,7 +1050,7 @@ hipError_t run(const DecodeArgs& a, hipStream_t st) {
             <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      decode_combine_kernel<PA_BF16, D, 2, false><<<groups, kWave * wpg, 0, st>>>(a);
+      decode_combine_kernel<PA_BF16, D, 2, false, true><<<groups, kWave * wpg, 0, st>>>(a);
       return hipGetLastError();
     }
   }
@@ -934,7 +1074,9 @@ hipError_t run(const DecodeArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int OUT = DTYPE == PA_F32 ? PA_F32 : PA_BF16;  // FP8 pools give bf16 output
-  decode_combine_kernel<OUT, D, HPW, false><<<groups, kWave * wpg, 0, st>>>(a);
+  // the matrix-core kernel hands over bf16 partials
+  constexpr bool PART_BF16 = DTYPE == PA_FP8_E4M3 || (DTYPE == PA_BF16 && HPW >= 4);
+  decode_combine_kernel<OUT, D, HPW, false, PART_BF16><<<groups, kWave * wpg, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -957,7 +1099,7 @@ hipError_t run_grouped(const DecodeArgs& a, hipStream_t st) {
     decode_mfma_kernel<D, H, false, DTYPE, 1, true><<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_combine_kernel<PA_BF16, D, H, true><<<groups, kWave * wpg, 0, st>>>(a);
+  decode_combine_kernel<PA_BF16, D, H, true, true><<<groups, kWave * wpg, 0, st>>>(a);
   return hipGetLastError();
 }
 

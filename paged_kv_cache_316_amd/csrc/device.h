@@ -96,7 +96,7 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   float* ws_acc;   // [2 * workers][heads per unit][D] unnormalised partial sums
-  float2* ws_ml;   // [2 * workers][heads per unit] (running max in log2 units, denominator)
+  float2* ws_ml;   // [2 * workers][kMLStride] (running max in log2 units, denominator) per head
   int4* ws_seg;    // [workers] split segment each wave started: (seq, unit, last wave, head)
   int32_t max_blocks_per_seq;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
@@ -137,6 +137,10 @@ hipError_t launch_copy_blocks(const pa_pool& pool, const int32_t* src_dst, int32
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // Columns (query heads of all members) of one unit of the grouped decode.
 constexpr int kGroupedCols = 16;
+// (max, denominator) records per partial slot of the decode workspace: one
+// 128-byte line per slot, whatever the unit's head count, so that a slot's
+// records never share a line with another slot's.
+constexpr int kMLStride = 16;
 bool decode_supported(int dtype, int head_dim, int group);
 // Query heads handled together with their KV head by one wave (divides the group size).
 int decode_heads_per_unit(int group);

@@ -21,7 +21,7 @@ namespace {
 
 // 32 MiB: the default launch (8 wavefronts per compute unit) of the largest
 // unit built (8 query heads of head_dim 128) on 256 compute units needs
-// 16.3 MiB.
+// 16.6 MiB.
 constexpr size_t kScratchBytes = size_t(32) << 20;
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];

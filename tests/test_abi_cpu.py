@@ -87,12 +87,12 @@ def test_decode_argument_checks():
 
 def test_workspace_formula():
     L = lib()
-    # MHA, 100 workers: 2*100 slots x 2 heads (FP8 MHA pairs KV heads) x (128 floats
-    # + (m, l)) + 100 split records
-    assert L.pa_decode_workspace_bytes(64, 40, 40, 128, 100) == 400 * 128 * 4 + 400 * 8 + 100 * 16
+    # MHA, 100 workers: 2*100 slots x 2 heads (FP8 MHA pairs KV heads) x 128 floats,
+    # a 128-byte line of (m, l) records per slot, and 100 split records
+    assert L.pa_decode_workspace_bytes(64, 40, 40, 128, 100) == 400 * 128 * 4 + 200 * 128 + 100 * 16
     # GQA 64/8: 8 query heads per unit
     n = L.pa_decode_workspace_bytes(256, 64, 8, 128, 10)
-    assert n == 20 * 8 * 128 * 4 + 20 * 8 * 8 + 10 * 16
+    assert n == 20 * 8 * 128 * 4 + 20 * 128 + 10 * 16
     assert L.pa_decode_workspace_bytes(4, 6, 4, 128, 10) == 0  # 6 not a multiple of 4
 
 
@@ -168,7 +168,7 @@ def test_shared_prefix_workspace_formula():
     # keys, 1 column block per KV head -> 2 waves per key range; about 4 waves
     # per CU on 256 CUs wants 512 ranges, capped at 256/8 = 32 ranges of 8 tiles
     dec = L.pa_decode_workspace_bytes(2, 2, 2, 128, 10)
-    assert dec == 2 * 10 * 2 * 128 * 4 + 2 * 10 * 2 * 8 + 10 * 16
+    assert dec == 2 * 10 * 2 * 128 * 4 + 2 * 10 * 128 + 10 * 16
     n = L.pa_decode_shared_prefix_workspace_bytes(2, 2, 2, 128, 16, 256, 10)
     # tail lse (4 floats), 32 x (m, l) and 32 x 128 floats per row
     assert n == dec + 16 + 32 * 4 * 8 + 32 * 4 * 128 * 4
