@@ -545,6 +545,14 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_balanced_ker
 // columns score (the others get -inf); so each shared K/V tile is read once
 // for the whole group, and each column's softmax runs over exactly its own
 // sequence's tokens.
+// LDS of one wave of decode_mfma_kernel: a K and a V tile (bf16 rows) per KV
+// head of the unit, then (units of >= 4 columns) two hold slots of HPW result
+// rows; smaller units stage their rows in the idle K tile instead.
+template <int D, int HPW, int KVP>
+constexpr size_t mfma_wave_lds() {
+  return size_t(KVP) * 2 * kTile * 2 * D + (HPW >= 4 ? size_t(2) * HPW * 2 * D : 0);
+}
+
 template <int D, int HPW, bool BIG_B, int KV, int KVP, bool GROUPED>
 __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
@@ -579,7 +587,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   if (w >= a.workers) return;
 
   // this wave's K tiles (one per KV head of the unit), then its V tiles
-  unsigned char* kt_lds = smem + wig * (2 * KVP * TB);
+  unsigned char* kt_lds = smem + wig * mfma_wave_lds<D, HPW, KVP>();
   unsigned char* vt = kt_lds + KVP * TB;
   auto swz = [](int r) { return (r / RPL) % CPR; };
   // load u of lane l: row u*RPI + l/GCPR, pool chunk l%GCPR; in LDS that is
@@ -747,24 +755,64 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
       }
   };
 
-  // Results leave through the wave's own LDS tiles, idle at a segment's end
-  // (LDS serves one wave's accesses in order, so this wave's reads of its
-  // last tile come first): end_segment assembles each column's row there,
-  // and flush() later writes the rows with 16 contiguous bytes per lane, each
-  // store instruction covering whole rows (256 bytes of bf16 output, 512 of
-  // fp32 partials for head_dim 128). flush() runs once the next segment's
-  // first K/V loads are issued (or when the wave is done). Stores and loads
-  // complete in issue order for this wave's counter of outstanding memory
-  // operations, so a store issued before a load delays every use of that
-  // load until the store is acknowledged, and stores that miss the L2 are
-  // acknowledged slowly while the chip streams K/V. Issued at a segment's end,
-  // the results of units of 8 query heads cost the Llama-2-70B-shaped batch
-  // 9 % of its rate.
-  int pend = 0;            // 0: nothing; 1: output rows; 2: partial rows (wave-uniform)
-  Cursor pend_x{};         // the segment the pending rows belong to
-  uint64_t pend_rows = 0;  // output: bit c set when column c's row is written
-  int pend_slot = 0;       // partials: the slot
-  float2 pend_ml = make_float2(0.f, 0.f);
+  // Results are held in the wave's LDS until the wave has streamed all its
+  // K/V: each segment's rows (bf16 output, or bf16 partial sums of a segment
+  // split between waves) go to one of two hold slots after the wave's tiles,
+  // and are written out when the wave is done (or when a third result needs
+  // a slot), 16 contiguous bytes per lane, each store instruction covering
+  // whole rows. (Units of fewer than 4 columns write theirs out earlier,
+  // see kHoldToEnd.) Writes issued while the chip streams K/V cost the stream far
+  // more than their own bytes: with the rows written at each segment's end,
+  // straight from the accumulators, units of 8 query heads lost 9 % of the
+  // rate on the Llama-2-70B-shaped batch (timing-only variants: the same
+  // instructions writing one line, or partials kept in a 256 KB region, ran
+  // at the rate of one-head units).
+  // Units of fewer than 4 columns write little per segment: they stage one
+  // segment's rows in the wave's K tile, idle at a segment's end (LDS serves
+  // one wave's accesses in order, so the reads of the last tile come first),
+  // and write them once the next segment's first K/V loads are issued, before
+  // any of that segment's tiles reach LDS (measured better for the two-head
+  // units of FP8 pools, which are at the register limit).
+  constexpr bool kHoldToEnd = HPW >= 4;
+  constexpr int kSlots = kHoldToEnd ? 2 : 1;
+  static_assert(kHoldToEnd || HPW * ROW <= KVP * TB, "staged rows must fit the K tile");
+  unsigned char* hold = kHoldToEnd ? kt_lds + 2 * KVP * TB : kt_lds;  // kSlots x HPW rows
+  // What each hold slot holds (wave-uniform, plain registers): kind 1 = output
+  // rows (bit c of rows: column c's row is written), 2 = partial rows for the
+  // workspace slot `slot`; s, kvh, hc: the segment.
+  int held = 0;
+  int kind0 = 0, s0 = 0, kvh0 = 0, hc0 = 0, slot0 = 0;
+  int kind1 = 0, s1 = 0, kvh1 = 0, hc1 = 0, slot1 = 0;
+  uint64_t rows0 = 0, rows1 = 0;
+  float2 ml0 = make_float2(0.f, 0.f), ml1 = make_float2(0.f, 0.f);  // partials' (m, l)
+  auto write_held = [&](int kind, int sq, int kvh, int hc, uint64_t rows, int slot,
+                        const unsigned char* rows_lds, float2 ml) {
+    Cursor x{};
+    x.s = sq;
+    x.kvh = kvh;
+    x.hc = hc;
+    constexpr int LPRW = ROW / 16;     // lanes per row
+    constexpr int RPW = kWave / LPRW;  // rows per store instruction
+    unsigned char* part = reinterpret_cast<unsigned char*>(a.ws_acc);  // bf16 partial rows
+#pragma unroll 1
+    for (int it = 0; it < (HPW + RPW - 1) / RPW; ++it) {
+      const int cc = it * RPW + lane / LPRW;
+      const bool use = cc < ncols && (kind == 2 || ((rows >> cc) & 1));
+      if (use) {
+        const uint4 v = *reinterpret_cast<const uint4*>(rows_lds + cc * ROW + (lane % LPRW) * 16);
+        unsigned char* dst = kind == 1 ? static_cast<unsigned char*>(a.out) + row_of(x, cc) * ROW
+                                       : part + (int64_t(slot) * HPW + cc) * ROW;
+        *reinterpret_cast<uint4*>(dst + (lane % LPRW) * 16) = v;
+      }
+    }
+    if (kind == 2 && g == 0 && i16 < ncols) a.ws_ml[int64_t(slot) * kMLStride + i16] = ml;
+  };
+  auto flush = [&]() {
+    if (held > 0) write_held(kind0, s0, kvh0, hc0, rows0, slot0, hold, ml0);
+    if (kSlots > 1 && held > 1)
+      write_held(kind1, s1, kvh1, hc1, rows1, slot1, hold + HPW * ROW, ml1);
+    held = 0;
+  };
   auto end_segment = [&](const Cursor& x, bool owns_start, bool owns_end) {
     float l = lpart + __shfl_xor(lpart, 16);
     l += __shfl_xor(l, 32);
@@ -773,8 +821,13 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     f32x4_t oc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oc[dt] = KVP == 2 && i16 >= CPH ? o[KVP - 1][dt] : o[0][dt];
-    unsigned char* stage = kt_lds;  // KVP * 2 * TB bytes: 16 rows of fp32 partials fit
-    pend_x = x;
+    if (held == kSlots) flush();
+    const int h = kSlots == 1 ? 0 : held;
+    ++held;
+    unsigned char* rows_lds = hold + h * HPW * ROW;
+    int kind, slot = 0;
+    uint64_t rows = 0;
+    float2 ml = make_float2(0.f, 0.f);
     if (owns_start && owns_end) {
       // a grouped member without tokens scored nothing: the walk wrote its zeros
       const bool keep = col && (!GROUPED || l > 0.f);
@@ -783,58 +836,31 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
       if (keep) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<uint2*>(stage + i16 * ROW + (16 * dt + 4 * g) * 2) =
+          *reinterpret_cast<uint2*>(rows_lds + i16 * ROW + (16 * dt + 4 * g) * 2) =
               make_uint2(pack_bf16(oc[dt][0] * inv, oc[dt][1] * inv),
                          pack_bf16(oc[dt][2] * inv, oc[dt][3] * inv));
       }
-      pend_rows = __ballot(g == 0 && keep);
-      pend = 1;
-      return;
-    }
-    // a split segment's partial sums go to the combine as bf16 (the (max,
-    // denominator) record stays fp32): half the bytes, and the writes back to
-    // memory of these partials cost the read stream far more than their size
-    if (col) {
+      kind = 1;
+      rows = __ballot(g == 0 && keep);
+    } else {
+      // partial sums of a split segment go to the combine as bf16 (the (max,
+      // denominator) record stays fp32); accumulation in the wave was fp32
+      if (col) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<uint2*>(stage + i16 * ROW + (16 * dt + 4 * g) * 2) =
-            make_uint2(pack_bf16(oc[dt][0] * vsc, oc[dt][1] * vsc),
-                       pack_bf16(oc[dt][2] * vsc, oc[dt][3] * vsc));
-    }
-    pend_slot = 2 * w + (owns_start ? 1 : 0);
-    pend_ml = make_float2(m * c2, l);
-    pend = 2;
-  };
-  auto flush = [&]() {
-    const unsigned char* stage = kt_lds;
-    if (pend == 1) {
-      constexpr int LPRW = ROW / 16;     // lanes per bf16 row
-      constexpr int RPW = kWave / LPRW;  // rows per store instruction
-#pragma unroll 1
-      for (int it = 0; it < (HPW + RPW - 1) / RPW; ++it) {
-        const int cc = it * RPW + lane / LPRW;
-        if (cc < ncols && ((pend_rows >> cc) & 1)) {
-          const uint4 v = *reinterpret_cast<const uint4*>(stage + cc * ROW + (lane % LPRW) * 16);
-          *reinterpret_cast<uint4*>(static_cast<unsigned char*>(a.out) + row_of(pend_x, cc) * ROW +
-                                    (lane % LPRW) * 16) = v;
-        }
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<uint2*>(rows_lds + i16 * ROW + (16 * dt + 4 * g) * 2) =
+              make_uint2(pack_bf16(oc[dt][0] * vsc, oc[dt][1] * vsc),
+                         pack_bf16(oc[dt][2] * vsc, oc[dt][3] * vsc));
       }
-    } else if (pend == 2) {
-      constexpr int LPRW = ROW / 16;     // lanes per bf16 row
-      constexpr int RPW = kWave / LPRW;  // rows per store instruction
-      unsigned char* part = reinterpret_cast<unsigned char*>(a.ws_acc);  // bf16 rows
-#pragma unroll 1
-      for (int it = 0; it < (HPW + RPW - 1) / RPW; ++it) {
-        const int cc = it * RPW + lane / LPRW;
-        if (cc < ncols) {
-          const uint4 v = *reinterpret_cast<const uint4*>(stage + cc * ROW + (lane % LPRW) * 16);
-          *reinterpret_cast<uint4*>(part + (int64_t(pend_slot) * HPW + cc) * ROW +
-                                    (lane % LPRW) * 16) = v;
-        }
-      }
-      if (g == 0 && i16 < ncols) a.ws_ml[int64_t(pend_slot) * kMLStride + i16] = pend_ml;
+      kind = 2;
+      slot = 2 * w + (owns_start ? 1 : 0);
+      ml = make_float2(m * c2, l);
     }
-    pend = 0;
+    if (kSlots == 1 || h == 0) {
+      kind0 = kind; s0 = x.s; kvh0 = x.kvh; hc0 = x.hc; rows0 = rows; slot0 = slot; ml0 = ml;
+    } else {
+      kind1 = kind; s1 = x.s; kvh1 = x.kvh; hc1 = x.hc; rows1 = rows; slot1 = slot; ml1 = ml;
+    }
   };
 
   // Tiles [j0, j1) of a run of L tokens whose blocks are row[0], row[1], ...,
@@ -873,7 +899,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
       int j = jc;
 #pragma unroll
       for (int b = 0; b < NB - 1; ++b) load_tile(min(j + b, jc_end - 1), kb[b], vb[b]);
-      flush();  // the previous segment's results, now behind these loads
+      if constexpr (!kHoldToEnd) flush();  // the previous segment's staged rows
       for (; j + NB <= jc_end; j += NB) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -921,7 +947,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
 
   walk_slice<D, 8, GROUPED>(a, w, lane, n_hchunk, HPW, KVP, prefetch, begin_segment, run_tiles,
                             end_segment);
-  flush();  // the slice's last segment
+  flush();  // the wave is done: its held results
 }
 
 // Combine the partials of each split segment. Wave w looks at the segment
@@ -1041,7 +1067,7 @@ hipError_t run(const DecodeArgs& a, hipStream_t st) {
   // (one contiguous run of both heads' rows per tile), combined as 2 heads
   if constexpr (DTYPE == PA_FP8_E4M3 && HPW == 1) {
     if (a.num_q_heads == a.num_kv_heads && a.num_kv_heads % 2 == 0) {
-      const size_t lds = size_t(wpg) * 2 * 2 * kTile * 2 * D;  // K and V tiles of 2 heads
+      const size_t lds = size_t(wpg) * mfma_wave_lds<D, 2, 2>();
       if (a.block_size >= kTile)
         decode_mfma_kernel<D, 2, true, DTYPE, 2, false>
             <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
@@ -1056,7 +1082,7 @@ hipError_t run(const DecodeArgs& a, hipStream_t st) {
   }
   // bf16 groups of >= 4 heads and every FP8 pool run on the matrix cores
   if constexpr (DTYPE == PA_FP8_E4M3 || (DTYPE == PA_BF16 && HPW >= 4)) {
-    const size_t lds = size_t(wpg) * 2 * kTile * 2 * D;  // a K and a V tile per wave (bf16)
+    const size_t lds = size_t(wpg) * mfma_wave_lds<D, HPW, 1>();
     if (a.block_size >= kTile)
       decode_mfma_kernel<D, HPW, true, DTYPE, 1, false>
           <<<groups, kWave * wpg, lds, st>>>(a, b_shift, n_hchunk, scale_log2);
@@ -1091,8 +1117,8 @@ hipError_t run_grouped(const DecodeArgs& a, hipStream_t st) {
   wpg = wpg < 1 ? 1 : (wpg > kMaxWavesPerGroup ? kMaxWavesPerGroup : wpg);
   const int groups = (a.workers + wpg - 1) / wpg;
   const float scale_log2 = a.scale * kLog2e;
-  const size_t lds = size_t(wpg) * 2 * kTile * 2 * D;  // a K and a V tile per wave (bf16)
   constexpr int H = kGroupedCols;
+  const size_t lds = size_t(wpg) * mfma_wave_lds<D, H, 1>();
   if (a.block_size >= kTile)
     decode_mfma_kernel<D, H, true, DTYPE, 1, true><<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
   else
