@@ -510,6 +510,49 @@ def mixed_row(ld, steps, warmup, workers):
                                  "chunks' flops at 2.5 PFLOP/s (perfect overlap)"}}
 
 
+def spec_verify_row(ld, steps, warmup, workers, k=4):
+    """Speculative-decoding verification on the Llama-2-70B-shaped batch: every
+    sequence checks k draft tokens in one call, its last k positions taken as
+    causal chunk rows ("vLLM PagedAttention explained", section 7.2: a chunk's
+    rows attend causally to the sequence's cached keys), on the chunked-prefill
+    kernel; beside the plain decode of the same batch (one row per sequence)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_316_amd as pkv
+    wl = ld.wl
+    S = len(wl.decode_seqs)
+    rng = np.random.default_rng(77)
+    q = torch.from_numpy(rng.standard_normal((S * k, wl.num_q_heads, wl.head_dim))
+                         .astype(np.float32)).to(torch.bfloat16).cuda()
+    loc = torch.arange(0, S * k + 1, k, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev):
+        p = ld.pools[i % len(ld.pools)]
+        if ev is not None:
+            ev[0].record(stream)
+            ev[1].record(stream)
+        pkv.prefill_chunk(q, loc, ld.lens_d, p, ld.tables_d, k, wl.scale, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+    _, _, v_ms = time_steps(step, steps, warmup)
+    _, _, d_ms = time_steps(decode_step_fn(ld, workers), steps, warmup)
+    t = float(v_ms.mean()) * 1e-3
+    gbps = ld.kv_bytes / t / 1e9
+    lens = ld.lens.astype("int64")
+    pairs = int(sum(int(L) * k - k * (k - 1) // 2 for L in lens))  # visible (row, key) pairs
+    return {"workload": WORKLOAD_TEXT[ld.name] + f"; every sequence verifies {k} draft tokens "
+                        "(its last positions as causal chunk rows)",
+            "draft_rows_per_seq": k, "verify_us": _stats_us(v_ms), "decode_us": _stats_us(d_ms),
+            "verify_over_decode": round(float(v_ms.mean() / d_ms.mean()), 3),
+            "kv_bytes": int(ld.kv_bytes), "flops": 4.0 * wl.head_dim * wl.num_q_heads * pairs,
+            "draft_tokens_per_s": round(S * k / t, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "kernel": "pa_prefill_chunk (k-row chunks, bf16 MFMA)"}}
+
+
 HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction
 
 
@@ -796,8 +839,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-rows", action="store_true",
                     help="skip the Llama-2-70B-shaped GQA decode, chunked-prefill, mixed-step, "
-                         "FP8-KV decode, block-swap, block-layout, tensor-parallel-shard, "
-                         "shared-block and shared-prefix decode rows")
+                         "speculative-verification, FP8-KV decode, block-swap, block-layout, "
+                         "tensor-parallel-shard, shared-block and shared-prefix decode rows")
     ap.add_argument("--rows", default="",
                     help="comma-separated extra rows to run (default: all), e.g. "
                          "prefill_llama70b,swap_llama13b")
@@ -914,6 +957,10 @@ def main():
             switch("llama70b")
             rows["mixed_llama70b_step"] = mixed_row(ld, max(10, args.steps // 10),
                                                     min(args.warmup, 5), args.workers)
+        if want("spec_verify_llama70b"):
+            switch("llama70b")
+            rows["spec_verify_llama70b"] = spec_verify_row(ld, short, min(args.warmup, 5),
+                                                           args.workers)
         if want("decode_llama13b_fp8") and args.workload != "llama13b_fp8":
             switch("llama13b_fp8")
             f = rows["decode_llama13b_fp8"] = decode_row(ld, short, args.warmup, args.workers)

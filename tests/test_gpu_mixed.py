@@ -144,6 +144,9 @@ class _Bf16:
     (16, 16, 64, 4, [5, 1000], [(64, 64), (3, 90)]),
     (6, 2, 128, 32, [], [(50, 50), (129, 260)]),              # chunks only
     (12, 4, 64, 8, [9, 19, 1, 333], []),                      # decode rows only
+    # speculative-decoding verification: a few draft rows per sequence
+    (16, 2, 128, 16, [70], [(4, 300), (5, 77), (2, 1000), (8, 8), (3, 513), (6, 6)]),
+    (8, 8, 128, 16, [], [(2, 2), (7, 129), (4, 2048)]),
 ])
 def test_mixed_ragged(case):
     Hq, Hkv, D, B, dl, chunks = case
