@@ -755,18 +755,17 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
       }
   };
 
-  // Results are held in the wave's LDS until the wave has streamed all its
-  // K/V: each segment's rows (bf16 output, or bf16 partial sums of a segment
-  // split between waves) go to one of two hold slots after the wave's tiles,
-  // and are written out when the wave is done (or when a third result needs
-  // a slot), 16 contiguous bytes per lane, each store instruction covering
-  // whole rows. (Units of fewer than 4 columns write theirs out earlier,
-  // see kHoldToEnd.) Writes issued while the chip streams K/V cost the stream far
-  // more than their own bytes: with the rows written at each segment's end,
-  // straight from the accumulators, units of 8 query heads lost 9 % of the
-  // rate on the Llama-2-70B-shaped batch (timing-only variants: the same
-  // instructions writing one line, or partials kept in a 256 KB region, ran
-  // at the rate of one-head units).
+  // Units of 4 or more columns hold their results in the wave's LDS until
+  // the wave has streamed all its K/V: each segment's rows (bf16 output, or
+  // bf16 partial sums of a segment split between waves) go to one of two
+  // hold slots after the wave's tiles, and are written out when the wave is
+  // done (or when a third result needs a slot), 16 contiguous bytes per lane,
+  // each store instruction covering whole rows. Writes issued while the chip
+  // streams K/V cost the stream far more than their own bytes: with the rows
+  // written at each segment's end, straight from the accumulators, units of 8
+  // query heads lost 9 % of the rate on the Llama-2-70B-shaped batch
+  // (timing-only variants: the same instructions writing one line, or
+  // partials kept in a 256 KB region, ran at the rate of one-head units).
   // Units of fewer than 4 columns write little per segment: they stage one
   // segment's rows in the wave's K tile, idle at a segment's end (LDS serves
   // one wave's accesses in order, so the reads of the last tile come first),
@@ -1132,7 +1131,11 @@ hipError_t run_grouped(const DecodeArgs& a, hipStream_t st) {
 template <int DTYPE, int D>
 hipError_t run_d(const DecodeArgs& a, hipStream_t st) {
   switch (decode_heads_per_unit(a.num_q_heads / a.num_kv_heads)) {
-    case 8: return run<DTYPE, D, 8>(a, st);
+    // fp32 rows of 128 dims with 8 heads per unit would spill registers: two
+    // units of 4 heads per KV head instead (each reads the KV head's rows)
+    case 8:
+      if constexpr (DTYPE == PA_F32 && D == 128) return run<DTYPE, D, 4>(a, st);
+      else return run<DTYPE, D, 8>(a, st);
     case 4: return run<DTYPE, D, 4>(a, st);
     case 2: return run<DTYPE, D, 2>(a, st);
     default: return run<DTYPE, D, 1>(a, st);
