@@ -13,6 +13,7 @@
 // its table entry j).
 #include <algorithm>
 #include <cstdint>
+#include <utility>
 #include <vector>
 
 #include "pagedkv.h"
@@ -69,18 +70,23 @@ pa_status pa_check_slots(const pa_pool* pool, const int64_t* slot_mapping, int32
   if (num_tokens == 0) return PA_OK;
   if (!slot_mapping) return fail(PA_ERR_INVALID, "%s: slot_mapping is NULL", who);
   const int64_t n_slots = int64_t(pool->num_blocks) * pool->block_size;
-  std::vector<int32_t> first(size_t(n_slots), -1);  // token that wrote each slot
+  // (slot, token) of every written token, sorted: a slot named twice shows up
+  // as two neighbours (memory and time follow the tokens, not the pool)
+  std::vector<std::pair<int64_t, int32_t>> named;
+  named.reserve(size_t(num_tokens));
   for (int32_t t = 0; t < num_tokens; ++t) {
     const int64_t slot = slot_mapping[t];
     if (slot < 0) continue;  // padding: skipped by the write
     if (slot >= n_slots)
       return fail(PA_ERR_INVALID, "%s: slot_mapping[%d]=%lld >= num_blocks * B = %lld", who, t,
                   static_cast<long long>(slot), static_cast<long long>(n_slots));
-    if (first[size_t(slot)] >= 0)
-      return fail(PA_ERR_INVALID, "%s: slot %lld named by tokens %d and %d", who,
-                  static_cast<long long>(slot), first[size_t(slot)], t);
-    first[size_t(slot)] = t;
+    named.emplace_back(slot, t);
   }
+  std::sort(named.begin(), named.end());
+  for (size_t i = 1; i < named.size(); ++i)
+    if (named[i].first == named[i - 1].first)
+      return fail(PA_ERR_INVALID, "%s: slot %lld named by tokens %d and %d", who,
+                  static_cast<long long>(named[i].first), named[i - 1].second, named[i].second);
   return PA_OK;
 }
 
