@@ -512,10 +512,14 @@ def mixed_row(ld, steps, warmup, workers):
 
 def spec_verify_row(ld, steps, warmup, workers, k=4):
     """Speculative-decoding verification on the Llama-2-70B-shaped batch: every
-    sequence checks k draft tokens in one call, its last k positions taken as
-    causal chunk rows ("vLLM PagedAttention explained", section 7.2: a chunk's
-    rows attend causally to the sequence's cached keys), on the chunked-prefill
-    kernel; beside the plain decode of the same batch (one row per sequence)."""
+    sequence checks k draft tokens in one call ("vLLM PagedAttention
+    explained" section 7.5, "vLLM inference engine deep dive" section 5.2: the
+    target model verifies the draft model's tokens in one pass), its last k
+    positions taken as causal chunk rows (section 7.2 of the first page).
+    pa_attention_mixed
+    runs such short chunks as one multi-row decode (each K/V row read once for
+    all k rows); beside it the same rows on the chunked-prefill kernel and the
+    plain decode of the batch (one row per sequence)."""
     import numpy as np
     import torch
     import paged_kv_cache_316_amd as pkv
@@ -526,17 +530,26 @@ def spec_verify_row(ld, steps, warmup, workers, k=4):
                          .astype(np.float32)).to(torch.bfloat16).cuda()
     loc = torch.arange(0, S * k + 1, k, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
+    ws = torch.empty(max(16, pkv.attention_mixed_workspace_bytes(0, S, wl.num_q_heads,
+                                                                 wl.num_kv_heads, wl.head_dim, k,
+                                                                 workers)),
+                     dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(i, ev):
-        p = ld.pools[i % len(ld.pools)]
-        if ev is not None:
-            ev[0].record(stream)
-            ev[1].record(stream)
-        pkv.prefill_chunk(q, loc, ld.lens_d, p, ld.tables_d, k, wl.scale, out=out)
-        if ev is not None:
-            ev[2].record(stream)
-    _, _, v_ms = time_steps(step, steps, warmup)
+    def timed(call):
+        def step(i, ev):
+            p = ld.pools[i % len(ld.pools)]
+            if ev is not None:
+                ev[0].record(stream)
+                ev[1].record(stream)
+            call(p)
+            if ev is not None:
+                ev[2].record(stream)
+        return time_steps(step, steps, warmup)[2]
+    v_ms = timed(lambda p: pkv.attention_mixed(q, loc, ld.lens_d, p, ld.tables_d, 0, k, wl.scale,
+                                               workers, out=out, workspace=ws))
+    pf_ms = timed(lambda p: pkv.prefill_chunk(q, loc, ld.lens_d, p, ld.tables_d, k, wl.scale,
+                                              out=out))
     _, _, d_ms = time_steps(decode_step_fn(ld, workers), steps, warmup)
     t = float(v_ms.mean()) * 1e-3
     gbps = ld.kv_bytes / t / 1e9
@@ -544,13 +557,15 @@ def spec_verify_row(ld, steps, warmup, workers, k=4):
     pairs = int(sum(int(L) * k - k * (k - 1) // 2 for L in lens))  # visible (row, key) pairs
     return {"workload": WORKLOAD_TEXT[ld.name] + f"; every sequence verifies {k} draft tokens "
                         "(its last positions as causal chunk rows)",
-            "draft_rows_per_seq": k, "verify_us": _stats_us(v_ms), "decode_us": _stats_us(d_ms),
+            "draft_rows_per_seq": k, "verify_us": _stats_us(v_ms),
+            "prefill_kernel_path_us": _stats_us(pf_ms), "decode_us": _stats_us(d_ms),
             "verify_over_decode": round(float(v_ms.mean() / d_ms.mean()), 3),
             "kv_bytes": int(ld.kv_bytes), "flops": 4.0 * wl.head_dim * wl.num_q_heads * pairs,
             "draft_tokens_per_s": round(S * k / t, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                         "kernel": "pa_prefill_chunk (k-row chunks, bf16 MFMA)"}}
+                         "kernel": "pa_attention_mixed, multi-row decode (k x G = 32 columns "
+                                   "per (sequence, KV head))"}}
 
 
 HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction

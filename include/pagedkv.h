@@ -356,24 +356,38 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,
  *   out, q       : device, [total_rows][num_q_heads][head_dim], the pool's dtype
  *                  (bf16 for a PA_FP8_E4M3 pool)
  *   q_start_loc  : device, int32 [num_decode + num_prefill + 1]; q_start_loc[i]
- *                  = i for i <= num_decode (only entries num_decode.. are read,
- *                  and only when num_prefill > 0)
+ *                  = i for i <= num_decode (read only when num_prefill > 0)
  *   seq_lens     : device, int32 [num_decode + num_prefill], tokens in the pool
  *                  for each sequence, its rows of this call included
  *   block_tables : device, int32 [num_decode + num_prefill][max_blocks_per_seq]
  *   max_q_len    : host, >= every prefill chunk's row count
  *   num_workers  : decode wavefronts; 0 = default (3 per compute unit when the
- *                  batch also has chunks, else pa_decode's default)
- *   workspace    : device, pa_decode_workspace_bytes(num_decode, num_q_heads,
- *                  num_kv_heads, head_dim, num_workers) bytes suffice (unused
- *                  when num_decode is 0)
- * With both kinds of rows, the chunks run on a second stream of the library's
- * (one per host thread and device, default priority) that forks from and joins
- * back into `stream`, so that the two kernels share the chip.
+ *                  batch also has chunks, 4 on the multi-row path below, else
+ *                  pa_decode's default)
+ *   workspace    : device, pa_attention_mixed_workspace_bytes(num_decode,
+ *                  num_prefill, num_q_heads, num_kv_heads, head_dim, max_q_len,
+ *                  num_workers) bytes, 16-byte aligned (unused when the batch
+ *                  has no decode rows and no short chunks)
+ * Short chunks (a bf16 pool and max_q_len * num_q_heads / num_kv_heads <= 32:
+ * small prompt pieces, and the target model checking a draft model's k tokens
+ * in one pass, "vLLM PagedAttention explained" section 7.5 and "vLLM inference
+ * engine deep dive" section 5.2) take the multi-row
+ * decode: every sequence, decode rows included, is one unit per KV head whose
+ * MFMA columns are its (row, query head) pairs, each masked at its own row's
+ * position, so each K/V row is read once for all of a sequence's rows.
+ * Otherwise, with both kinds of rows, the chunks run on a second stream of the
+ * library's (one per host thread and device, default priority) that forks
+ * from and joins back into `stream`, so that the two kernels share the chip.
  * Prefill rows need a bf16 pool (PA_ERR_UNSUPPORTED otherwise); decode rows
  * take every pa_decode dtype. Each row's result is that of pa_decode or
  * pa_prefill_chunk for it alone (up to the decode's worker count).
  */
+/* Workspace bytes of pa_attention_mixed for a batch of this shape (0 for
+ * invalid sizes). */
+size_t pa_attention_mixed_workspace_bytes(int32_t num_decode, int32_t num_prefill,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t max_q_len,
+                                          int32_t num_workers);
 pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_loc,
                              const int32_t* seq_lens, const pa_pool* pool,
                              const int32_t* block_tables, int32_t max_blocks_per_seq,

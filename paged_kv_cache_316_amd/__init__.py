@@ -15,6 +15,7 @@ from .ops import (DecodePlan, KVPool, attention_mixed, cache_write, check_batch,
                   decode_grouped, decode_grouped_workspace_bytes, check_grouped,
                   group_prefix_lens, set_input_checks,
                   decode_shared_prefix_workspace_bytes, decode_workspace_bytes, prefill_chunk,
+                  attention_mixed_workspace_bytes,
                   probe_stream_read, swap_blocks, swap_in, swap_out, PA_SWAP_IN, PA_SWAP_OUT)
 
 __all__ = ["AllocatorStateError", "OutOfBlocks", "PagedKVError", "LIB_PATH", "SIGNATURES", "lib",
@@ -24,5 +25,5 @@ __all__ = ["AllocatorStateError", "OutOfBlocks", "PagedKVError", "LIB_PATH", "SI
            "decode_grouped_workspace_bytes", "check_grouped", "group_prefix_lens",
            "set_input_checks",
            "decode_shared_prefix", "decode_shared_prefix_workspace_bytes",
-           "decode_workspace_bytes", "prefill_chunk", "probe_stream_read", "swap_blocks", "swap_in",
+           "decode_workspace_bytes", "attention_mixed_workspace_bytes", "prefill_chunk", "probe_stream_read", "swap_blocks", "swap_in",
            "swap_out", "PA_SWAP_IN", "PA_SWAP_OUT"]

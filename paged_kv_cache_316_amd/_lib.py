@@ -51,6 +51,7 @@ SIGNATURES = {
                                     c_int32, c_int32, c_float, c_int32, c_void_p]),
     "pa_decode_noalloc_scratch_bytes": (c_size_t, []),
     "pa_decode_grouped_workspace_bytes": (c_size_t, [c_int32] * 5),
+    "pa_attention_mixed_workspace_bytes": (c_size_t, [c_int32] * 7),
     "pa_decode_grouped": (c_int32, [c_void_p, c_void_p, _P(PaPool), c_void_p, c_int32, c_void_p,
                                     c_void_p, c_int32, c_int32, c_int32, c_float, c_int32,
                                     c_void_p, c_size_t, c_void_p]),

@@ -2,6 +2,7 @@
 // workspace sizing and dispatch to the HIP launchers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -69,6 +70,28 @@ DecodeLayout grouped_layout(int32_t head_dim, int32_t workers) {
   d.ml_bytes = size_t(2) * d.workers * kMLStride * 8;
   d.seg_bytes = size_t(d.workers) * 16;
   return d;
+}
+
+// Multi-row decode: slots of kMultiRowCols bf16 partial rows, records of as
+// many (max, denominator) pairs; one wave per SIMD by default.
+DecodeLayout multirow_layout(int32_t head_dim, int32_t workers) {
+  DecodeLayout d{};
+  d.workers = workers > 0 ? workers : device_cus() * kMultiRowWaves;
+  d.heads_per_unit = kMultiRowCols;
+  const size_t slots = size_t(2) * d.workers * d.heads_per_unit;
+  d.acc_bytes = slots * head_dim * 2;
+  d.ml_bytes = slots * 8;
+  d.seg_bytes = size_t(d.workers) * 16;
+  return d;
+}
+
+// A mixed batch runs as one multi-row decode when its chunks are short: a
+// bf16 pool and every sequence's rows x query heads per KV head within the
+// columns of one unit.
+bool multirow_fits(int32_t dtype, int32_t head_dim, int32_t G, int32_t num_prefill,
+                   int32_t max_q_len) {
+  return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) && num_prefill > 0 &&
+         max_q_len >= 1 && int64_t(max_q_len) * G <= kMultiRowCols;
 }
 
 // Members per unit of the grouped decode: the largest divisor of group_size
@@ -199,6 +222,7 @@ DecodeArgs decode_args(void* out, const void* q, const pa_pool* pool, const int3
   a.prefix_lens = nullptr;
   a.group_size = 1;
   a.num_groups = num_seqs;
+  a.q_start_loc = nullptr;
   return a;
 }
 
@@ -371,6 +395,27 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
       num_workers < 0 || num_q_heads % num_kv_heads)
     return 0;
   return pa::decode_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers).total();
+}
+
+size_t pa_attention_mixed_workspace_bytes(int32_t num_decode, int32_t num_prefill,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t max_q_len,
+                                          int32_t num_workers) {
+  if (num_decode < 0 || num_prefill < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || max_q_len < 0 || num_workers < 0 || num_q_heads % num_kv_heads)
+    return 0;
+  const int32_t G = num_q_heads / num_kv_heads;
+  size_t need = 16;
+  if (pa::multirow_fits(PA_BF16, head_dim, G, num_prefill, max_q_len))
+    return std::max(need, pa::multirow_layout(head_dim, num_workers).total());
+  if (num_decode > 0) {
+    const bool both = num_prefill > 0 && max_q_len > 0;
+    const int32_t workers =
+        num_workers > 0 ? num_workers : (both ? pa::device_cus() * pa::kMixedDecodeWavesPerCU : 0);
+    need = std::max(need, pa::decode_layout(num_decode, num_q_heads, num_kv_heads, head_dim,
+                                            workers).total());
+  }
+  return need;
 }
 
 pa_status pa_decode(void* out, const void* q, const pa_pool* pool, const int32_t* block_tables,
@@ -563,6 +608,24 @@ pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_lo
     return fail(PA_ERR_UNSUPPORTED, "%s: dtype=%d head_dim=%d group=%d not built", who,
                 pool->dtype, pool->head_dim, G);
   const bool chunks = num_prefill > 0 && max_q_len > 0;
+  if (pa::multirow_fits(pool->dtype, pool->head_dim, G, num_prefill, max_q_len)) {
+    // short chunks (speculative verification, small prompt pieces): decode
+    // rows and chunk rows in one multi-row decode over all the sequences
+    const pa::DecodeLayout lay = pa::multirow_layout(pool->head_dim, num_workers);
+    if (!workspace || workspace_bytes < lay.total())
+      return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed "
+                  "(pa_attention_mixed_workspace_bytes)", who,
+                  workspace ? workspace_bytes : size_t(0), lay.total());
+    if (reinterpret_cast<uintptr_t>(workspace) & 15)
+      return fail(PA_ERR_INVALID, "%s: workspace must be 16-byte aligned", who);
+    if (int64_t(num_decode) + num_prefill >= (int64_t(1) << 30))
+      return fail(PA_ERR_UNSUPPORTED, "%s: too many sequences", who);
+    pa::DecodeArgs a = pa::decode_args(out, q, pool, block_tables, max_blocks_per_seq, seq_lens,
+                                       num_decode + num_prefill, num_q_heads, scale, lay,
+                                       workspace);
+    a.q_start_loc = q_start_loc;
+    return pa::hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)), who);
+  }
   const bool both = chunks && num_decode > 0;
   // With both kinds of rows, the chunks (bound by the compute units) run on a
   // second stream beside the decode rows (bound by HBM), joined before return.

@@ -194,9 +194,10 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
   total = uniform64(total * units);
   const int64_t W = total < a.workers ? total : a.workers;  // every active wave gets >= 1 tile
 
-  // empty sequences: zeros, written by wave (s mod Wz)
+  // empty sequences: zeros, written by wave (s mod Wz) (a multi-row batch
+  // has no rows for them: a sequence's rows are already in its length)
   const int Wz = W > 0 ? int(W) : a.workers;
-  for (int s = w; s < a.num_seqs; s += Wz) {
+  for (int s = w; s < (a.q_start_loc ? 0 : a.num_seqs); s += Wz) {
     if ((GROUPED ? a.seq_lens[s] : len_of(a, s)) > 0) continue;
     uint4* o = static_cast<uint4*>(a.out) + (int64_t(s) * Hq * D) / VEC;
     for (int i = lane; i < Hq * D / VEC; i += kWave) o[i] = make_uint4(0, 0, 0, 0);
@@ -553,11 +554,16 @@ constexpr size_t mfma_wave_lds() {
   return size_t(KVP) * 2 * kTile * 2 * D + (HPW >= 4 ? size_t(2) * HPW * 2 * D : 0);
 }
 
-template <int D, int HPW, bool BIG_B, int KV, int KVP, bool GROUPED>
-__global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
+template <int D, int HPW, bool BIG_B, int KV, int KVP, bool GROUPED, bool MR = false>
+__global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) void decode_mfma_kernel(
     DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
   static_assert(!GROUPED || (KVP == 1 && HPW == kGroupedCols), "grouped units: 16 columns");
+  static_assert(!MR || (KVP == 1 && !GROUPED && HPW == kMultiRowCols), "multi-row units: 32 columns");
   constexpr bool FP8 = KV == PA_FP8_E4M3;
+  // MFMA column tiles of 16: multi-row units (MR) have two; a lane holds
+  // column ct * 16 + lane % 16 of tile ct
+  constexpr int NCT = MR ? 2 : 1;
+  constexpr int MLS = HPW > kMLStride ? HPW : kMLStride;  // (m, l) records per workspace slot
   constexpr int ROW = 2 * D;        // bytes per bf16 K/V row in LDS
   constexpr int GROW = FP8 ? D : ROW;  // bytes per row in the pool
   constexpr int KS = D / 32;        // 16x16x32 k-steps over head_dim
@@ -574,7 +580,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   // tiles in flight per wave: an FP8 tile is half the bytes, so more of them
   // are needed to keep as many bytes in flight (a paired tile is twice the bytes)
   constexpr int NB = FP8 && KVP == 1 ? 4 : 2;
-  static_assert(HPW <= 16, "one MFMA N tile holds the unit's heads");
+  static_assert(HPW <= 16 * NCT, "the MFMA N tiles hold the unit's columns");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int lane = threadIdx.x % kWave;
@@ -611,16 +617,20 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   const unsigned char* vp = static_cast<const unsigned char*>(a.v_pool);
   const int64_t block_bytes = int64_t(Hkv) * B * GROW;
 
-  uint4 qop[KS], qnext[KS];
-  f32x4_t o[KVP][DT];
-  float m, lpart;
+  uint4 qop[NCT][KS], qnext[NCT][KS];
+  f32x4_t o[KVP * NCT][DT];
+  float m[NCT], lpart[NCT];
+  int lim[NCT];  // multi-row: keys a column attends (its row's position + 1; 0 if unused)
   const float c2 = FP8 ? scale_log2 * a.k_scale : scale_log2;
   const float vsc = FP8 ? a.v_scale : 1.f;
-  const int ncols = GROUPED ? a.group_size * G : HPW;  // columns in use
+  // columns in use (multi-row: of the current segment, rows of its sequence x G)
+  int ncols = GROUPED ? a.group_size * G : HPW;
+  auto rows_of = [&](int sq) { return a.q_start_loc[sq + 1] - a.q_start_loc[sq]; };
   auto head_of = [&](const Cursor& x) { return x.kvh * G + x.hc * HPW; };
-  // (sequence, query head) row of q / out of column c (c < ncols)
+  // (row, query head) row of q / out of column c (c < ncols)
   auto row_of = [&](const Cursor& x, int c) -> int64_t {
     if constexpr (GROUPED) return int64_t(x.s * a.group_size + c / G) * Hq + x.kvh * G + c % G;
+    else if constexpr (MR) return int64_t(a.q_start_loc[x.s] + c / G) * Hq + x.kvh * G + c % G;
     else return int64_t(x.s) * Hq + head_of(x) + c;
   };
   // Where tile j of a segment lies: the table row of its part (the sequence's
@@ -652,26 +662,49 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
   };
   // the segment's query loads and the block-table window of its tile x.j
   auto prefetch = [&](const Cursor& x) -> int {
-    // columns past the unit's heads multiply zeros (their load is clamped to a real head)
-    const unsigned char* qp = static_cast<const unsigned char*>(a.q) +
-                              row_of(x, min(i16, ncols - 1)) * ROW + 16 * g;
+    // columns past the unit's heads multiply zeros (their load is clamped to a
+    // real column); a multi-row sequence without rows loads nothing
+    const int nc = MR ? rows_of(x.s) * G : ncols;
+    if (!MR || nc > 0) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qnext[ks] = *reinterpret_cast<const uint4*>(qp + 64 * ks);
+      for (int ct = 0; ct < NCT; ++ct) {
+        const unsigned char* qp = static_cast<const unsigned char*>(a.q) +
+                                  row_of(x, min(ct * 16 + i16, nc - 1)) * ROW + 16 * g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qnext[ct][ks] = *reinterpret_cast<const uint4*>(qp + 64 * ks);
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qnext[ct][ks] = make_uint4(0, 0, 0, 0);
+    }
     const Part pt = part_of(x, x.j);
     const int nblk = (pt.L + Bm1) >> b_shift;
     const int jb0 = (pt.j * kTile) >> b_shift;
     return jb0 + lane < nblk ? pt.row[jb0 + lane] : 0;
   };
   auto begin_segment = [&](const Cursor& x) {
-    (void)x;
+    int nrows = 0;
+    if constexpr (MR) {
+      nrows = rows_of(x.s);
+      ncols = nrows * G;
+    }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qop[ks] = i16 < ncols ? qnext[ks] : make_uint4(0, 0, 0, 0);
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = ct * 16 + i16;
 #pragma unroll
-    for (int p = 0; p < KVP; ++p)
+      for (int ks = 0; ks < KS; ++ks) qop[ct][ks] = c < ncols ? qnext[ct][ks] : make_uint4(0, 0, 0, 0);
+      // row c / G of the sequence sits at position L - nrows + c / G
+      if constexpr (MR) lim[ct] = c < ncols ? x.L - nrows + c / G + 1 : 0;
+      m[ct] = -INFINITY;
+      lpart[ct] = 0.f;
+    }
+#pragma unroll
+    for (int p = 0; p < KVP * NCT; ++p)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[p][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m = -INFINITY;
-    lpart = 0.f;
   };
 
   // colok: this lane's column scores the tile (false: its scores are -inf)
@@ -696,6 +729,67 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
         *reinterpret_cast<uint4*>(vd + wr[u]) = vr[ut];
       }
     }
+    if constexpr (MR) {
+      // multi-row: one K operand read serves both column tiles, one V^T read
+      // both products; each column is masked at its own row's position
+      f32x4_t sc[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) sc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 kop = *reinterpret_cast<const uint4*>(kt_lds + (kr0 ^ (64u * ks)));
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          sc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop),
+                                                          __builtin_bit_cast(bf16x8_t, qop[ct][ks]),
+                                                          sc[ct], 0, 0, 0);
+      }
+      const int key0 = j * kTile + 4 * g;
+      uint2 pb[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key0 + i >= lim[ct]) sc[ct][i] = -INFINITY;
+        float mx = fmaxf(fmaxf(sc[ct][0], sc[ct][1]), fmaxf(sc[ct][2], sc[ct][3]));
+        {  // max over the 4 lanes of column ct*16 + l%16
+          const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                            false, false);
+          mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+          const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                            false, false);
+          mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+        }
+        const bool moved = m[ct] == -INFINITY ? mx != -INFINITY : (mx - m[ct]) * c2 > 8.f;
+        const float mn = moved ? mx : m[ct];
+        const float nms = mn == -INFINITY ? 0.f : -mn * c2;
+        const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m[ct], c2, nms)) : 1.f;
+        m[ct] = mn;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[ct][i], c2, nms));
+        pb[ct] = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
+        const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+        float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb[ct].x), ones, 0.f,
+                                                   false);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb[ct].y), ones, ps, false);
+        lpart[ct] = lpart[ct] * alpha + ps;
+        if (__ballot(moved)) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)(vt + (rd0 ^ (32u * dt))));
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              va, __builtin_bit_cast(bf16x4_t, pb[ct]), o[ct][dt], 0, 0, 0);
+      }
+      return;
+    }
     f32x4_t scp[KVP];
 #pragma unroll
     for (int p = 0; p < KVP; ++p) {
@@ -704,7 +798,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
       for (int ks = 0; ks < KS; ++ks) {
         const uint4 kop = *reinterpret_cast<const uint4*>(kt_lds + p * TB + (kr0 ^ (64u * ks)));
         scp[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop),
-                                                        __builtin_bit_cast(bf16x8_t, qop[ks]),
+                                                        __builtin_bit_cast(bf16x8_t, qop[0][ks]),
                                                         scp[p], 0, 0, 0);
       }
     }
@@ -724,11 +818,11 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
                                                         false, false);
       mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
     }
-    const bool moved = m == -INFINITY ? mx != -INFINITY : (mx - m) * c2 > 8.f;
-    const float mn = moved ? mx : m;
+    const bool moved = m[0] == -INFINITY ? mx != -INFINITY : (mx - m[0]) * c2 > 8.f;
+    const float mn = moved ? mx : m[0];
     const float nms = mn == -INFINITY ? 0.f : -mn * c2;
-    const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m, c2, nms)) : 1.f;
-    m = mn;
+    const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m[0], c2, nms)) : 1.f;
+    m[0] = mn;
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, nms));
@@ -736,7 +830,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
     float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb.x), ones, 0.f, false);
     ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb.y), ones, ps, false);
-    lpart = lpart * alpha + ps;
+    lpart[0] = lpart[0] * alpha + ps;
     if (__ballot(moved)) {
 #pragma unroll
       for (int p = 0; p < KVP; ++p)
@@ -793,10 +887,13 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     constexpr int LPRW = ROW / 16;     // lanes per row
     constexpr int RPW = kWave / LPRW;  // rows per store instruction
     unsigned char* part = reinterpret_cast<unsigned char*>(a.ws_acc);  // bf16 partial rows
+    // multi-row units: output rows by the mask, all partial rows (the combine
+    // reads only the columns of the sequence's rows)
+    const int nc = MR ? HPW : ncols;
 #pragma unroll 1
     for (int it = 0; it < (HPW + RPW - 1) / RPW; ++it) {
       const int cc = it * RPW + lane / LPRW;
-      const bool use = cc < ncols && (kind == 2 || ((rows >> cc) & 1));
+      const bool use = cc < nc && (kind == 2 || ((rows >> cc) & 1));
       if (use) {
         const uint4 v = *reinterpret_cast<const uint4*>(rows_lds + cc * ROW + (lane % LPRW) * 16);
         unsigned char* dst = kind == 1 ? static_cast<unsigned char*>(a.out) + row_of(x, cc) * ROW
@@ -804,7 +901,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
         *reinterpret_cast<uint4*>(dst + (lane % LPRW) * 16) = v;
       }
     }
-    if (kind == 2 && g == 0 && i16 < ncols) a.ws_ml[int64_t(slot) * kMLStride + i16] = ml;
+    if (!MR && kind == 2 && g == 0 && i16 < ncols) a.ws_ml[int64_t(slot) * MLS + i16] = ml;
   };
   auto flush = [&]() {
     if (held > 0) write_held(kind0, s0, kvh0, hc0, rows0, slot0, hold, ml0);
@@ -813,48 +910,59 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
     held = 0;
   };
   auto end_segment = [&](const Cursor& x, bool owns_start, bool owns_end) {
-    float l = lpart + __shfl_xor(lpart, 16);
-    l += __shfl_xor(l, 32);
-    const bool col = i16 < ncols;
-    // this lane's column: with paired KV heads, column 1 is in the second set
-    f32x4_t oc[DT];
+    float l[NCT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oc[dt] = KVP == 2 && i16 >= CPH ? o[KVP - 1][dt] : o[0][dt];
+    for (int ct = 0; ct < NCT; ++ct) {
+      l[ct] = lpart[ct] + __shfl_xor(lpart[ct], 16);
+      l[ct] += __shfl_xor(l[ct], 32);
+    }
     if (held == kSlots) flush();
     const int h = kSlots == 1 ? 0 : held;
     ++held;
     unsigned char* rows_lds = hold + h * HPW * ROW;
-    int kind, slot = 0;
+    const bool whole = owns_start && owns_end;
+    const int kind = whole ? 1 : 2;
+    const int slot = whole ? 0 : 2 * w + (owns_start ? 1 : 0);
     uint64_t rows = 0;
-    float2 ml = make_float2(0.f, 0.f);
-    if (owns_start && owns_end) {
-      // a grouped member without tokens scored nothing: the walk wrote its zeros
-      const bool keep = col && (!GROUPED || l > 0.f);
-      if (a.lse && g == 0 && keep) a.lse[row_of(x, i16)] = m * c2 + __builtin_amdgcn_logf(l);
-      const float inv = vsc / l;
-      if (keep) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<uint2*>(rows_lds + i16 * ROW + (16 * dt + 4 * g) * 2) =
-              make_uint2(pack_bf16(oc[dt][0] * inv, oc[dt][1] * inv),
-                         pack_bf16(oc[dt][2] * inv, oc[dt][3] * inv));
-      }
-      kind = 1;
-      rows = __ballot(g == 0 && keep);
-    } else {
-      // partial sums of a split segment go to the combine as bf16 (the (max,
-      // denominator) record stays fp32); accumulation in the wave was fp32
-      if (col) {
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = ct * 16 + i16;
+      const bool col = c < ncols;
+      // this lane's column: with paired KV heads, column 1 is in the second set
+      f32x4_t oc[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<uint2*>(rows_lds + i16 * ROW + (16 * dt + 4 * g) * 2) =
-              make_uint2(pack_bf16(oc[dt][0] * vsc, oc[dt][1] * vsc),
-                         pack_bf16(oc[dt][2] * vsc, oc[dt][3] * vsc));
+      for (int dt = 0; dt < DT; ++dt)
+        oc[dt] = MR ? o[ct][dt] : (KVP == 2 && i16 >= CPH ? o[KVP - 1][dt] : o[0][dt]);
+      if (whole) {
+        // a grouped member without tokens scored nothing: the walk wrote its zeros
+        const bool keep = col && (!GROUPED || l[ct] > 0.f);
+        if (a.lse && g == 0 && keep) a.lse[row_of(x, c)] = m[ct] * c2 + __builtin_amdgcn_logf(l[ct]);
+        const float inv = vsc / l[ct];
+        if (keep) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<uint2*>(rows_lds + c * ROW + (16 * dt + 4 * g) * 2) =
+                make_uint2(pack_bf16(oc[dt][0] * inv, oc[dt][1] * inv),
+                           pack_bf16(oc[dt][2] * inv, oc[dt][3] * inv));
+        }
+        rows |= uint64_t(__ballot(g == 0 && keep)) << (16 * ct);
+      } else {
+        // partial sums of a split segment go to the combine as bf16 (the (max,
+        // denominator) record stays fp32); accumulation in the wave was fp32
+        if (col) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<uint2*>(rows_lds + c * ROW + (16 * dt + 4 * g) * 2) =
+                make_uint2(pack_bf16(oc[dt][0] * vsc, oc[dt][1] * vsc),
+                           pack_bf16(oc[dt][2] * vsc, oc[dt][3] * vsc));
+        }
+        // multi-row units write their (max, denominator) records now (two per
+        // lane); the others keep theirs with the held rows
+        if (MR && g == 0 && col)
+          a.ws_ml[int64_t(slot) * MLS + c] = make_float2(m[ct] * c2, l[ct]);
       }
-      kind = 2;
-      slot = 2 * w + (owns_start ? 1 : 0);
-      ml = make_float2(m * c2, l);
     }
+    const float2 ml = whole ? make_float2(0.f, 0.f) : make_float2(m[0] * c2, l[0]);
     if (kSlots == 1 || h == 0) {
       kind0 = kind; s0 = x.s; kvh0 = x.kvh; hc0 = x.hc; rows0 = rows; slot0 = slot; ml0 = ml;
     } else {
@@ -955,8 +1063,10 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_mfma_kernel(
 // (w, last] that continued it.
 // PART_BF16: the partial sums are bf16 rows (written by the matrix-core
 // kernel), else fp32 rows.
-template <int DTYPE, int D, int HPW, bool GROUPED, bool PART_BF16>
+// MR: multi-row units (columns = (row, query head) pairs of the sequence's rows).
+template <int DTYPE, int D, int HPW, bool GROUPED, bool PART_BF16, bool MR = false>
 __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int MLS = HPW > kMLStride ? HPW : kMLStride;
   using RS = RowShape<DTYPE, D>;
   constexpr int VEC = RS::VEC, LPR = RS::LPR;
   const int lane = threadIdx.x % kWave;
@@ -991,7 +1101,7 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kern
 #pragma unroll
       for (int k = 0; k < HPL; ++k) {
         const int hh = min(lane / LPR + k * GROUPS, HPW - 1);
-        ml[q][k] = a.ws_ml[int64_t(sl) * kMLStride + hh];
+        ml[q][k] = a.ws_ml[int64_t(sl) * MLS + hh];
         if constexpr (PART_BF16) {
           static_assert(VEC == 8, "bf16 partials: one 16-byte load per lane");
           const uint4 b = *reinterpret_cast<const uint4*>(
@@ -1030,7 +1140,8 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kern
     }
   }
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int ncols = GROUPED ? a.group_size * G : HPW;
+  const int ncols = GROUPED ? a.group_size * G
+                             : MR ? (a.q_start_loc[seg.x + 1] - a.q_start_loc[seg.x]) * G : HPW;
 #pragma unroll
   for (int k = 0; k < HPL; ++k) {
     const int hh = lane / LPR + k * GROUPS;
@@ -1039,6 +1150,8 @@ __global__ __launch_bounds__(kWave * kMaxWavesPerGroup) void decode_combine_kern
     if (GROUPED && !(den[k] > 0.f)) continue;
     const float inv = 1.f / den[k];
     const int64_t row = GROUPED ? int64_t(seg.x * a.group_size + hh / G) * a.num_q_heads +
+                                      head0 + hh % G
+                        : MR    ? int64_t(a.q_start_loc[seg.x] + hh / G) * a.num_q_heads +
                                       head0 + hh % G
                                 : int64_t(seg.x) * a.num_q_heads + head0 + hh;
     if (a.lse && c == 0) a.lse[row] = M[k] + __builtin_amdgcn_logf(den[k]);
@@ -1128,6 +1241,31 @@ hipError_t run_grouped(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Multi-row decode (bf16 pools): units of (sequence, KV head) with up to
+// kMultiRowCols (row, query head) columns, one wave per SIMD.
+template <int D>
+hipError_t run_multirow(const DecodeArgs& a, hipStream_t st) {
+  int b_shift = 0;
+  while ((1 << b_shift) < a.block_size) ++b_shift;
+  const int cus = a.num_cus > 0 ? a.num_cus : 1;
+  int wpg = (a.workers + cus - 1) / cus;
+  wpg = wpg < 1 ? 1 : (wpg > kMultiRowWaves ? kMultiRowWaves : wpg);
+  const int groups = (a.workers + wpg - 1) / wpg;
+  const float scale_log2 = a.scale * kLog2e;
+  constexpr int H = kMultiRowCols;
+  const size_t lds = size_t(wpg) * mfma_wave_lds<D, H, 1>();
+  if (a.block_size >= kTile)
+    decode_mfma_kernel<D, H, true, PA_BF16, 1, false, true>
+        <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
+  else
+    decode_mfma_kernel<D, H, false, PA_BF16, 1, false, true>
+        <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_combine_kernel<PA_BF16, D, H, false, true, true><<<groups, kWave * wpg, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 template <int DTYPE, int D>
 hipError_t run_d(const DecodeArgs& a, hipStream_t st) {
   switch (decode_heads_per_unit(a.num_q_heads / a.num_kv_heads)) {
@@ -1156,6 +1294,12 @@ bool decode_supported(int dtype, int head_dim, int group) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  if (a.q_start_loc) {
+    if (a.dtype != PA_BF16 || a.prefix_lens || a.len_offset) return hipErrorInvalidValue;
+    if (a.head_dim == 128) return run_multirow<128>(a, st);
+    if (a.head_dim == 64) return run_multirow<64>(a, st);
+    return hipErrorInvalidValue;
+  }
   if (a.prefix_lens) {
     if (a.group_size < 1 || a.group_size * (a.num_q_heads / a.num_kv_heads) > kGroupedCols)
       return hipErrorInvalidValue;

@@ -116,7 +116,15 @@ struct DecodeArgs {
   // member's own tokens for its columns only.
   const int32_t* prefix_lens;
   int32_t group_size, num_groups;
+  // Several query rows per sequence (set q_start_loc, int32 [num_seqs + 1]):
+  // sequence s has rows q_start_loc[s] .. q_start_loc[s+1]-1 of q and out,
+  // row r at position seq_lens[s] - rows + r, attending causally to keys
+  // 0 .. that position. Each (sequence, KV head) is one unit whose columns
+  // are (row r, query head h) = r * G + h, at most kMultiRowCols of them.
+  const int32_t* q_start_loc;
 };
+constexpr int kMultiRowCols = 32;
+constexpr int kMultiRowWaves = 4;  // multi-row decode: waves per CU (one per SIMD)
 
 hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void* v_new,
                               const int64_t* slots, int32_t T, hipStream_t stream);

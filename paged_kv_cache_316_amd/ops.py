@@ -234,6 +234,14 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, h
                                                workers))
 
 
+def attention_mixed_workspace_bytes(num_decode: int, num_prefill: int, num_q_heads: int,
+                                    num_kv_heads: int, head_dim: int, max_q_len: int,
+                                    workers: int = 0) -> int:
+    return int(lib().pa_attention_mixed_workspace_bytes(num_decode, num_prefill, num_q_heads,
+                                                        num_kv_heads, head_dim, max_q_len,
+                                                        workers))
+
+
 class DecodePlan:
     """Output and workspace for repeated decode calls of one shape."""
 
@@ -393,8 +401,9 @@ def attention_mixed(q: torch.Tensor, q_start_loc: torch.Tensor, seq_lens: torch.
         out = torch.empty_like(q)
     _need(out, "out", pool.io_dtype)
     if workspace is None:
-        n = decode_workspace_bytes(max(num_decode, 1), q.shape[1], pool.num_kv_heads,
-                                   pool.head_dim, workers)
+        n = attention_mixed_workspace_bytes(int(num_decode), S - int(num_decode), q.shape[1],
+                                            pool.num_kv_heads, pool.head_dim, int(max_q_len),
+                                            workers)
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
     if _CHECK_INPUTS:
         check_batch(pool, block_tables, seq_lens)

@@ -96,6 +96,29 @@ def test_workspace_formula():
     assert L.pa_decode_workspace_bytes(4, 6, 4, 128, 10) == 0  # 6 not a multiple of 4
 
 
+def test_mixed_workspace_formula():
+    L = lib()
+    # short chunks (4 rows x 8 query heads per KV head = 32 columns): the
+    # multi-row decode, 2 slots per worker of 32 columns, each D bf16 values and
+    # an 8-byte (m, l) record, plus 100 split records
+    assert (L.pa_attention_mixed_workspace_bytes(0, 256, 64, 8, 128, 4, 100)
+            == 2 * 100 * 32 * 128 * 2 + 2 * 100 * 32 * 8 + 100 * 16)
+    assert (L.pa_attention_mixed_workspace_bytes(3, 5, 16, 16, 64, 32, 7)
+            == 2 * 7 * 32 * 64 * 2 + 2 * 7 * 32 * 8 + 7 * 16)
+    # decode rows only: the decode's workspace
+    assert (L.pa_attention_mixed_workspace_bytes(64, 0, 64, 8, 128, 0, 10)
+            == L.pa_decode_workspace_bytes(64, 64, 8, 128, 10))
+    # 5 rows x 8 heads do not fit 32 columns: chunks go to the prefill kernel,
+    # which needs no workspace; with no decode rows only the 16-byte minimum
+    assert L.pa_attention_mixed_workspace_bytes(0, 8, 64, 8, 128, 5, 10) == 16
+    assert (L.pa_attention_mixed_workspace_bytes(4, 8, 64, 8, 128, 512, 10)
+            == L.pa_decode_workspace_bytes(4, 64, 8, 128, 10))
+    # invalid sizes
+    assert L.pa_attention_mixed_workspace_bytes(0, 8, 6, 4, 128, 4, 10) == 0
+    assert L.pa_attention_mixed_workspace_bytes(-1, 8, 64, 8, 128, 4, 10) == 0
+    assert L.pa_attention_mixed_workspace_bytes(0, 8, 64, 8, 128, -1, 10) == 0
+
+
 def test_prefill_argument_checks():
     L = lib()
     p = _pool(dtype=0)
