@@ -565,7 +565,8 @@ def spec_verify_row(ld, steps, warmup, workers, k=4):
             "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                          "kernel": "pa_attention_mixed, multi-row decode (k x G = 32 columns "
-                                   "per (sequence, KV head))"}}
+                                   "per (sequence, KV head) on a pair of waves sharing each "
+                                   "K/V tile in LDS) + combine"}}
 
 
 HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction

@@ -361,9 +361,11 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,
  *                  for each sequence, its rows of this call included
  *   block_tables : device, int32 [num_decode + num_prefill][max_blocks_per_seq]
  *   max_q_len    : host, >= every prefill chunk's row count
- *   num_workers  : decode wavefronts; 0 = default (3 per compute unit when the
- *                  batch also has chunks, 4 on the multi-row path below, else
- *                  pa_decode's default)
+ *   num_workers  : decode work slices, one wavefront each (on the multi-row
+ *                  path below with more than 16 columns per unit, a
+ *                  workgroup of two wavefronts); 0 = default (3 wavefronts per
+ *                  compute unit when the batch also has chunks, 8 on the
+ *                  multi-row path, else pa_decode's default)
  *   workspace    : device, pa_attention_mixed_workspace_bytes(num_decode,
  *                  num_prefill, num_q_heads, num_kv_heads, head_dim, max_q_len,
  *                  num_workers) bytes, 16-byte aligned (unused when the batch
@@ -374,7 +376,9 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,
  * engine deep dive" section 5.2) take the multi-row
  * decode: every sequence, decode rows included, is one unit per KV head whose
  * MFMA columns are its (row, query head) pairs, each masked at its own row's
- * position, so each K/V row is read once for all of a sequence's rows.
+ * position, so each K/V row is read once for all of a sequence's rows (units
+ * of more than 16 columns: two wavefronts of one workgroup, 16 columns each,
+ * that share every K/V tile through LDS).
  * Otherwise, with both kinds of rows, the chunks run on a second stream of the
  * library's (one per host thread and device, default priority) that forks
  * from and joins back into `stream`, so that the two kernels share the chip.

@@ -72,11 +72,13 @@ DecodeLayout grouped_layout(int32_t head_dim, int32_t workers) {
   return d;
 }
 
-// Multi-row decode: slots of kMultiRowCols bf16 partial rows, records of as
-// many (max, denominator) pairs; one wave per SIMD by default.
-DecodeLayout multirow_layout(int32_t head_dim, int32_t workers) {
+// Multi-row decode: per work slice, slots of kMultiRowCols bf16 partial rows
+// and records of as many (max, denominator) pairs. A slice is one wave, or a
+// pair of waves when units have more than 16 columns; 8 waves per compute
+// unit by default.
+DecodeLayout multirow_layout(int32_t head_dim, int32_t workers, bool pair) {
   DecodeLayout d{};
-  d.workers = workers > 0 ? workers : device_cus() * kMultiRowWaves;
+  d.workers = workers > 0 ? workers : device_cus() * kMultiRowWaves / (pair ? 2 : 1);
   d.heads_per_unit = kMultiRowCols;
   const size_t slots = size_t(2) * d.workers * d.heads_per_unit;
   d.acc_bytes = slots * head_dim * 2;
@@ -84,6 +86,9 @@ DecodeLayout multirow_layout(int32_t head_dim, int32_t workers) {
   d.seg_bytes = size_t(d.workers) * 16;
   return d;
 }
+
+// Units of more than 16 columns run on a pair of waves (16 columns each).
+bool multirow_pair(int32_t G, int32_t max_q_len) { return int64_t(max_q_len) * G > 16; }
 
 // A mixed batch runs as one multi-row decode when its chunks are short: a
 // bf16 pool and every sequence's rows x query heads per KV head within the
@@ -223,6 +228,7 @@ DecodeArgs decode_args(void* out, const void* q, const pa_pool* pool, const int3
   a.group_size = 1;
   a.num_groups = num_seqs;
   a.q_start_loc = nullptr;
+  a.mr_pair = 0;
   return a;
 }
 
@@ -407,7 +413,8 @@ size_t pa_attention_mixed_workspace_bytes(int32_t num_decode, int32_t num_prefil
   const int32_t G = num_q_heads / num_kv_heads;
   size_t need = 16;
   if (pa::multirow_fits(PA_BF16, head_dim, G, num_prefill, max_q_len))
-    return std::max(need, pa::multirow_layout(head_dim, num_workers).total());
+    return std::max(need, pa::multirow_layout(head_dim, num_workers,
+                                              pa::multirow_pair(G, max_q_len)).total());
   if (num_decode > 0) {
     const bool both = num_prefill > 0 && max_q_len > 0;
     const int32_t workers =
@@ -611,7 +618,8 @@ pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_lo
   if (pa::multirow_fits(pool->dtype, pool->head_dim, G, num_prefill, max_q_len)) {
     // short chunks (speculative verification, small prompt pieces): decode
     // rows and chunk rows in one multi-row decode over all the sequences
-    const pa::DecodeLayout lay = pa::multirow_layout(pool->head_dim, num_workers);
+    const bool pair = pa::multirow_pair(G, max_q_len);
+    const pa::DecodeLayout lay = pa::multirow_layout(pool->head_dim, num_workers, pair);
     if (!workspace || workspace_bytes < lay.total())
       return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed "
                   "(pa_attention_mixed_workspace_bytes)", who,
@@ -624,6 +632,7 @@ pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_lo
                                        num_decode + num_prefill, num_q_heads, scale, lay,
                                        workspace);
     a.q_start_loc = q_start_loc;
+    a.mr_pair = pair ? 1 : 0;
     return pa::hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream)), who);
   }
   const bool both = chunks && num_decode > 0;

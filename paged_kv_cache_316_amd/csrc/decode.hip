@@ -149,7 +149,8 @@ struct Cursor {
 // tile and returns that window, then begin(cursor), run(cursor, j0, j1, window)
 // for the slice's tiles [j0, j1) of it, and end(cursor, owns_start, owns_end),
 // which stores the result; finally it records the segment the slice starts and
-// leaves open (if any) for the combine kernel. Also writes zeros for empty
+// leaves open (if any) for the combine kernel (when `record`: of two waves
+// walking one slice, only one records it). Also writes zeros for empty
 // sequences. VEC: elements of the output dtype per 16 bytes; hpw: query heads
 // per unit.
 // Order at a segment boundary: the next segment's prefetch comes before the
@@ -178,7 +179,7 @@ __device__ __forceinline__ int group_tiles(const DecodeArgs& a, int g) {
 template <int D, int VEC, bool GROUPED, class Prefetch, class Begin, class Run, class End>
 __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane, int n_hchunk,
                                            int hpw, int kvp, Prefetch prefetch, Begin begin,
-                                           Run run, End end) {
+                                           Run run, End end, bool record = true) {
   const int S = GROUPED ? a.num_groups : a.num_seqs;
   const int Hq = a.num_q_heads;
   const int G = Hq / a.num_kv_heads;
@@ -205,7 +206,7 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
       for (int h = lane; h < Hq; h += kWave) a.lse[int64_t(s) * Hq + h] = -INFINITY;
   }
   if (w >= W) {
-    if (lane == 0) a.ws_seg[w] = make_int4(-1, 0, 0, 0);
+    if (lane == 0 && record) a.ws_seg[w] = make_int4(-1, 0, 0, 0);
     return;
   }
   const int64_t g_begin = total * w / W, g_end = total * (w + 1) / W;
@@ -290,7 +291,7 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
     if (!more) break;
     begin(cur);
   }
-  if (lane == 0) a.ws_seg[w] = split;
+  if (lane == 0 && record) a.ws_seg[w] = split;
 }
 
 template <int DTYPE, int D, int HPW, bool BIG_B>
@@ -554,16 +555,26 @@ constexpr size_t mfma_wave_lds() {
   return size_t(KVP) * 2 * kTile * 2 * D + (HPW >= 4 ? size_t(2) * HPW * 2 * D : 0);
 }
 
-template <int D, int HPW, bool BIG_B, int KV, int KVP, bool GROUPED, bool MR = false>
+// LDS of a pair of multi-row waves (one workgroup): two stages of a K and a V
+// tile that both waves read, then each wave's two hold slots of 16 rows.
+template <int D>
+constexpr size_t mr_pair_lds() {
+  return size_t(2) * 2 * kTile * 2 * D + size_t(2) * 2 * 16 * 2 * D;
+}
+constexpr int kMRPairTiles = 2;  // tiles in flight per wave of a pair
+
+template <int D, int HPW, bool BIG_B, int KV, int KVP, bool GROUPED, bool MR = false,
+          bool PAIR = false>
 __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) void decode_mfma_kernel(
     DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
+  static_assert(!PAIR || MR, "pairs of waves are a multi-row launch");
   static_assert(!GROUPED || (KVP == 1 && HPW == kGroupedCols), "grouped units: 16 columns");
-  static_assert(!MR || (KVP == 1 && !GROUPED && HPW == kMultiRowCols), "multi-row units: 32 columns");
+  static_assert(!MR || (KVP == 1 && !GROUPED && HPW == 16), "multi-row waves: 16 columns");
   constexpr bool FP8 = KV == PA_FP8_E4M3;
-  // MFMA column tiles of 16: multi-row units (MR) have two; a lane holds
-  // column ct * 16 + lane % 16 of tile ct
-  constexpr int NCT = MR ? 2 : 1;
-  constexpr int MLS = HPW > kMLStride ? HPW : kMLStride;  // (m, l) records per workspace slot
+  // columns of a workspace slot: a multi-row unit's (up to 32, split over a
+  // pair of waves), else the wave's own
+  constexpr int UC = MR ? kMultiRowCols : HPW;
+  constexpr int MLS = UC > kMLStride ? UC : kMLStride;  // (m, l) records per workspace slot
   constexpr int ROW = 2 * D;        // bytes per bf16 K/V row in LDS
   constexpr int GROW = FP8 ? D : ROW;  // bytes per row in the pool
   constexpr int KS = D / 32;        // 16x16x32 k-steps over head_dim
@@ -577,10 +588,15 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
   constexpr int CPH = HPW / KVP;    // MFMA columns (query heads) per KV head of the unit
   constexpr int RPL = 256 / ROW;    // rows per 256-byte LDS bank line
   constexpr int TB = kTile * ROW;   // bytes of one K or V tile in LDS
+  // PAIR: the two waves of a workgroup share each K/V tile, each loading half
+  // of its rows (NL loads per tensor) into a stage both read
+  constexpr int NL = PAIR ? NI / 2 : NI;
+  constexpr int NLT = PAIR ? NL : NIT;
   // tiles in flight per wave: an FP8 tile is half the bytes, so more of them
-  // are needed to keep as many bytes in flight (a paired tile is twice the bytes)
-  constexpr int NB = FP8 && KVP == 1 ? 4 : 2;
-  static_assert(HPW <= 16 * NCT, "the MFMA N tiles hold the unit's columns");
+  // are needed to keep as many bytes in flight (a paired tile is twice the
+  // bytes; a wave of a pair loads half a tile)
+  constexpr int NB = PAIR ? kMRPairTiles : FP8 && KVP == 1 ? 4 : 2;
+  static_assert(HPW <= 16, "one MFMA N tile holds the wave's columns");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int lane = threadIdx.x % kWave;
@@ -590,11 +606,20 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
   const int G = Hq / Hkv;
   const int g = lane / 16, i16 = lane % 16;
   const int B = a.block_size, Bm1 = B - 1;
-  if (w >= a.workers) return;
+  // Multi-row pairs: the two waves of workgroup k walk work slice k; wave ct
+  // holds unit columns [16 ct, 16 ct + 16) of its units and loads rows
+  // [ct * NL * RPI, (ct + 1) * NL * RPI) of each tile.
+  const int ct = PAIR ? wig : 0;
+  const int wk = PAIR ? int(blockIdx.x) : w;  // this wave's work slice
+  const int cb = 16 * ct;                     // unit column of the wave's column 0
+  const int row0 = ct * NL * RPI;
+  if (wk >= a.workers) return;  // (both waves of a pair)
 
   // this wave's K tiles (one per KV head of the unit), then its V tiles
-  unsigned char* kt_lds = smem + wig * mfma_wave_lds<D, HPW, KVP>();
+  // (pairs: the workgroup's two stages, taken in turn)
+  unsigned char* kt_lds = PAIR ? smem : smem + wig * mfma_wave_lds<D, HPW, KVP>();
   unsigned char* vt = kt_lds + KVP * TB;
+  int tcount = 0;  // pairs: tiles computed so far (the same in both waves)
   auto swz = [](int r) { return (r / RPL) % CPR; };
   // load u of lane l: row u*RPI + l/GCPR, pool chunk l%GCPR; in LDS that is
   // chunk l%GCPR of the bf16 row (two chunks, 2c and 2c+1, for FP8 codes)
@@ -602,7 +627,7 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
   uint32_t wr[NI], wr2[NI];
 #pragma unroll
   for (int u = 0; u < NI; ++u) {
-    const int r = u * RPI + lrow;
+    const int r = row0 + u * RPI + lrow;
     const int c0 = FP8 ? 2 * lch : lch;
     wr[u] = uint32_t(r * ROW + ((c0 ^ swz(r)) * 16));
     wr2[u] = uint32_t(r * ROW + (((c0 + 1) ^ swz(r)) * 16));
@@ -617,10 +642,10 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
   const unsigned char* vp = static_cast<const unsigned char*>(a.v_pool);
   const int64_t block_bytes = int64_t(Hkv) * B * GROW;
 
-  uint4 qop[NCT][KS], qnext[NCT][KS];
-  f32x4_t o[KVP * NCT][DT];
-  float m[NCT], lpart[NCT];
-  int lim[NCT];  // multi-row: keys a column attends (its row's position + 1; 0 if unused)
+  uint4 qop[KS], qnext[KS];
+  f32x4_t o[KVP][DT];
+  float m, lpart;
+  int lim = 0;  // multi-row: keys this lane's column attends (its row's position + 1)
   const float c2 = FP8 ? scale_log2 * a.k_scale : scale_log2;
   const float vsc = FP8 ? a.v_scale : 1.f;
   // columns in use (multi-row: of the current segment, rows of its sequence x G)
@@ -663,22 +688,13 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
   // the segment's query loads and the block-table window of its tile x.j
   auto prefetch = [&](const Cursor& x) -> int {
     // columns past the unit's heads multiply zeros (their load is clamped to a
-    // real column); a multi-row sequence without rows loads nothing
+    // real column); a multi-row wave with no column in the unit loads nothing
     const int nc = MR ? rows_of(x.s) * G : ncols;
-    if (!MR || nc > 0) {
+    if (!MR || cb < nc) {
+      const unsigned char* qp = static_cast<const unsigned char*>(a.q) +
+                                row_of(x, min(cb + i16, nc - 1)) * ROW + 16 * g;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const unsigned char* qp = static_cast<const unsigned char*>(a.q) +
-                                  row_of(x, min(ct * 16 + i16, nc - 1)) * ROW + 16 * g;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          qnext[ct][ks] = *reinterpret_cast<const uint4*>(qp + 64 * ks);
-      }
-    } else {
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qnext[ct][ks] = make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) qnext[ks] = *reinterpret_cast<const uint4*>(qp + 64 * ks);
     }
     const Part pt = part_of(x, x.j);
     const int nblk = (pt.L + Bm1) >> b_shift;
@@ -686,36 +702,41 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
     return jb0 + lane < nblk ? pt.row[jb0 + lane] : 0;
   };
   auto begin_segment = [&](const Cursor& x) {
-    int nrows = 0;
+    const int c = cb + i16;  // this lane's unit column
     if constexpr (MR) {
-      nrows = rows_of(x.s);
+      const int nrows = rows_of(x.s);
       ncols = nrows * G;
-    }
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int c = ct * 16 + i16;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qop[ct][ks] = c < ncols ? qnext[ct][ks] : make_uint4(0, 0, 0, 0);
       // row c / G of the sequence sits at position L - nrows + c / G
-      if constexpr (MR) lim[ct] = c < ncols ? x.L - nrows + c / G + 1 : 0;
-      m[ct] = -INFINITY;
-      lpart[ct] = 0.f;
+      lim = c < ncols ? x.L - nrows + c / G + 1 : 0;
     }
 #pragma unroll
-    for (int p = 0; p < KVP * NCT; ++p)
+    for (int ks = 0; ks < KS; ++ks) qop[ks] = c < ncols ? qnext[ks] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int p = 0; p < KVP; ++p)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[p][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    lpart = 0.f;
   };
 
   // colok: this lane's column scores the tile (false: its scores are -inf)
   auto compute = [&](int j, int L, const uint4* kr, const uint4* vr, bool colok) {
+    unsigned char* ktile = kt_lds;
+    unsigned char* vtile = vt;
+    if constexpr (PAIR) {
+      // stage tcount % 2: both waves read the other stage last, and each
+      // passed the last barrier after its reads of this one completed
+      ktile = smem + (tcount & 1) * 2 * TB;
+      vtile = ktile + TB;
+      ++tcount;
+    }
     // tiles -> LDS (the previous tile's reads were issued earlier by this
     // wave, and LDS serves one wave's accesses in order)
 #pragma unroll
-    for (int ut = 0; ut < NIT; ++ut) {
+    for (int ut = 0; ut < NLT; ++ut) {
       const int u = ut % NI;
-      unsigned char* kd = kt_lds + (ut / NI) * TB;  // tile of KV head ut / NI
-      unsigned char* vd = vt + (ut / NI) * TB;
+      unsigned char* kd = ktile + (ut / NI) * TB;  // tile of KV head ut / NI
+      unsigned char* vd = vtile + (ut / NI) * TB;
       if constexpr (FP8) {
         uint4 k0, k1, v0, v1;
         widen_e4m3(kr[ut], k0, k1);
@@ -729,66 +750,14 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
         *reinterpret_cast<uint4*>(vd + wr[u]) = vr[ut];
       }
     }
-    if constexpr (MR) {
-      // multi-row: one K operand read serves both column tiles, one V^T read
-      // both products; each column is masked at its own row's position
-      f32x4_t sc[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) sc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kop = *reinterpret_cast<const uint4*>(kt_lds + (kr0 ^ (64u * ks)));
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          sc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop),
-                                                          __builtin_bit_cast(bf16x8_t, qop[ct][ks]),
-                                                          sc[ct], 0, 0, 0);
-      }
-      const int key0 = j * kTile + 4 * g;
-      uint2 pb[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (key0 + i >= lim[ct]) sc[ct][i] = -INFINITY;
-        float mx = fmaxf(fmaxf(sc[ct][0], sc[ct][1]), fmaxf(sc[ct][2], sc[ct][3]));
-        {  // max over the 4 lanes of column ct*16 + l%16
-          const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                            false, false);
-          mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-          const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                            false, false);
-          mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-        }
-        const bool moved = m[ct] == -INFINITY ? mx != -INFINITY : (mx - m[ct]) * c2 > 8.f;
-        const float mn = moved ? mx : m[ct];
-        const float nms = mn == -INFINITY ? 0.f : -mn * c2;
-        const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m[ct], c2, nms)) : 1.f;
-        m[ct] = mn;
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[ct][i], c2, nms));
-        pb[ct] = make_uint2(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]));
-        const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
-        float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb[ct].x), ones, 0.f,
-                                                   false);
-        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb[ct].y), ones, ps, false);
-        lpart[ct] = lpart[ct] * alpha + ps;
-        if (__ballot(moved)) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)(vt + (rd0 ^ (32u * dt))));
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              va, __builtin_bit_cast(bf16x4_t, pb[ct]), o[ct][dt], 0, 0, 0);
-      }
-      return;
+    if constexpr (PAIR) {
+      // the other half of the tile is the partner's: meet once both halves
+      // are written (LDS writes done; the K/V loads in flight stay so). The
+      // empty asm statements keep LDS accesses on their side of the barrier.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
     f32x4_t scp[KVP];
 #pragma unroll
@@ -796,19 +765,21 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
       scp[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kop = *reinterpret_cast<const uint4*>(kt_lds + p * TB + (kr0 ^ (64u * ks)));
+        const uint4 kop = *reinterpret_cast<const uint4*>(ktile + p * TB + (kr0 ^ (64u * ks)));
         scp[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop),
-                                                        __builtin_bit_cast(bf16x8_t, qop[0][ks]),
+                                                        __builtin_bit_cast(bf16x8_t, qop[ks]),
                                                         scp[p], 0, 0, 0);
       }
     }
     // column i16 is scored against the K tile of its own KV head
     f32x4_t sc = scp[0];
     if constexpr (KVP == 2) sc = i16 >= CPH ? scp[1] : scp[0];
+    // keys past the end, and (multi-row) past this lane's row, score -inf
     const int key0 = j * kTile + 4 * g;
+    const int Lc = MR ? lim : L;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (key0 + i >= L || !colok) sc[i] = -INFINITY;
+      if (key0 + i >= Lc || !colok) sc[i] = -INFINITY;
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     {  // max over lanes l, l^16, l^32, l^48 (the 4 lanes of head l%16), on the VALU
       const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
@@ -818,11 +789,11 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
                                                         false, false);
       mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
     }
-    const bool moved = m[0] == -INFINITY ? mx != -INFINITY : (mx - m[0]) * c2 > 8.f;
-    const float mn = moved ? mx : m[0];
+    const bool moved = m == -INFINITY ? mx != -INFINITY : (mx - m) * c2 > 8.f;
+    const float mn = moved ? mx : m;
     const float nms = mn == -INFINITY ? 0.f : -mn * c2;
-    const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m[0], c2, nms)) : 1.f;
-    m[0] = mn;
+    const float alpha = moved ? __builtin_amdgcn_exp2f(fmaf(m, c2, nms)) : 1.f;
+    m = mn;
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, nms));
@@ -830,7 +801,7 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
     const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
     float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb.x), ones, 0.f, false);
     ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb.y), ones, ps, false);
-    lpart[0] = lpart[0] * alpha + ps;
+    lpart = lpart * alpha + ps;
     if (__ballot(moved)) {
 #pragma unroll
       for (int p = 0; p < KVP; ++p)
@@ -843,7 +814,7 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const v4i16_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)(vt + p * TB + (rd0 ^ (32u * dt))));
+            (lds_v4i16_t*)(vtile + p * TB + (rd0 ^ (32u * dt))));
         o[p][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(bf16x4_t, pb),
                                                            o[p][dt], 0, 0, 0);
       }
@@ -869,7 +840,10 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
   constexpr bool kHoldToEnd = HPW >= 4;
   constexpr int kSlots = kHoldToEnd ? 2 : 1;
   static_assert(kHoldToEnd || HPW * ROW <= KVP * TB, "staged rows must fit the K tile");
-  unsigned char* hold = kHoldToEnd ? kt_lds + 2 * KVP * TB : kt_lds;  // kSlots x HPW rows
+  // kSlots x HPW rows (pairs: after the two shared stages, one set per wave)
+  unsigned char* hold = PAIR         ? smem + 4 * TB + ct * kSlots * HPW * ROW
+                        : kHoldToEnd ? kt_lds + 2 * KVP * TB
+                                     : kt_lds;
   // What each hold slot holds (wave-uniform, plain registers): kind 1 = output
   // rows (bit c of rows: column c's row is written), 2 = partial rows for the
   // workspace slot `slot`; s, kvh, hc: the segment.
@@ -887,8 +861,9 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
     constexpr int LPRW = ROW / 16;     // lanes per row
     constexpr int RPW = kWave / LPRW;  // rows per store instruction
     unsigned char* part = reinterpret_cast<unsigned char*>(a.ws_acc);  // bf16 partial rows
-    // multi-row units: output rows by the mask, all partial rows (the combine
-    // reads only the columns of the sequence's rows)
+    // multi-row waves: output rows by the mask, all partial rows (the combine
+    // reads only the columns of the sequence's rows); held row cc is the
+    // wave's column cc, unit column cb + cc
     const int nc = MR ? HPW : ncols;
 #pragma unroll 1
     for (int it = 0; it < (HPW + RPW - 1) / RPW; ++it) {
@@ -896,8 +871,9 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
       const bool use = cc < nc && (kind == 2 || ((rows >> cc) & 1));
       if (use) {
         const uint4 v = *reinterpret_cast<const uint4*>(rows_lds + cc * ROW + (lane % LPRW) * 16);
-        unsigned char* dst = kind == 1 ? static_cast<unsigned char*>(a.out) + row_of(x, cc) * ROW
-                                       : part + (int64_t(slot) * HPW + cc) * ROW;
+        unsigned char* dst = kind == 1
+                                 ? static_cast<unsigned char*>(a.out) + row_of(x, cb + cc) * ROW
+                                 : part + (int64_t(slot) * UC + cb + cc) * ROW;
         *reinterpret_cast<uint4*>(dst + (lane % LPRW) * 16) = v;
       }
     }
@@ -910,59 +886,53 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
     held = 0;
   };
   auto end_segment = [&](const Cursor& x, bool owns_start, bool owns_end) {
-    float l[NCT];
+    float l = lpart + __shfl_xor(lpart, 16);
+    l += __shfl_xor(l, 32);
+    const int c = cb + i16;  // this lane's unit column
+    const bool col = c < ncols;
+    // this lane's column: with paired KV heads, column 1 is in the second set
+    f32x4_t oc[DT];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      l[ct] = lpart[ct] + __shfl_xor(lpart[ct], 16);
-      l[ct] += __shfl_xor(l[ct], 32);
-    }
+    for (int dt = 0; dt < DT; ++dt) oc[dt] = KVP == 2 && i16 >= CPH ? o[KVP - 1][dt] : o[0][dt];
     if (held == kSlots) flush();
     const int h = kSlots == 1 ? 0 : held;
     ++held;
     unsigned char* rows_lds = hold + h * HPW * ROW;
-    const bool whole = owns_start && owns_end;
-    const int kind = whole ? 1 : 2;
-    const int slot = whole ? 0 : 2 * w + (owns_start ? 1 : 0);
+    int kind, slot = 0;
     uint64_t rows = 0;
+    float2 ml = make_float2(0.f, 0.f);
+    if (owns_start && owns_end) {
+      // a grouped member without tokens scored nothing: the walk wrote its zeros
+      const bool keep = col && (!GROUPED || l > 0.f);
+      if (a.lse && g == 0 && keep) a.lse[row_of(x, c)] = m * c2 + __builtin_amdgcn_logf(l);
+      const float inv = vsc / l;
+      if (keep) {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int c = ct * 16 + i16;
-      const bool col = c < ncols;
-      // this lane's column: with paired KV heads, column 1 is in the second set
-      f32x4_t oc[DT];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        oc[dt] = MR ? o[ct][dt] : (KVP == 2 && i16 >= CPH ? o[KVP - 1][dt] : o[0][dt]);
-      if (whole) {
-        // a grouped member without tokens scored nothing: the walk wrote its zeros
-        const bool keep = col && (!GROUPED || l[ct] > 0.f);
-        if (a.lse && g == 0 && keep) a.lse[row_of(x, c)] = m[ct] * c2 + __builtin_amdgcn_logf(l[ct]);
-        const float inv = vsc / l[ct];
-        if (keep) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            *reinterpret_cast<uint2*>(rows_lds + c * ROW + (16 * dt + 4 * g) * 2) =
-                make_uint2(pack_bf16(oc[dt][0] * inv, oc[dt][1] * inv),
-                           pack_bf16(oc[dt][2] * inv, oc[dt][3] * inv));
-        }
-        rows |= uint64_t(__ballot(g == 0 && keep)) << (16 * ct);
-      } else {
-        // partial sums of a split segment go to the combine as bf16 (the (max,
-        // denominator) record stays fp32); accumulation in the wave was fp32
-        if (col) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            *reinterpret_cast<uint2*>(rows_lds + c * ROW + (16 * dt + 4 * g) * 2) =
-                make_uint2(pack_bf16(oc[dt][0] * vsc, oc[dt][1] * vsc),
-                           pack_bf16(oc[dt][2] * vsc, oc[dt][3] * vsc));
-        }
-        // multi-row units write their (max, denominator) records now (two per
-        // lane); the others keep theirs with the held rows
-        if (MR && g == 0 && col)
-          a.ws_ml[int64_t(slot) * MLS + c] = make_float2(m[ct] * c2, l[ct]);
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<uint2*>(rows_lds + i16 * ROW + (16 * dt + 4 * g) * 2) =
+              make_uint2(pack_bf16(oc[dt][0] * inv, oc[dt][1] * inv),
+                         pack_bf16(oc[dt][2] * inv, oc[dt][3] * inv));
       }
+      kind = 1;
+      rows = __ballot(g == 0 && keep);
+    } else {
+      // partial sums of a split segment go to the combine as bf16 (the (max,
+      // denominator) record stays fp32); accumulation in the wave was fp32
+      if (col) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<uint2*>(rows_lds + i16 * ROW + (16 * dt + 4 * g) * 2) =
+              make_uint2(pack_bf16(oc[dt][0] * vsc, oc[dt][1] * vsc),
+                         pack_bf16(oc[dt][2] * vsc, oc[dt][3] * vsc));
+      }
+      kind = 2;
+      slot = 2 * wk + (owns_start ? 1 : 0);
+      ml = make_float2(m * c2, l);
+      // multi-row waves write their (max, denominator) records now (the
+      // columns in use change from one segment to the next); the others keep
+      // theirs with the held rows
+      if (MR && g == 0 && col) a.ws_ml[int64_t(slot) * MLS + c] = ml;
     }
-    const float2 ml = whole ? make_float2(0.f, 0.f) : make_float2(m[0] * c2, l[0]);
     if (kSlots == 1 || h == 0) {
       kind0 = kind; s0 = x.s; kvh0 = x.kvh; hc0 = x.hc; rows0 = rows; slot0 = slot; ml0 = ml;
     } else {
@@ -988,8 +958,8 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
         int pb = 0;
         if constexpr (BIG_B) pb = __builtin_amdgcn_readlane(win, ((j * kTile) >> b_shift) - jb0);
 #pragma unroll
-        for (int ut = 0; ut < NIT; ++ut) {  // rows of KV head kvh + ut / NI
-          const int t = min(j * kTile + (ut % NI) * RPI + lrow, Lm1);
+        for (int ut = 0; ut < NLT; ++ut) {  // rows of KV head kvh + ut / NI
+          const int t = min(j * kTile + row0 + (ut % NI) * RPI + lrow, Lm1);
           if constexpr (!BIG_B) pb = __shfl(win, (t >> b_shift) - jb0);
           const int64_t off = int64_t(pb) * block_bytes + head_off +
                               int64_t(ut / NI) * B * GROW + int64_t(t & Bm1) * GROW;
@@ -1002,7 +972,7 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
       // load is unconditional (past the chunk it re-reads the chunk's last
       // tile, an L2 hit): with conditional loads the compiler cannot count the
       // loads in flight and waits for all of them.
-      uint4 kb[NB][NIT], vb[NB][NIT];
+      uint4 kb[NB][NLT], vb[NB][NLT];
       int j = jc;
 #pragma unroll
       for (int b = 0; b < NB - 1; ++b) load_tile(min(j + b, jc_end - 1), kb[b], vb[b]);
@@ -1028,6 +998,11 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
   // the tokens after it of member 0, 1, ... (through that member's row, from
   // the entry of the prefix's end on), each scored by that member's columns.
   auto run_tiles = [&](const Cursor& x, int j0, int j1, int win0) {
+    if constexpr (MR) {
+      // none of this wave's columns has a row here (pairs: skip only together,
+      // when the sequence has no rows; a wave without columns scores -inf)
+      if (PAIR ? ncols == 0 : cb >= ncols) return;
+    }
     if constexpr (!GROUPED) {
       run_part(a.block_tables + int64_t(x.s) * a.max_blocks_per_seq, x.L, j0, j1, x.kvh, true,
                win0, true);
@@ -1052,8 +1027,8 @@ __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) 
     }
   };
 
-  walk_slice<D, 8, GROUPED>(a, w, lane, n_hchunk, HPW, KVP, prefetch, begin_segment, run_tiles,
-                            end_segment);
+  walk_slice<D, 8, GROUPED>(a, wk, lane, n_hchunk, HPW, KVP, prefetch, begin_segment, run_tiles,
+                            end_segment, ct == 0);
   flush();  // the wave is done: its held results
 }
 
@@ -1242,27 +1217,42 @@ hipError_t run_grouped(const DecodeArgs& a, hipStream_t st) {
 }
 
 // Multi-row decode (bf16 pools): units of (sequence, KV head) with up to
-// kMultiRowCols (row, query head) columns, one wave per SIMD.
+// kMultiRowCols (row, query head) columns, 16 per wave: units of more than 16
+// run on a workgroup of two waves that share each K/V tile in LDS; two waves
+// per SIMD.
 template <int D>
 hipError_t run_multirow(const DecodeArgs& a, hipStream_t st) {
   int b_shift = 0;
   while ((1 << b_shift) < a.block_size) ++b_shift;
-  const int cus = a.num_cus > 0 ? a.num_cus : 1;
-  int wpg = (a.workers + cus - 1) / cus;
-  wpg = wpg < 1 ? 1 : (wpg > kMultiRowWaves ? kMultiRowWaves : wpg);
-  const int groups = (a.workers + wpg - 1) / wpg;
   const float scale_log2 = a.scale * kLog2e;
-  constexpr int H = kMultiRowCols;
-  const size_t lds = size_t(wpg) * mfma_wave_lds<D, H, 1>();
-  if (a.block_size >= kTile)
-    decode_mfma_kernel<D, H, true, PA_BF16, 1, false, true>
-        <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
-  else
-    decode_mfma_kernel<D, H, false, PA_BF16, 1, false, true>
-        <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
+  constexpr int H = 16;
+  if (a.mr_pair) {
+    // one workgroup of two waves per work slice
+    const size_t lds = mr_pair_lds<D>();
+    if (a.block_size >= kTile)
+      decode_mfma_kernel<D, H, true, PA_BF16, 1, false, true, true>
+          <<<a.workers, 2 * kWave, lds, st>>>(a, b_shift, 1, scale_log2);
+    else
+      decode_mfma_kernel<D, H, false, PA_BF16, 1, false, true, true>
+          <<<a.workers, 2 * kWave, lds, st>>>(a, b_shift, 1, scale_log2);
+  } else {
+    const int cus = a.num_cus > 0 ? a.num_cus : 1;
+    int wpg = (a.workers + cus - 1) / cus;
+    wpg = wpg < 1 ? 1 : (wpg > kMultiRowWaves ? kMultiRowWaves : wpg);
+    const int groups = (a.workers + wpg - 1) / wpg;
+    const size_t lds = size_t(wpg) * mfma_wave_lds<D, H, 1>();
+    if (a.block_size >= kTile)
+      decode_mfma_kernel<D, H, true, PA_BF16, 1, false, true>
+          <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
+    else
+      decode_mfma_kernel<D, H, false, PA_BF16, 1, false, true>
+          <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_combine_kernel<PA_BF16, D, H, false, true, true><<<groups, kWave * wpg, 0, st>>>(a);
+  const int cwpg = a.workers < kMaxWavesPerGroup ? a.workers : kMaxWavesPerGroup;
+  decode_combine_kernel<PA_BF16, D, kMultiRowCols, false, true, true>
+      <<<(a.workers + cwpg - 1) / cwpg, kWave * cwpg, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -122,9 +122,13 @@ struct DecodeArgs {
   // 0 .. that position. Each (sequence, KV head) is one unit whose columns
   // are (row r, query head h) = r * G + h, at most kMultiRowCols of them.
   const int32_t* q_start_loc;
+  // Multi-row units of more than 16 columns (mr_pair = 1) run on a workgroup
+  // of two waves, each holding 16 of the columns and loading half of every
+  // K/V tile into LDS that both read; `workers` then counts the pairs.
+  int32_t mr_pair;
 };
 constexpr int kMultiRowCols = 32;
-constexpr int kMultiRowWaves = 4;  // multi-row decode: waves per CU (one per SIMD)
+constexpr int kMultiRowWaves = 8;  // multi-row decode: waves per CU (two per SIMD)
 
 hipError_t launch_cache_write(const pa_pool& pool, const void* k_new, const void* v_new,
                               const int64_t* slots, int32_t T, hipStream_t stream);

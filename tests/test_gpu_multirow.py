@@ -2,8 +2,10 @@
 batches whose chunks are short (max_q_len x query heads per KV head <= 32, a
 bf16 pool) run as one multi-row decode over every sequence, decode rows
 included; each (row, query head) column attends causally up to its own
-row's position. Cases: speculative-verification shapes (a few draft rows per
-sequence) for groups of 8, 4, 2 and 1 query heads, head_dim 64 and 128,
+row's position; units of more than 16 columns run on a pair of waves that
+share each K/V tile, smaller ones on one wave. Cases: speculative-verification
+shapes (a few draft rows per sequence) for groups of 8, 4, 2 and 1 query
+heads, head_dim 64 and 128, both launch shapes,
 blocks of 4 to 64 tokens, chunks without rows, decode rows mixed in, every
 split of the work between wavefronts, and the Llama-2-70B-shaped workload
 (small, and full size with every row compared).
@@ -59,6 +61,10 @@ CASES = {
     "g1_k32_d128": (4, 4, 128, 16, [], [(32, 640), (31, 31), (5, 6)]),
     "g8_b64": (16, 2, 128, 64, [70], [(4, 256), (3, 130), (4, 64)]),
     "g8_d64_b32": (16, 2, 64, 32, [1], [(4, 97), (2, 2)]),
+    # at most 16 columns per unit: one wave per unit instead of a pair
+    "g8_k2": (64, 8, 128, 16, [5, 900], [(2, 300), (2, 4), (1, 1000), (2, 513), (0, 40)]),
+    "g4_k3_b8": (16, 4, 128, 8, [33], [(3, 129), (1, 700), (3, 16)]),
+    "g1_k16_d64": (8, 8, 64, 16, [2], [(16, 64), (9, 300), (16, 16)]),
 }
 
 
@@ -68,9 +74,11 @@ def test_short_chunks(name):
 
 
 @pytest.mark.parametrize("workers", [1, 5, 64, 1000])
-def test_worker_splits(workers):
-    """Units split between wavefronts at any tile recombine to the same rows."""
-    _run(CASES["g8_k4"], workers=workers)
+@pytest.mark.parametrize("name", ["g8_k4", "g8_k2"])
+def test_worker_splits(name, workers):
+    """Units split between work slices (pairs of waves for g8_k4, single
+    waves for g8_k2) at any tile recombine to the same rows."""
+    _run(CASES[name], workers=workers)
 
 
 def _verify_llama70b(wl, k=4):
