@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 MODEL_LAYERS = {"llama13b": 40, "llama70b": 80, "prefix": 40, "cow": 40, "cow504": 40, "beam": 40,
-                "tiny": 1, "llama13b_fp8": 40}
+                "tiny": 1, "llama13b_fp8": 40, "llama70b_fp8": 80}
 
 WORKLOAD_TEXT = {
     "llama13b": "LLaMA-13B-shaped decode layer: 64 seqs, 40 MHA heads x 128, bf16 KV, "
@@ -49,6 +49,9 @@ WORKLOAD_TEXT = {
     "llama13b_fp8": "LLaMA-13B-shaped decode layer with an FP8 (OCP E4M3) KV cache: 64 seqs, "
                     "40 MHA heads x 128, scale 2^-6 per pool, bf16 q/out, block 16, "
                     "lengths U[1,2048], random placement",
+    "llama70b_fp8": "Llama-2-70B-shaped GQA decode layer with an FP8 (OCP E4M3) KV cache: 256 "
+                    "seqs, 64 q / 8 KV heads x 128, scale 2^-6 per pool, bf16 q/out, block 16, "
+                    "lengths log-uniform [128,8192]",
 }
 
 
@@ -516,10 +519,10 @@ def spec_verify_row(ld, steps, warmup, workers, k=4):
     explained" section 7.5, "vLLM inference engine deep dive" section 5.2: the
     target model verifies the draft model's tokens in one pass), its last k
     positions taken as causal chunk rows (section 7.2 of the first page).
-    pa_attention_mixed
-    runs such short chunks as one multi-row decode (each K/V row read once for
-    all k rows); beside it the same rows on the chunked-prefill kernel and the
-    plain decode of the batch (one row per sequence)."""
+    pa_attention_mixed runs such short chunks as one multi-row decode (each
+    K/V row read once for all k rows); beside it the same rows on the
+    chunked-prefill kernel (bf16 pools only) and the plain decode of the batch
+    (one row per sequence)."""
     import numpy as np
     import torch
     import paged_kv_cache_316_amd as pkv
@@ -548,8 +551,10 @@ def spec_verify_row(ld, steps, warmup, workers, k=4):
         return time_steps(step, steps, warmup)[2]
     v_ms = timed(lambda p: pkv.attention_mixed(q, loc, ld.lens_d, p, ld.tables_d, 0, k, wl.scale,
                                                workers, out=out, workspace=ws))
-    pf_ms = timed(lambda p: pkv.prefill_chunk(q, loc, ld.lens_d, p, ld.tables_d, k, wl.scale,
-                                              out=out))
+    # the chunked-prefill kernel reads bf16 pools only
+    pf_ms = (None if wl.pool_dtype == "fp8_e4m3" else
+             timed(lambda p: pkv.prefill_chunk(q, loc, ld.lens_d, p, ld.tables_d, k, wl.scale,
+                                               out=out)))
     _, _, d_ms = time_steps(decode_step_fn(ld, workers), steps, warmup)
     t = float(v_ms.mean()) * 1e-3
     gbps = ld.kv_bytes / t / 1e9
@@ -558,7 +563,8 @@ def spec_verify_row(ld, steps, warmup, workers, k=4):
     return {"workload": WORKLOAD_TEXT[ld.name] + f"; every sequence verifies {k} draft tokens "
                         "(its last positions as causal chunk rows)",
             "draft_rows_per_seq": k, "verify_us": _stats_us(v_ms),
-            "prefill_kernel_path_us": _stats_us(pf_ms), "decode_us": _stats_us(d_ms),
+            "prefill_kernel_path_us": None if pf_ms is None else _stats_us(pf_ms),
+            "decode_us": _stats_us(d_ms),
             "verify_over_decode": round(float(v_ms.mean() / d_ms.mean()), 3),
             "kv_bytes": int(ld.kv_bytes), "flops": 4.0 * wl.head_dim * wl.num_q_heads * pairs,
             "draft_tokens_per_s": round(S * k / t, 1),
@@ -977,6 +983,10 @@ def main():
             switch("llama70b")
             rows["spec_verify_llama70b"] = spec_verify_row(ld, short, min(args.warmup, 5),
                                                            args.workers)
+        if want("spec_verify_llama70b_fp8"):
+            switch("llama70b_fp8")
+            rows["spec_verify_llama70b_fp8"] = spec_verify_row(ld, short, min(args.warmup, 5),
+                                                               args.workers)
         if want("decode_llama13b_fp8") and args.workload != "llama13b_fp8":
             switch("llama13b_fp8")
             f = rows["decode_llama13b_fp8"] = decode_row(ld, short, args.warmup, args.workers)

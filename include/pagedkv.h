@@ -370,21 +370,24 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,
  *                  num_prefill, num_q_heads, num_kv_heads, head_dim, max_q_len,
  *                  num_workers) bytes, 16-byte aligned (unused when the batch
  *                  has no decode rows and no short chunks)
- * Short chunks (a bf16 pool and max_q_len * num_q_heads / num_kv_heads <= 32:
- * small prompt pieces, and the target model checking a draft model's k tokens
- * in one pass, "vLLM PagedAttention explained" section 7.5 and "vLLM inference
- * engine deep dive" section 5.2) take the multi-row
- * decode: every sequence, decode rows included, is one unit per KV head whose
- * MFMA columns are its (row, query head) pairs, each masked at its own row's
- * position, so each K/V row is read once for all of a sequence's rows (units
- * of more than 16 columns: two wavefronts of one workgroup, 16 columns each,
- * that share every K/V tile through LDS).
+ * Short chunks (a bf16 or PA_FP8_E4M3 pool and max_q_len * num_q_heads /
+ * num_kv_heads <= 32, or <= 16 for FP8 pools of head_dim 64: small prompt
+ * pieces, and the target model checking a draft model's k tokens in one pass,
+ * "vLLM PagedAttention explained" section 7.5 and "vLLM inference engine deep
+ * dive" section 5.2) take the multi-row decode: every sequence, decode rows
+ * included, is one unit per KV head whose MFMA columns are its (row, query
+ * head) pairs, each masked at its own row's position, so each K/V row is read
+ * once for all of a sequence's rows (units of more than 16 columns: two
+ * wavefronts of one workgroup, 16 columns each, that share every K/V tile
+ * through LDS).
  * Otherwise, with both kinds of rows, the chunks run on a second stream of the
  * library's (one per host thread and device, default priority) that forks
  * from and joins back into `stream`, so that the two kernels share the chip.
- * Prefill rows need a bf16 pool (PA_ERR_UNSUPPORTED otherwise); decode rows
- * take every pa_decode dtype. Each row's result is that of pa_decode or
- * pa_prefill_chunk for it alone (up to the decode's worker count).
+ * Chunks the multi-row decode does not take need a bf16 pool
+ * (PA_ERR_UNSUPPORTED otherwise); decode rows take every pa_decode dtype.
+ * Each row's result is that of pa_decode or pa_prefill_chunk for it alone
+ * (up to the decode's worker count), or, on the multi-row path, the same
+ * causal attention up to rounding.
  */
 /* Workspace bytes of pa_attention_mixed for a batch of this shape (0 for
  * invalid sizes). */

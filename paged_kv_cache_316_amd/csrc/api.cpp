@@ -91,12 +91,15 @@ DecodeLayout multirow_layout(int32_t head_dim, int32_t workers, bool pair) {
 bool multirow_pair(int32_t G, int32_t max_q_len) { return int64_t(max_q_len) * G > 16; }
 
 // A mixed batch runs as one multi-row decode when its chunks are short: a
-// bf16 pool and every sequence's rows x query heads per KV head within the
-// columns of one unit.
+// bf16 or FP8 pool and every sequence's rows x query heads per KV head within
+// the columns of one unit. FP8 rows of 64 dims fill a tile with one wave-wide
+// load, which a pair of waves cannot split: there, at most 16 columns.
 bool multirow_fits(int32_t dtype, int32_t head_dim, int32_t G, int32_t num_prefill,
                    int32_t max_q_len) {
-  return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) && num_prefill > 0 &&
-         max_q_len >= 1 && int64_t(max_q_len) * G <= kMultiRowCols;
+  const int64_t cols = int64_t(max_q_len) * G;
+  const int64_t max_cols = dtype == PA_FP8_E4M3 && head_dim == 64 ? 16 : kMultiRowCols;
+  return (dtype == PA_BF16 || dtype == PA_FP8_E4M3) && (head_dim == 64 || head_dim == 128) &&
+         num_prefill > 0 && max_q_len >= 1 && cols <= max_cols;
 }
 
 // Members per unit of the grouped decode: the largest divisor of group_size
@@ -608,14 +611,17 @@ pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_lo
        reinterpret_cast<uintptr_t>(pool->k_pool) | reinterpret_cast<uintptr_t>(pool->v_pool)) & 15)
     return fail(PA_ERR_INVALID, "%s: out/q/pools must be 16-byte aligned", who);
   const int32_t G = num_q_heads / pool->num_kv_heads;
-  if (num_prefill > 0 && !pa::prefill_supported(pool->dtype, pool->head_dim, pool->block_size, G))
-    return fail(PA_ERR_UNSUPPORTED, "%s: prefill rows need a bf16 pool (dtype=%d head_dim=%d)",
-                who, pool->dtype, pool->head_dim);
+  const bool multirow = pa::multirow_fits(pool->dtype, pool->head_dim, G, num_prefill, max_q_len);
+  if (num_prefill > 0 && !multirow &&
+      !pa::prefill_supported(pool->dtype, pool->head_dim, pool->block_size, G))
+    return fail(PA_ERR_UNSUPPORTED, "%s: chunks longer than the multi-row path takes need a bf16 "
+                "pool (dtype=%d head_dim=%d max_q_len=%d)", who, pool->dtype, pool->head_dim,
+                max_q_len);
   if (num_decode > 0 && !pa::decode_supported(pool->dtype, pool->head_dim, G))
     return fail(PA_ERR_UNSUPPORTED, "%s: dtype=%d head_dim=%d group=%d not built", who,
                 pool->dtype, pool->head_dim, G);
   const bool chunks = num_prefill > 0 && max_q_len > 0;
-  if (pa::multirow_fits(pool->dtype, pool->head_dim, G, num_prefill, max_q_len)) {
+  if (multirow) {
     // short chunks (speculative verification, small prompt pieces): decode
     // rows and chunk rows in one multi-row decode over all the sequences
     const bool pair = pa::multirow_pair(G, max_q_len);

@@ -561,13 +561,15 @@ template <int D>
 constexpr size_t mr_pair_lds() {
   return size_t(2) * 2 * kTile * 2 * D + size_t(2) * 2 * 16 * 2 * D;
 }
-constexpr int kMRPairTiles = 2;  // tiles in flight per wave of a pair
+constexpr int kMRPairTiles = 2;  // tiles in flight per wave of a pair (3-4 measured slower)
 
 template <int D, int HPW, bool BIG_B, int KV, int KVP, bool GROUPED, bool MR = false,
           bool PAIR = false>
 __global__ __launch_bounds__(kWave * (MR ? kMultiRowWaves : kMaxWavesPerGroup)) void decode_mfma_kernel(
     DecodeArgs a, int32_t b_shift, int32_t n_hchunk, float scale_log2) {
   static_assert(!PAIR || MR, "pairs of waves are a multi-row launch");
+  static_assert(!PAIR || (KV == PA_FP8_E4M3 ? D : 2 * D) * kTile >= 2048,
+                "a pair splits each tile's rows: at least two wave-wide loads per tile");
   static_assert(!GROUPED || (KVP == 1 && HPW == kGroupedCols), "grouped units: 16 columns");
   static_assert(!MR || (KVP == 1 && !GROUPED && HPW == 16), "multi-row waves: 16 columns");
   constexpr bool FP8 = KV == PA_FP8_E4M3;
@@ -1216,25 +1218,30 @@ hipError_t run_grouped(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Multi-row decode (bf16 pools): units of (sequence, KV head) with up to
+// Multi-row decode (bf16 and FP8 pools): units of (sequence, KV head) with up to
 // kMultiRowCols (row, query head) columns, 16 per wave: units of more than 16
 // run on a workgroup of two waves that share each K/V tile in LDS; two waves
 // per SIMD.
-template <int D>
+template <int KV, int D>
 hipError_t run_multirow(const DecodeArgs& a, hipStream_t st) {
   int b_shift = 0;
   while ((1 << b_shift) < a.block_size) ++b_shift;
   const float scale_log2 = a.scale * kLog2e;
   constexpr int H = 16;
   if (a.mr_pair) {
-    // one workgroup of two waves per work slice
-    const size_t lds = mr_pair_lds<D>();
-    if (a.block_size >= kTile)
-      decode_mfma_kernel<D, H, true, PA_BF16, 1, false, true, true>
-          <<<a.workers, 2 * kWave, lds, st>>>(a, b_shift, 1, scale_log2);
-    else
-      decode_mfma_kernel<D, H, false, PA_BF16, 1, false, true, true>
-          <<<a.workers, 2 * kWave, lds, st>>>(a, b_shift, 1, scale_log2);
+    // one workgroup of two waves per work slice (not for FP8 rows of 64 dims,
+    // whose tile is one wave-wide load)
+    if constexpr (KV == PA_FP8_E4M3 && D == 64) {
+      return hipErrorInvalidValue;
+    } else {
+      const size_t lds = mr_pair_lds<D>();
+      if (a.block_size >= kTile)
+        decode_mfma_kernel<D, H, true, KV, 1, false, true, true>
+            <<<a.workers, 2 * kWave, lds, st>>>(a, b_shift, 1, scale_log2);
+      else
+        decode_mfma_kernel<D, H, false, KV, 1, false, true, true>
+            <<<a.workers, 2 * kWave, lds, st>>>(a, b_shift, 1, scale_log2);
+    }
   } else {
     const int cus = a.num_cus > 0 ? a.num_cus : 1;
     int wpg = (a.workers + cus - 1) / cus;
@@ -1242,10 +1249,10 @@ hipError_t run_multirow(const DecodeArgs& a, hipStream_t st) {
     const int groups = (a.workers + wpg - 1) / wpg;
     const size_t lds = size_t(wpg) * mfma_wave_lds<D, H, 1>();
     if (a.block_size >= kTile)
-      decode_mfma_kernel<D, H, true, PA_BF16, 1, false, true>
+      decode_mfma_kernel<D, H, true, KV, 1, false, true>
           <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
     else
-      decode_mfma_kernel<D, H, false, PA_BF16, 1, false, true>
+      decode_mfma_kernel<D, H, false, KV, 1, false, true>
           <<<groups, kWave * wpg, lds, st>>>(a, b_shift, 1, scale_log2);
   }
   hipError_t e = hipGetLastError();
@@ -1285,9 +1292,14 @@ bool decode_supported(int dtype, int head_dim, int group) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   if (a.q_start_loc) {
-    if (a.dtype != PA_BF16 || a.prefix_lens || a.len_offset) return hipErrorInvalidValue;
-    if (a.head_dim == 128) return run_multirow<128>(a, st);
-    if (a.head_dim == 64) return run_multirow<64>(a, st);
+    if (a.prefix_lens || a.len_offset) return hipErrorInvalidValue;
+    if (a.dtype == PA_BF16) {
+      if (a.head_dim == 128) return run_multirow<PA_BF16, 128>(a, st);
+      if (a.head_dim == 64) return run_multirow<PA_BF16, 64>(a, st);
+    } else if (a.dtype == PA_FP8_E4M3) {
+      if (a.head_dim == 128) return run_multirow<PA_FP8_E4M3, 128>(a, st);
+      if (a.head_dim == 64) return run_multirow<PA_FP8_E4M3, 64>(a, st);
+    }
     return hipErrorInvalidValue;
   }
   if (a.prefix_lens) {

@@ -175,6 +175,17 @@ def llama70b(rng, size):
                          prefill_n=pn, prefill_len=pl)
 
 
+def llama70b_fp8(rng, size):
+    """The llama70b structure with an FP8 (E4M3) KV cache, one scale per pool
+    (2^-6): the GQA shape for attention over FP8 codes (decode, and short
+    chunks such as speculative verification)."""
+    wl = llama70b(rng, size)
+    wl.name = "llama70b_fp8"
+    wl.kv_dtype = "fp8_e4m3"
+    wl.k_scale = wl.v_scale = 2.0 ** -6
+    return wl
+
+
 def _parallel_sampling(name, rng, size, prompt_full, prompt_small):
     """Parallel sampling: each prompt is forked into 3 samples that share its
     blocks (ref count 3) and then append divergent tails, one token per step."""
@@ -324,6 +335,7 @@ CONFIGS: Dict[str, tuple] = {
     "prefix": (4, prefix),
     "llama70b": (5, llama70b),
     "llama13b_fp8": (21, llama13b_fp8),
+    "llama70b_fp8": (51, llama70b_fp8),
 }
 
 
