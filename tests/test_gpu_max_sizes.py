@@ -9,6 +9,9 @@ oracle through the C ABI:
   write, block copy, decode, chunked prefill) needs 64-bit addressing;
 - a batch of 8 192 short sequences (a long work list, the per-64-sequence
   length windows of the walker).
+
+Each case also runs the multi-row decode of pa_attention_mixed (the last few
+positions of sequences as causal rows, as in speculative verification).
 """
 
 import numpy as np
@@ -63,13 +66,23 @@ def test_context_of_131072_tokens(Hq):
     _note(f"131072-token context, Hq={Hq}: writing {nb} blocks")
     ks, vs = _write(pool, tables, [L], Hkv, D, B, rng)
     q = torch.from_numpy(rng.standard_normal((1, Hq, D)).astype(np.float32)).bfloat16()
-    out = pkv.decode(q.cuda(), pool, torch.from_numpy(tables).cuda(),
-                     torch.tensor([L], dtype=torch.int32, device="cuda"), 1 / np.sqrt(D))
+    d_tables = torch.from_numpy(tables).cuda()
+    d_lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    out = pkv.decode(q.cuda(), pool, d_tables, d_lens, 1 / np.sqrt(D))
     torch.cuda.synchronize()
-    want = decode_attention(q.double().numpy(), [ks[0].double().numpy()],
-                            [vs[0].double().numpy()], 1 / np.sqrt(D))
+    K, V = ks[0].double().numpy(), vs[0].double().numpy()
+    want = decode_attention(q.double().numpy(), [K], [V], 1 / np.sqrt(D))
     stats = assert_close(_Bf16, out_f64(out), want, f"L={L} Hq={Hq}")
     _note(f"  {stats}")
+    # the last 4 positions as causal rows: multi-row decode (64 heads: 32
+    # columns per unit, a pair of waves; 8 heads: 4 columns, single waves)
+    k = 4
+    q4 = torch.from_numpy(rng.standard_normal((k, Hq, D)).astype(np.float32)).bfloat16()
+    loc = torch.tensor([0, k], dtype=torch.int32, device="cuda")
+    out4 = pkv.attention_mixed(q4.cuda(), loc, d_lens, pool, d_tables, 0, k, 1 / np.sqrt(D))
+    torch.cuda.synchronize()
+    want4 = prefill_attention(q4.double().numpy(), K, V, L - k, 1 / np.sqrt(D))
+    _note(f"  multi-row: {assert_close(_Bf16, out_f64(out4), want4, f'L={L} Hq={Hq} rows')}")
 
 
 def test_pool_beyond_4gib():
@@ -130,6 +143,19 @@ def test_pool_beyond_4gib():
     torch.cuda.synchronize()
     want = prefill_attention(qp.double().numpy(), kk[0], vv[0], lens[0] - C, 1 / np.sqrt(D))
     _note(f"  prefill: {assert_close(_Bf16, out_f64(out), want, 'prefill')}")
+
+    # multi-row decode: the last 4 positions of every sequence but the
+    # 1-token one (1 row there), 64 heads (32 columns per unit)
+    rows = [min(4, L) for L in lens]
+    q4 = torch.from_numpy(rng.standard_normal((sum(rows), Hq, D)).astype(np.float32)).bfloat16()
+    loc4 = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    out = pkv.attention_mixed(q4.cuda(), torch.from_numpy(loc4).cuda(), d_lens, pool, d_tables, 0,
+                              4, 1 / np.sqrt(D))
+    torch.cuda.synchronize()
+    qd = q4.double().numpy()
+    want = np.concatenate([prefill_attention(qd[loc4[s]:loc4[s + 1]], kk[s], vv[s], L - rows[s],
+                                             1 / np.sqrt(D)) for s, L in enumerate(lens)])
+    _note(f"  multi-row: {assert_close(_Bf16, out_f64(out), want, 'multi-row')}")
     del pool
     torch.cuda.empty_cache()
 
@@ -150,9 +176,23 @@ def test_batch_of_8192_sequences():
     _note(f"{S} sequences, {sum(lens)} tokens")
     ks, vs = _write(pool, tables, lens, Hkv, D, B, rng)
     q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float32)).bfloat16()
-    out = pkv.decode(q.cuda(), pool, torch.from_numpy(tables).cuda(),
-                     torch.tensor(lens, dtype=torch.int32, device="cuda"), 1 / np.sqrt(D))
+    d_tables = torch.from_numpy(tables).cuda()
+    d_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = pkv.decode(q.cuda(), pool, d_tables, d_lens, 1 / np.sqrt(D))
     torch.cuda.synchronize()
-    want = decode_attention(q.double().numpy(), [k.double().numpy() for k in ks],
-                            [v.double().numpy() for v in vs], 1 / np.sqrt(D))
+    kk = [k.double().numpy() for k in ks]
+    vv = [v.double().numpy() for v in vs]
+    want = decode_attention(q.double().numpy(), kk, vv, 1 / np.sqrt(D))
     _note(f"  {assert_close(_Bf16, out_f64(out), want, f'{S} sequences')}")
+    # multi-row decode over the same batch: up to 3 rows per sequence (single
+    # waves, 3 columns per unit), the last positions of each
+    rows = [min(3, L) for L in lens]
+    q3 = torch.from_numpy(rng.standard_normal((sum(rows), Hq, D)).astype(np.float32)).bfloat16()
+    loc3 = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    out = pkv.attention_mixed(q3.cuda(), torch.from_numpy(loc3).cuda(), d_lens, pool, d_tables, 0,
+                              3, 1 / np.sqrt(D))
+    torch.cuda.synchronize()
+    qd = q3.double().numpy()
+    want = np.concatenate([prefill_attention(qd[loc3[s]:loc3[s + 1]], kk[s], vv[s], L - rows[s],
+                                             1 / np.sqrt(D)) for s, L in enumerate(lens)])
+    _note(f"  multi-row: {assert_close(_Bf16, out_f64(out), want, f'{S} sequences, rows')}")
