@@ -63,6 +63,16 @@ int main(void) {
              PA_ERR_INVALID, "decode with NULL buffers refused");
   expect(pa_cache_write(NULL, NULL, NULL, NULL, 1, NULL) == PA_ERR_INVALID,
          "cache write without a pool refused");
+
+  /* workspace sizes: the multi-row decode of 4 rows x 8 query heads per KV
+     head (32 columns) takes, per work slice, two 32-row slots of bf16
+     partials and (max, denominator) records, and one split record */
+  expect(pa_attention_mixed_workspace_bytes(0, 256, 64, 8, 128, 4, 10) ==
+             (size_t)(2 * 10 * 32 * 128 * 2 + 2 * 10 * 32 * 8 + 10 * 16),
+         "multi-row workspace size");
+  expect(pa_attention_mixed_workspace_bytes(0, 8, 6, 4, 128, 4, 10) == 0,
+         "workspace size of 6 query heads over 4 KV heads is 0");
+  expect(pa_decode_workspace_bytes(64, 40, 40, 128, 100) > 0, "decode workspace size");
   printf("%d failures\n", failures);
   return failures != 0;
 }
