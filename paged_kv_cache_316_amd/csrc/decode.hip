@@ -50,6 +50,12 @@ namespace {
 
 constexpr int kMaxWavesPerGroup = 8;  // one workgroup per CU holds that CU's waves
 constexpr int kTile = 16;  // tokens per tile
+// Weights of the work split: a tile counts kTileW, the start of a segment
+// kSegW (its query and table loads and the first tile's round trip). Timing
+// each wave put a segment start at about 60 % of a tile; of the weights 2, 4
+// and 6 (in quarters of a tile), 4 gave the best rates over the batches.
+constexpr int kTileW = 4;
+constexpr int kSegW = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef short bf16x2_t __attribute__((__vector_size__(2 * sizeof(short))));
@@ -187,13 +193,23 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
   auto item_len = [&](int s) -> int { return GROUPED ? group_tiles(a, s) : len_of(a, s); };
   auto item_tiles = [&](int v) -> int { return GROUPED ? v : tiles_of(v); };
 
+  // Positions along the work list: a unit of n tiles spans kTileW * n +
+  // kSegW of them, its tile j starting at kSegW + kTileW * j; kSegW stands for
+  // the start-up cost of a segment, in the same quarters of a tile's time, so
+  // that slices full of short units get fewer tiles. Slice w covers positions
+  // [total * w / W, total * (w + 1) / W) and walks the tiles that start in it.
+  // Slices are at least a tile wide, so every slice that lies inside a unit's
+  // tiles walks at least one of them (the combine relies on that).
+  auto unit_w = [&](int n) -> int64_t { return int64_t(kTileW) * n + kSegW; };
   int64_t total = 0;
   for (int base = 0; base < S; base += kWave) {
     const int s = base + lane;
-    total += wave_sum_i32(s < S ? item_tiles(item_len(s)) : 0);
+    const int t = s < S ? item_tiles(item_len(s)) : 0;
+    total += wave_sum_i32(t > 0 ? kTileW * t + kSegW : 0);
   }
   total = uniform64(total * units);
-  const int64_t W = total < a.workers ? total : a.workers;  // every active wave gets >= 1 tile
+  // every active slice is at least a tile wide
+  const int64_t W = total / kTileW < a.workers ? total / kTileW : a.workers;
 
   // empty sequences: zeros, written by wave (s mod Wz) (a multi-row batch
   // has no rows for them: a sequence's rows are already in its length)
@@ -222,15 +238,17 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
     return __builtin_amdgcn_readlane(lwin, s - lwin_base);
   };
 
-  // locate g_begin: the item whose tiles (times units) contain it
+  // locate g_begin: the item whose units contain it, then the unit and the
+  // first of its tiles that starts at or after g_begin
   Cursor cur{};
   {
-    int64_t before = 0;  // tiles x units before this chunk of items
+    int64_t before = 0;  // positions before this chunk of items
     for (int base = 0; base < S; base += kWave) {
       const int s = base + lane;
       const int t = s < S ? item_tiles(item_len(s)) : 0;
-      const int64_t incl = before + int64_t(wave_incl_scan_i32(t, lane)) * units;
-      const int64_t excl = incl - int64_t(t) * units;
+      const int tw = t > 0 ? kTileW * t + kSegW : 0;
+      const int64_t incl = before + int64_t(wave_incl_scan_i32(tw, lane)) * units;
+      const int64_t excl = incl - int64_t(tw) * units;
       const unsigned long long hit = __ballot(s < S && t > 0 && excl <= g_begin && g_begin < incl);
       if (hit) {
         const int l = __builtin_ctzll(hit);
@@ -238,53 +256,66 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int w, int lane,
         cur.s = base + l;
         cur.n = __builtin_amdgcn_readfirstlane(__shfl(t, l));
         cur.L = seq_len(cur.s);
+        const int64_t uw = unit_w(cur.n);
         const int64_t off = g_begin - seq0;
-        cur.u = int(off / cur.n);
-        cur.j = int(off - int64_t(cur.u) * cur.n);
+        cur.u = int(off / uw);
+        const int64_t r = off - int64_t(cur.u) * uw;  // position inside the unit
+        cur.j = r <= kSegW ? 0 : int((r - kSegW + kTileW - 1) / kTileW);
         cur.kvh = (cur.u / n_hchunk) * kvp;
         cur.hc = cur.u % n_hchunk;
-        cur.seg0 = seq0 + int64_t(cur.u) * cur.n;
+        cur.seg0 = seq0 + int64_t(cur.u) * uw;
         break;
       }
       before = uniform64(__shfl(incl, kWave - 1));
     }
   }
-
+  // to tile 0 of the next unit: of this sequence, or of the next non-empty one
+  auto advance = [&]() {
+    cur.j = 0;
+    cur.seg0 += unit_w(cur.n);
+    ++cur.u;
+    if (++cur.hc == n_hchunk) {
+      cur.hc = 0;
+      cur.kvh += kvp;
+    }
+    if (cur.u == units) {
+      cur.u = cur.kvh = cur.hc = 0;
+      do {
+        ++cur.s;
+        cur.L = seq_len(cur.s);
+        cur.n = item_tiles(cur.L);
+      } while (cur.n == 0 && cur.s + 1 < S);
+    }
+  };
+  // tiles of the current unit that start before g_end
+  auto tiles_before_end = [&]() -> int {
+    const int64_t room = g_end - cur.seg0 - kSegW;
+    return room <= 0 ? 0 : int(min(int64_t(cur.n), (room + kTileW - 1) / kTileW));
+  };
+  if (cur.j >= cur.n) advance();  // no tile of that unit starts in the slice
+  if (tiles_before_end() <= cur.j) {  // no tile at all starts in the slice
+    if (lane == 0 && record) a.ws_seg[w] = make_int4(-1, 0, 0, 0);
+    return;
+  }
 
   // walk the segments of this slice
-  int64_t g = g_begin;
   int4 split = make_int4(-1, 0, 0, 0);  // the segment this slice starts and leaves unfinished
   int win = prefetch(cur);
   begin(cur);
   while (true) {
-    const int j1 = int(min(int64_t(cur.n), int64_t(cur.j) + (g_end - g)));
+    const int j1 = tiles_before_end();
     const bool owns_start = cur.j == 0, owns_end = j1 == cur.n;
     run(cur, cur.j, j1, win);
     if (owns_start && !owns_end) {  // only the last segment of a slice can be left open
-      const int64_t last = cur.seg0 + cur.n - 1;
+      const int64_t last = cur.seg0 + unit_w(cur.n) - kTileW;  // start of the unit's last tile
       split = make_int4(cur.s, cur.u, int(((last + 1) * W - 1) / total),
                         cur.kvh * G + cur.hc * hpw);
     }
-    g += j1 - cur.j;
-    const bool more = g < g_end;
+    // another segment follows when the next unit's first tile starts in the slice
+    const bool more = owns_end && cur.seg0 + unit_w(cur.n) + kSegW < g_end;
     const Cursor done = cur;
     if (more) {
-      // next segment: next unit of this sequence, or the next non-empty sequence
-      cur.j = 0;
-      cur.seg0 += cur.n;
-      ++cur.u;
-      if (++cur.hc == n_hchunk) {
-        cur.hc = 0;
-        cur.kvh += kvp;
-      }
-      if (cur.u == units) {
-        cur.u = cur.kvh = cur.hc = 0;
-        do {
-          ++cur.s;
-          cur.L = seq_len(cur.s);
-          cur.n = item_tiles(cur.L);
-        } while (cur.n == 0);
-      }
+      advance();
       win = prefetch(cur);  // its loads go out before the stores of `done`
     }
     end(done, owns_start, owns_end);
