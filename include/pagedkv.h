@@ -253,7 +253,7 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
  *      pa_decode kernels, which also record each row's log-sum-exp;
  *   2. one pass on the matrix cores attends all num_seqs * G query rows of a KV
  *      head to the P*B shared tokens, keys cut into ranges, and writes
- *      unnormalised partials;
+ *      unnormalised partials (sums as bf16, maxima and denominators fp32);
  *   3. a merge combines the partials and the tail result by the log-sum-exp
  *      rule into `out`.
  * Arguments are those of pa_decode, plus:

@@ -130,7 +130,7 @@ PrefixLayout prefix_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv
   p.lse_off = align16(p.dec.total());
   p.ml_off = p.lse_off + align16(rows * 4);
   p.acc_off = p.ml_off + align16(size_t(p.plan.n_split) * rows * 8);
-  p.end = p.acc_off + size_t(p.plan.n_split) * rows * head_dim * 4;
+  p.end = p.acc_off + size_t(p.plan.n_split) * rows * head_dim * 2;
   return p;
 }
 
@@ -569,7 +569,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const pa_pool* pool,
   p.v_pool = pool->v_pool;
   p.block_tables = block_tables;
   p.lse = lse;
-  p.p_acc = reinterpret_cast<float*>(ws + lay.acc_off);
+  p.p_acc = reinterpret_cast<uint16_t*>(ws + lay.acc_off);
   p.p_ml = reinterpret_cast<float2*>(ws + lay.ml_off);
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;

@@ -167,7 +167,7 @@ struct PrefixArgs {
   const void* v_pool;
   const int32_t* block_tables;  // row 0's first num_prefix_blocks entries: the shared blocks
   const float* lse;             // [S][Hq] suffix log-sum-exp (log2 units, -inf if empty)
-  float* p_acc;                 // [n_split][S][Hq][D] unnormalised prefix partials
+  uint16_t* p_acc;              // [n_split][S][Hq][D] unnormalised prefix partials, bf16
   float2* p_ml;                 // [n_split][S][Hq] (max in log2 units, denominator)
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
   int32_t num_prefix_blocks, n_split;

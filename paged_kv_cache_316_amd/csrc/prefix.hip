@@ -33,20 +33,27 @@ constexpr int kPMaxGroups = 2;
 // a wave needs more than 256 registers (more groups, or FP8 widening)
 constexpr int waves_per_group(int ng, bool fp8) { return ng >= 4 || (ng >= 2 && fp8) ? 4 : 8; }
 constexpr float kPLog2e = 1.4426950408889634f;
+constexpr int kPChunk = 4;  // 16-key tiles per LDS stage of the shared pass
 
-// One wave: KV head kvh, NG groups of 16 columns (columns 16*NG*cb onwards),
-// key tiles [t0, t1).
-// Same operand layouts as the GQA decode kernel: K and V tiles go through the
-// wave's own LDS (rows swizzled so that the reads below are conflict-free);
-// S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 keys x 16 columns); the
-// accumulator is already the B operand of O^T = V^T P^T
-// (v_mfma_f32_16x16x16_bf16, V^T read with ds_read_b64_tr_b16); the
-// exponent base of a column moves only when its max grows by more than 2^8.
+// One workgroup: KV head kvh, key tiles [t0, t1), WPG column blocks of NG
+// groups of 16 columns (one block per wave). The key range is walked in
+// chunks of kPChunk tiles: the waves split each chunk's wave-wide K/V loads
+// between them and write them, widened for FP8 pools, into one of two LDS
+// stages, so every tile is read from the pool once per workgroup; one
+// barrier per chunk, and the next chunk's loads stay in flight across it.
+// Every wave of the workgroup loads and meets the barriers; only those with
+// columns compute. Operand layouts as in the GQA decode kernel (rows swizzled
+// so that the reads below are conflict-free): S^T = K Q^T on
+// v_mfma_f32_16x16x32_bf16 (16 keys x 16 columns); the accumulator is
+// already the B operand of O^T = V^T P^T (v_mfma_f32_16x16x16_bf16, V^T read
+// with ds_read_b64_tr_b16); the exponent base of a column moves only when its
+// max grows by more than 2^8.
 template <int D, int NG, bool BIG_B, int KV>
 __global__ __launch_bounds__(kWave * waves_per_group(NG, KV == PA_FP8_E4M3)) void prefix_partial_kernel(
     PrefixArgs a, int32_t b_shift, int32_t n_cblk, int32_t n_cgrp, int32_t tiles_per_split,
     float scale_log2) {
   constexpr bool FP8 = KV == PA_FP8_E4M3;
+  constexpr int WPG = waves_per_group(NG, FP8);
   constexpr int ROW = 2 * D;           // bytes per bf16 row in LDS
   constexpr int GROW = FP8 ? D : ROW;  // bytes per row in the pool
   constexpr int KS = D / 32;
@@ -54,15 +61,17 @@ __global__ __launch_bounds__(kWave * waves_per_group(NG, KV == PA_FP8_E4M3)) voi
   constexpr int CPR = ROW / 16;
   constexpr int GCPR = GROW / 16;
   constexpr int RPI = 1024 / GROW;     // rows per wave-wide 16-byte load
-  constexpr int NI = kPTile / RPI;
+  constexpr int NI = kPTile / RPI;     // such loads per tile
   constexpr int RPL = 256 / ROW;
-  constexpr int TB = kPTile * ROW;
-  constexpr int NB = FP8 ? 4 : 2;      // tiles in flight per wave
+  constexpr int TB = kPTile * ROW;     // one bf16 tile in LDS
+  constexpr int CB = kPChunk * TB;     // the K (or V) half of a stage
+  constexpr int NLD = 2 * kPChunk * NI;  // wave-wide loads per chunk, K then V
+  static_assert(NLD % WPG == 0, "a chunk's loads split evenly over the waves");
+  constexpr int NL = NLD / WPG;        // this wave's share
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int lane = threadIdx.x % kWave;
   const int wig = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wpg = blockDim.x / kWave;
   // Workgroup i runs on XCD i % 8: renumber so that neighbouring work items
   // (same KV head and key range, hence the same K/V) share an XCD's L2.
   int wg = blockIdx.x;
@@ -71,8 +80,8 @@ __global__ __launch_bounds__(kWave * waves_per_group(NG, KV == PA_FP8_E4M3)) voi
   const int rest = wg / n_cgrp;
   const int sp = rest % a.n_split;
   const int kvh = rest / a.n_split;
-  const int cb = cg * wpg + wig;
-  if (cb >= n_cblk) return;
+  const int cb = cg * WPG + wig;
+  const bool active = cb < n_cblk;  // wave-uniform
 
   const int S = a.num_seqs, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
@@ -83,18 +92,25 @@ __global__ __launch_bounds__(kWave * waves_per_group(NG, KV == PA_FP8_E4M3)) voi
   const int n_tiles = (Lp + kPTile - 1) / kPTile;
   const int t0 = sp * tiles_per_split;
   const int t1 = min(t0 + tiles_per_split, n_tiles);
+  const int nch = (t1 - t0 + kPChunk - 1) / kPChunk;
 
-  unsigned char* kt_lds = smem + wig * (2 * TB);
-  unsigned char* vt = kt_lds + TB;
   auto swz = [](int r) { return (r / RPL) % CPR; };
   const int lrow = lane / GCPR, lch = lane % GCPR;
-  uint32_t wr[NI], wr2[NI];
+  // this wave's loads of a chunk: load li = wig + WPG * k is the K load li
+  // (li < NLD / 2) or the V load li - NLD / 2; load kk of a kind reads rows
+  // (kk % NI) * RPI + lrow of the chunk's tile kk / NI
+  int ltile[NL];
+  uint32_t wr[NL], wr2[NL];
 #pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int r = u * RPI + lrow;
+  for (int k = 0; k < NL; ++k) {
+    const int li = wig + WPG * k;
+    const int kk = li % (NLD / 2);
+    ltile[k] = kk / NI;
+    const int r = (kk % NI) * RPI + lrow;
     const int c0 = FP8 ? 2 * lch : lch;
-    wr[u] = uint32_t(r * ROW + ((c0 ^ swz(r)) * 16));
-    wr2[u] = uint32_t(r * ROW + (((c0 + 1) ^ swz(r)) * 16));
+    const uint32_t base = uint32_t((li >= NLD / 2 ? CB : 0) + ltile[k] * TB + r * ROW);
+    wr[k] = base + uint32_t((c0 ^ swz(r)) * 16);
+    wr2[k] = base + uint32_t(((c0 + 1) ^ swz(r)) * 16);
   }
   const uint32_t kr0 = uint32_t(i16 * ROW + ((g ^ swz(i16)) * 16));
   const int rr = 4 * g + i16 / 4;
@@ -108,8 +124,8 @@ __global__ __launch_bounds__(kWave * waves_per_group(NG, KV == PA_FP8_E4M3)) voi
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
     const int col = (cb * NG + q) * 16 + i16;
-    valid[q] = col < N;
-    const int cc = min(col, N - 1);
+    valid[q] = active && col < N;
+    const int cc = max(min(col, N - 1), 0);
     orow[q] = int64_t(cc / G) * Hq + kvh * G + cc % G;
     const unsigned char* qp = static_cast<const unsigned char*>(a.q) + orow[q] * ROW + 16 * g;
 #pragma unroll
@@ -130,31 +146,16 @@ __global__ __launch_bounds__(kWave * waves_per_group(NG, KV == PA_FP8_E4M3)) voi
   const float c2 = FP8 ? scale_log2 * a.k_scale : scale_log2;
   const float vsc = FP8 ? a.v_scale : 1.f;
 
-  // one 16-key tile for the NG column groups: the K and V operands are read
-  // from LDS once and shared by the groups
-  auto compute = [&](int j, const uint4* kr, const uint4* vr) {
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      if constexpr (FP8) {
-        uint4 k0, k1, v0, v1;
-        widen_e4m3(kr[u], k0, k1);
-        widen_e4m3(vr[u], v0, v1);
-        *reinterpret_cast<uint4*>(kt_lds + wr[u]) = k0;
-        *reinterpret_cast<uint4*>(kt_lds + wr2[u]) = k1;
-        *reinterpret_cast<uint4*>(vt + wr[u]) = v0;
-        *reinterpret_cast<uint4*>(vt + wr2[u]) = v1;
-      } else {
-        *reinterpret_cast<uint4*>(kt_lds + wr[u]) = kr[u];
-        *reinterpret_cast<uint4*>(vt + wr[u]) = vr[u];
-      }
-    }
+  // one 16-key tile (tile j, at kt / kt + CB in LDS) for the NG column
+  // groups: the K and V operands are read from LDS once and shared by them
+  auto compute = [&](int j, const unsigned char* kt) {
     uint4 kop[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kop[ks] = *reinterpret_cast<const uint4*>(kt_lds + (kr0 ^ (64u * ks)));
+    for (int ks = 0; ks < KS; ++ks) kop[ks] = *reinterpret_cast<const uint4*>(kt + (kr0 ^ (64u * ks)));
     v4i16_t va[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      va[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vt + (rd0 ^ (32u * dt))));
+      va[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(kt + CB + (rd0 ^ (32u * dt))));
     const int key0 = j * kPTile + 4 * g;
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
@@ -201,9 +202,11 @@ __global__ __launch_bounds__(kWave * waves_per_group(NG, KV == PA_FP8_E4M3)) voi
     }
   };
 
-  // Row 0 of the block tables holds the shared blocks. Tiles are walked in
-  // chunks whose blocks fit a 64-entry window of that row (one entry per
-  // lane); keys past the prefix are clamped to its last token and masked.
+  // Row 0 of the block tables holds the shared blocks. A chunk's 64 keys
+  // lie in at most 64 blocks, whose ids one 64-entry window of that row holds
+  // (one entry per lane), loaded a chunk ahead of its K/V loads. Keys past
+  // the split's last tile re-read that tile (not computed); keys past the
+  // prefix are clamped to its last token and masked.
   const int32_t* row = a.block_tables;
   const int nblk = a.num_prefix_blocks;
   const unsigned char* kp = static_cast<const unsigned char*>(a.k_pool);
@@ -211,41 +214,75 @@ __global__ __launch_bounds__(kWave * waves_per_group(NG, KV == PA_FP8_E4M3)) voi
   const int64_t block_bytes = int64_t(Hkv) * B * GROW;
   const int64_t head_off = int64_t(kvh) * B * GROW + lch * 16;
   const int Lm1 = Lp - 1;
-  for (int jc = t0; jc < t1;) {
+  auto window = [&](int c) -> int {
+    const int jb0 = ((t0 + c * kPChunk) * kPTile) >> b_shift;
+    return c < nch && jb0 + lane < nblk ? row[jb0 + lane] : 0;
+  };
+  uint4 st[NL];  // this wave's share of the next chunk, on its way from the pool
+  auto load_chunk = [&](int c, int win) {
+    const int jc = t0 + c * kPChunk;
     const int jb0 = (jc * kPTile) >> b_shift;
-    const int win = jb0 + lane < nblk ? row[jb0 + lane] : 0;
-    const int jc_end = min(t1, ((jb0 + kWave) << b_shift) / kPTile);
-    auto load_tile = [&](int j, uint4* kr, uint4* vr) {
-      int pb = 0;
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int j = min(jc + ltile[k], t1 - 1);
+      const int li = wig + WPG * k;
+      const int t = min(j * kPTile + ((li % (NLD / 2)) % NI) * RPI + lrow, Lm1);
+      int pb;
       if constexpr (BIG_B) pb = __builtin_amdgcn_readlane(win, ((j * kPTile) >> b_shift) - jb0);
+      else pb = __shfl(win, (t >> b_shift) - jb0);
+      const int64_t off = int64_t(pb) * block_bytes + head_off + int64_t(t & Bm1) * GROW;
+      st[k] = load_stream16(reinterpret_cast<const uint4*>((li >= NLD / 2 ? vp : kp) + off));
+    }
+  };
+  auto store_chunk = [&](int stage) {
+    unsigned char* dst = smem + stage * 2 * CB;
 #pragma unroll
-      for (int u = 0; u < NI; ++u) {
-        const int t = min(j * kPTile + u * RPI + lrow, Lm1);
-        if constexpr (!BIG_B) pb = __shfl(win, (t >> b_shift) - jb0);
-        const int64_t off = int64_t(pb) * block_bytes + head_off + int64_t(t & Bm1) * GROW;
-        kr[u] = load_stream16(reinterpret_cast<const uint4*>(kp + off));
-        vr[u] = load_stream16(reinterpret_cast<const uint4*>(vp + off));
-      }
-    };
-    // NB tiles in flight; every load is unconditional (past the chunk it
-    // re-reads the chunk's last tile) so the compiler can count them
-    uint4 kb[NB][NI], vb[NB][NI];
-    int j = jc;
-#pragma unroll
-    for (int b = 0; b < NB - 1; ++b) load_tile(min(j + b, jc_end - 1), kb[b], vb[b]);
-    for (; j + NB <= jc_end; j += NB) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int jl = min(j + b + NB - 1, jc_end - 1);
-        load_tile(jl, kb[(b + NB - 1) % NB], vb[(b + NB - 1) % NB]);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(j + b, kb[b], vb[b]);
+    for (int k = 0; k < NL; ++k) {
+      if constexpr (FP8) {
+        uint4 lo, hi;
+        widen_e4m3(st[k], lo, hi);
+        *reinterpret_cast<uint4*>(dst + wr[k]) = lo;
+        *reinterpret_cast<uint4*>(dst + wr2[k]) = hi;
+      } else {
+        *reinterpret_cast<uint4*>(dst + wr[k]) = st[k];
       }
     }
+  };
+  // LDS writes of every wave done; the loads in flight stay so. The empty asm
+  // statements keep LDS accesses on their side of the barrier.
+  auto meet = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  int win = window(0);
+  int win_next = window(1);
+  load_chunk(0, win);
+  store_chunk(0);
+  win = win_next;
+  win_next = window(2);
+  if (nch > 1) load_chunk(1, win);
+  meet();
+  for (int c = 0; c < nch; ++c) {
+    if (active) {
+      const unsigned char* kt = smem + (c & 1) * 2 * CB;
+      const int jc = t0 + c * kPChunk;
 #pragma unroll
-    for (int b = 0; b < NB - 1; ++b)
-      if (j + b < jc_end) compute(j + b, kb[b], vb[b]);
-    jc = jc_end;
+      for (int t = 0; t < kPChunk; ++t)
+        if (jc + t < t1) compute(jc + t, kt + t * TB);
+    }
+    if (c + 1 < nch) {
+      // stage (c + 1) & 1 was last read in chunk c - 1, before the last barrier
+      store_chunk((c + 1) & 1);
+      if (c + 2 < nch) {
+        win = win_next;
+        win_next = window(c + 3);
+        load_chunk(c + 2, win);
+      }
+      meet();
+    }
   }
 
 #pragma unroll
@@ -254,11 +291,11 @@ __global__ __launch_bounds__(kWave * waves_per_group(NG, KV == PA_FP8_E4M3)) voi
     l += __shfl_xor(l, 32);
     if (!valid[q]) continue;
     const int64_t prow = int64_t(sp) * S * Hq + orow[q];
-    float4* dst = reinterpret_cast<float4*>(a.p_acc + prow * D);
+    uint2* dst = reinterpret_cast<uint2*>(a.p_acc + prow * D);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      dst[(16 * dt + 4 * g) / 4] = make_float4(o[q][dt][0] * vsc, o[q][dt][1] * vsc,
-                                               o[q][dt][2] * vsc, o[q][dt][3] * vsc);
+      dst[(16 * dt + 4 * g) / 4] = make_uint2(pack_bf16(o[q][dt][0] * vsc, o[q][dt][1] * vsc),
+                                              pack_bf16(o[q][dt][2] * vsc, o[q][dt][3] * vsc));
     if (g == 0) a.p_ml[prow] = make_float2(m[q] * c2, l);
   }
 }
@@ -287,16 +324,15 @@ __global__ __launch_bounds__(256) void prefix_merge_kernel(PrefixArgs a) {
     const float2 ml = a.p_ml[sp * rows + r];
     const float f = __builtin_amdgcn_exp2f(ml.x - Ms);
     den = fmaf(ml.y, f, den);
-    const float4* src = reinterpret_cast<const float4*>(a.p_acc + (sp * rows + r) * D + c * 8);
-    const float4 x0 = src[0], x1 = src[1];
-    num[0] = fmaf(x0.x, f, num[0]);
-    num[1] = fmaf(x0.y, f, num[1]);
-    num[2] = fmaf(x0.z, f, num[2]);
-    num[3] = fmaf(x0.w, f, num[3]);
-    num[4] = fmaf(x1.x, f, num[4]);
-    num[5] = fmaf(x1.y, f, num[5]);
-    num[6] = fmaf(x1.z, f, num[6]);
-    num[7] = fmaf(x1.w, f, num[7]);
+    const uint4 x = *reinterpret_cast<const uint4*>(a.p_acc + (sp * rows + r) * D + c * 8);
+    num[0] = fmaf(bf16_lo(x.x), f, num[0]);
+    num[1] = fmaf(bf16_hi(x.x), f, num[1]);
+    num[2] = fmaf(bf16_lo(x.y), f, num[2]);
+    num[3] = fmaf(bf16_hi(x.y), f, num[3]);
+    num[4] = fmaf(bf16_lo(x.z), f, num[4]);
+    num[5] = fmaf(bf16_hi(x.z), f, num[5]);
+    num[6] = fmaf(bf16_lo(x.w), f, num[6]);
+    num[7] = fmaf(bf16_hi(x.w), f, num[7]);
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   *o = make_uint4(pack_bf16(num[0] * inv, num[1] * inv), pack_bf16(num[2] * inv, num[3] * inv),
@@ -308,10 +344,10 @@ hipError_t run_prefix(const PrefixArgs& a, const PrefixPlan& p, hipStream_t st) 
   int b_shift = 0;
   while ((1 << b_shift) < a.block_size) ++b_shift;
   constexpr int WPG = waves_per_group(NG, KV == PA_FP8_E4M3);
-  const int wpg = p.n_cblk < WPG ? p.n_cblk : WPG;
+  const int wpg = WPG;  // every wave takes a share of the loads, with or without columns
   const int n_cgrp = (p.n_cblk + wpg - 1) / wpg;
   const int groups = a.num_kv_heads * a.n_split * n_cgrp;
-  const size_t lds = size_t(wpg) * 2 * kPTile * 2 * D;
+  const size_t lds = size_t(2) * 2 * kPChunk * kPTile * 2 * D;  // 2 stages of K and V
   const float scale_log2 = a.scale * kPLog2e;
   if (a.block_size >= kPTile)
     prefix_partial_kernel<D, NG, true, KV><<<groups, kWave * wpg, lds, st>>>(

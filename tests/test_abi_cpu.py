@@ -193,8 +193,8 @@ def test_shared_prefix_workspace_formula():
     dec = L.pa_decode_workspace_bytes(2, 2, 2, 128, 10)
     assert dec == 2 * 10 * 2 * 128 * 4 + 2 * 10 * 128 + 10 * 16
     n = L.pa_decode_shared_prefix_workspace_bytes(2, 2, 2, 128, 16, 256, 10)
-    # tail lse (4 floats), 32 x (m, l) and 32 x 128 floats per row
-    assert n == dec + 16 + 32 * 4 * 8 + 32 * 4 * 128 * 4
+    # tail lse (4 floats), 32 x (m, l) and 32 x 128 bf16 partial sums per row
+    assert n == dec + 16 + 32 * 4 * 8 + 32 * 4 * 128 * 2
 
 
 def test_mixed_argument_checks():
