@@ -363,7 +363,7 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* q_start_loc,
  *   max_q_len    : host, >= every prefill chunk's row count
  *   num_workers  : decode work slices, one wavefront each (on the multi-row
  *                  path below with more than 16 columns per unit, a
- *                  workgroup of two wavefronts); 0 = default (3 wavefronts per
+ *                  workgroup of two wavefronts); 0 = default (2 wavefronts per
  *                  compute unit when the batch also has chunks, 8 on the
  *                  multi-row path, else pa_decode's default)
  *   workspace    : device, pa_attention_mixed_workspace_bytes(num_decode,

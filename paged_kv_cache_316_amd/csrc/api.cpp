@@ -139,7 +139,7 @@ bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 // Second stream for work that may overlap the caller's (default priority),
 // with the two events of a fork / join; one set per host thread and device,
 // created on first use and kept until the process ends.
-constexpr int32_t kMixedDecodeWavesPerCU = 3;  // default decode workers beside prefill chunks
+constexpr int32_t kMixedDecodeWavesPerCU = 2;  // default decode workers beside prefill chunks
 constexpr bool kMixedDecodeFirst = false;      // launch order of the two kernels
 struct SideStream {
   hipStream_t stream = nullptr;

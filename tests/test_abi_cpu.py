@@ -211,8 +211,8 @@ def test_mixed_argument_checks():
     assert call(out=None) == -1
     assert call(loc=None) == -1                            # chunks need q_start_loc
     assert call(ws=None) == -5                             # decode rows need the workspace
-    # beside chunks the decode defaults to 3 waves per CU (256 CUs without a device)
-    assert call(wsb=L.pa_decode_workspace_bytes(3, 8, 8, 128, 3 * 256) - 1) == -5
+    # beside chunks the decode defaults to 2 waves per CU (256 CUs without a device)
+    assert call(wsb=L.pa_decode_workspace_bytes(3, 8, 8, 128, 2 * 256) - 1) == -5
     fp8 = _pool(num_kv_heads=8, dtype=2)
     fp8.k_scale, fp8.v_scale = 1.0, 1.0
     assert call(pool=fp8) == -2 and b"bf16" in L.pa_last_error()  # FP8 chunks: not built

@@ -64,9 +64,12 @@ def test_mixed_step_small():
     s1 = assert_close(wl, got[:nd], decode_out(wl, b["dec"]), "decode rows")
     s2 = assert_close(wl, got[nd:], prefill_out(wl), "prefill rows")
     _note(f"  decode {s1}  prefill {s2}")
-    # the same kernels as the separate calls: bitwise the same rows
+    # the same kernels as the separate calls: bitwise the same rows, given the
+    # decode the same number of work slices (beside chunks the mixed call
+    # defaults to 2 per compute unit, the plain decode to 8)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     d = pkv.decode(b["q"][:nd].contiguous(), g.pool, b["tables"][:nd].contiguous(),
-                   b["lens"][:nd].contiguous(), wl.scale)
+                   b["lens"][:nd].contiguous(), wl.scale, workers=2 * cus)
     p = pkv.prefill_chunk(b["q"][nd:].contiguous(), (b["loc"][nd:] - nd).contiguous(),
                           b["lens"][nd:].contiguous(), g.pool, b["tables"][nd:].contiguous(),
                           b["C"], wl.scale)
