@@ -168,8 +168,9 @@ pa_status pa_probe_stream_read(const void* buf, size_t bytes, int32_t grid, uint
 
 /*
  * Workspace needed by pa_decode, in bytes, for these sizes and worker count
- * (0 = the library's default: 8 wavefronts per compute unit of the current
- * device). Returns 0 for invalid sizes.
+ * (0 = the library's default: sized for 8 wavefronts per compute unit of the
+ * current device, which covers every default launch). Returns 0 for invalid
+ * sizes.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t num_workers);
@@ -192,8 +193,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                  a sequence of length 0 gets an all-zero output
  *   num_q_heads  : multiple of pool->num_kv_heads
  *   scale        : softmax scale, finite and > 0 (typically 1/sqrt(head_dim))
- *   num_workers  : 0 = default; any positive count gives the same result up to
- *                  fp32 rounding order
+ *   num_workers  : 0 = default (8 wavefronts per compute unit; 4 for bf16
+ *                  pools whose query groups run on the matrix cores, 4 or
+ *                  more query heads per unit); any positive count gives the
+ *                  same result up to fp32 rounding order
  *   workspace    : device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
  *                  aligned; scratch (no contents are needed before or kept
  *                  after a call). Calls that share a workspace must not overlap.
@@ -311,6 +314,8 @@ size_t pa_decode_grouped_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                  shared blocks are then read once per sub-group);
  *                  PA_ERR_UNSUPPORTED when even one sequence's query heads
  *                  per KV head exceed 16.
+ *   num_workers  : 0 = default (4 wavefronts per compute unit for bf16
+ *                  pools, 8 for FP8 pools)
  *   workspace    : device, >= pa_decode_grouped_workspace_bytes(...) bytes,
  *                  16-byte aligned, scratch; calls sharing one must not overlap.
  * bf16 and PA_FP8_E4M3 pools, head_dim 64 or 128 (PA_ERR_UNSUPPORTED

@@ -17,6 +17,7 @@ namespace pa {
 
 namespace {
 constexpr int32_t kWavesPerCU = 8;  // default decode workers per compute unit
+constexpr int32_t kMatrixWavesPerCU = 4;  // the same for the bf16 matrix-core decodes
 
 int32_t device_cus() {
   static int32_t cached = 0;
@@ -265,11 +266,25 @@ pa_status decode_check(const DecodeCall& c, const char* who, size_t* need) {
   return PA_OK;
 }
 
+// Default work slices of the bf16 matrix-core decodes (query groups of 4 or
+// more heads per unit, and the grouped decode): they stream as fast with 4
+// waves per CU as with 8, and fewer slices split fewer units (Llama-2-70B
+// layer +0.8 %, one tensor-parallel shard of it +5 %, parallel samples /
+// beams +3 %). MHA and FP8 pools keep 8 per CU. Workspaces stay sized for
+// the larger default, so the size queries need no dtype.
+int32_t matrix_default_workers(int32_t layout_workers) {
+  const int32_t w = device_cus() * kMatrixWavesPerCU;
+  return w < layout_workers ? w : layout_workers;
+}
+
 pa_status decode_launch(const DecodeCall& c, void* workspace, void* stream, const char* who) {
   const DecodeLayout lay = decode_layout(c.num_seqs, c.num_q_heads, c.pool->num_kv_heads,
                                          c.pool->head_dim, c.num_workers);
-  const DecodeArgs a = decode_args(c.out, c.q, c.pool, c.block_tables, c.max_blocks_per_seq,
-                                   c.seq_lens, c.num_seqs, c.num_q_heads, c.scale, lay, workspace);
+  DecodeArgs a = decode_args(c.out, c.q, c.pool, c.block_tables, c.max_blocks_per_seq,
+                             c.seq_lens, c.num_seqs, c.num_q_heads, c.scale, lay, workspace);
+  const int32_t G = c.num_q_heads / c.pool->num_kv_heads;
+  if (c.num_workers == 0 && c.pool->dtype == PA_BF16 && decode_heads_per_unit(G) >= 4)
+    a.workers = matrix_default_workers(lay.workers);
   return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)), who);
 }
 
@@ -488,6 +503,7 @@ pa_status pa_decode_grouped(void* out, const void* q, const pa_pool* pool,
     return fail(PA_ERR_INVALID, "%s: workspace must be 16-byte aligned", who);
   pa::DecodeArgs a = pa::decode_args(out, q, pool, block_tables, max_blocks_per_seq, seq_lens,
                                      num_seqs, num_q_heads, scale, lay, workspace);
+  if (num_workers == 0 && pool->dtype == PA_BF16) a.workers = pa::matrix_default_workers(lay.workers);
   a.prefix_lens = prefix_lens;
   a.group_size = members;
   a.num_groups = num_seqs / members;
@@ -667,9 +683,11 @@ pa_status pa_attention_mixed(void* out, const void* q, const int32_t* q_start_lo
       return s;
   }
   auto run_decode = [&]() -> pa_status {  // rows 0 .. num_decode-1, one per sequence
-    const pa::DecodeArgs a = pa::decode_args(out, q, pool, block_tables, max_blocks_per_seq,
-                                             seq_lens, num_decode, num_q_heads, scale, lay,
-                                             workspace);
+    pa::DecodeArgs a = pa::decode_args(out, q, pool, block_tables, max_blocks_per_seq, seq_lens,
+                                       num_decode, num_q_heads, scale, lay, workspace);
+    // decode rows alone: pa_decode's defaults
+    if (num_workers == 0 && !both && pool->dtype == PA_BF16 && pa::decode_heads_per_unit(G) >= 4)
+      a.workers = pa::matrix_default_workers(lay.workers);
     return pa::hip_status(pa::launch_decode(a, st), who);
   };
   auto run_chunks = [&]() -> pa_status {
