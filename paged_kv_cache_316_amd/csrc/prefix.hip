@@ -12,8 +12,10 @@
 //  2. prefix_partial_kernel: for every KV head, the queries of all sequences
 //     (S * G columns: sequence s, query head kvh*G + hh is column s*G + hh)
 //     against the P*B shared keys, on the matrix cores. The keys are cut into
-//     n_split ranges; each (KV head, 16-column block, key range) is one wave,
-//     which writes unnormalised partials (sum_t 2^(x_t - m) v_t, m, l).
+//     n_split ranges; a workgroup takes one (KV head, key range) and a few
+//     column blocks, one per wave, whose waves share the range's K/V tiles
+//     through LDS; each wave writes unnormalised partials
+//     (sum_t 2^(x_t - m) v_t as bf16, m, l).
 //  3. prefix_merge_kernel: per row, M = max of the partial maxima and the
 //     suffix log-sum-exp, and out = (sum_c acc_c 2^(m_c-M) + o_s l_s 2^(m_s-M)) /
 //     (sum_c l_c 2^(m_c-M) + l_s 2^(m_s-M)), o_s being the suffix output.
