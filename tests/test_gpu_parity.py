@@ -96,6 +96,21 @@ def test_repeated_calls_reuse_workspace():
     assert_close(wl, out_f64(outs[0]), decode_out(wl), "repeat")
 
 
+@pytest.mark.parametrize("name,per_cu", [("llama13b", 8), ("llama70b", 4), ("llama13b_fp8", 8)])
+def test_default_work_slices_by_path(name, per_cu):
+    """The default number of work slices depends on the path: 4 per compute
+    unit for the bf16 matrix-core decode (query groups of 4 or more heads), 8
+    for MHA and FP8 pools. A default call gives the same bits as a call that
+    asks for that count (the split, and so the rounding order, follow it)."""
+    wl = workloads.make(name, "small")
+    g = Loaded(wl)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    base = g.decode()
+    explicit = g.decode(workers=per_cu * cus)
+    assert torch.equal(base.view(torch.int16), explicit.view(torch.int16)), name
+    assert_close(wl, out_f64(base), decode_out(wl), f"{name} default slices")
+
+
 def test_placement_invariance_bitwise():
     """Permuting physical block ids (pool'[pi(b)] = pool[b], table' = pi(table))
     gives a bitwise-identical output."""
