@@ -56,6 +56,19 @@ def test_sharing_workloads_small(name):
     print(f"  {stats}", flush=True)
 
 
+@pytest.mark.parametrize("name", ["cow", "beam"])
+def test_default_work_slices(name):
+    """Over bf16 pools the grouped decode defaults to 4 work slices per
+    compute unit: a default call gives the same bits as one that asks for
+    that count."""
+    wl = workloads.make(name, "small")
+    g = Loaded(wl)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    base, _ = _grouped(g, wl)
+    explicit, _ = _grouped(g, wl, 4 * cus)
+    assert torch.equal(base.view(torch.int16), explicit.view(torch.int16)), name
+
+
 @pytest.mark.parametrize("workers", [1, 3, 7, 64, 333, 2048])
 @pytest.mark.parametrize("name", ["cow504", "beam"])
 def test_worker_splits(name, workers):
